@@ -1,0 +1,97 @@
+"""Step schedule of the denoising loop — test infrastructure only.
+
+SparseD abstract: full attention in the early steps, then a head-specific
+pattern computed once and reused at every later step.  Step-dLLM abstract:
+the block mask is refreshed at anchor steps and reused within each interval.
+PulseCol abstract: the column pattern is identified at an early step and
+refreshed only at a few intermediate steps.
+
+Action of step t, with S = {select_step} u {select_step + m * interval, m >= 1}
+u refresh_steps (steps below total_steps):
+  t in S     : DENSE_SELECT if t < dense_steps or (refresh_dense and t > select_step),
+               else SELECT_SPARSE;
+  t not in S : DENSE if t < dense_steps, else SPARSE.
+SELECT_SPARSE selects from the step's own Q/K and then attends with the new
+mask.  DENSE_SELECT attends densely; a block pattern is selected from the
+step's Q/K, a column pattern from the dense pass's log-sum-exp; either
+applies from the next sparse step on.
+"""
+
+import numpy as np
+
+from .attention import block_sparse_attention, column_sparse_attention, dense_attention
+from .select import (
+    column_scores,
+    count_from_fraction,
+    pooled_mass,
+    select_columns,
+    select_mass_cap,
+    select_topk,
+)
+
+ACTIONS = ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE")
+
+
+def select_steps(total_steps, select_step, refresh_interval=0, refresh_steps=()):
+    s = {select_step}
+    if refresh_interval > 0:
+        s.update(range(select_step + refresh_interval, total_steps, refresh_interval))
+    s.update(refresh_steps)
+    return {t for t in s if 0 <= t < total_steps}
+
+
+def schedule_actions(total_steps, dense_steps, select_step, refresh_interval=0,
+                     refresh_steps=(), refresh_dense=False):
+    if select_step > dense_steps:
+        raise ValueError("the first sparse step would have no pattern")
+    S = select_steps(total_steps, select_step, refresh_interval, refresh_steps)
+    acts = []
+    for t in range(total_steps):
+        if t in S:
+            dense = t < dense_steps or (refresh_dense and t > select_step)
+            acts.append("DENSE_SELECT" if dense else "SELECT_SPARSE")
+        else:
+            acts.append("DENSE" if t < dense_steps else "SPARSE")
+    return acts
+
+
+def run_schedule(w, step_inputs, steps=None):
+    """Run a whole schedule of workload `w` (small shapes only).
+
+    step_inputs(t) -> dict(q, k, v) for step t.  Returns a list, per step, of
+    dict(action, o, lse, pattern) where pattern is (row_ptr, col_idx) for
+    blocks or col_idx for columns (the pattern in force after the step).
+    """
+    acts = schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
+                            w.refresh_steps, w.refresh_dense)
+    steps = range(w.total_steps) if steps is None else steps
+    pattern = None
+    out = []
+    for t in range(w.total_steps):
+        a = acts[t]
+        x = step_inputs(t)
+        q, k, v = x["q"], x["k"], x["v"]
+        o = lse = None
+        if w.selector == "blocks":
+            if a in ("DENSE_SELECT", "SELECT_SPARSE"):
+                A = pooled_mass(q, k, w.block, w.block)
+                if w.budget == "topk":
+                    pattern = select_topk(A, w.keep_frac)
+                else:
+                    rp, ci, _ = select_mass_cap(A, w.mass, w.max_mean_density)
+                    pattern = (rp, ci)
+            if a in ("DENSE", "DENSE_SELECT"):
+                o, lse = dense_attention(q, k, v)
+            else:
+                o, lse = block_sparse_attention(q, k, v, pattern[0], pattern[1], w.block, w.block)
+        else:
+            if a in ("DENSE", "DENSE_SELECT"):
+                o, lse = dense_attention(q, k, v)
+                if a == "DENSE_SELECT":
+                    kcol = count_from_fraction(w.column_keep_frac, np.asarray(k).shape[2])
+                    pattern = select_columns(column_scores(q, k, lse), kcol)
+            else:
+                o, lse = column_sparse_attention(q, k, v, pattern)
+        if t in steps:
+            out.append({"step": t, "action": a, "o": o, "lse": lse, "pattern": pattern})
+    return out

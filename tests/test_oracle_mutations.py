@@ -1,0 +1,148 @@
+"""The pins catch plausible mistakes: each test plants one mistake in the
+oracle (on the CPU, through monkeypatch) and checks that a pin now fails."""
+
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+import oracle
+import oracle.attention as oatt
+import oracle.select as osel
+from workloads import tiny_random
+
+
+def _x(seed, Hq=4, Hkv=2, L=13, d=8):
+    return {n: v.astype(np.float64) for n, v in tiny_random(seed, 1, Hq, Hkv, L, d).items()}
+
+
+def pin_dense_vs_torch():
+    x = _x(1)
+    o, lse = oracle.dense_attention(x["q"], x["k"], x["v"])
+    kt = torch.from_numpy(np.repeat(x["k"], 2, axis=1))
+    vt = torch.from_numpy(np.repeat(x["v"], 2, axis=1))
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(x["q"]), kt, vt).numpy()
+    np.testing.assert_allclose(o, ref, atol=1e-12)
+    s = np.einsum("bhid,bhjd->bhij", x["q"], kt.numpy()) / np.sqrt(8)
+    np.testing.assert_allclose(lse, logsumexp(s, axis=-1), atol=1e-12)
+
+
+def pin_pooling_closed_form():
+    x = np.arange(5, dtype=np.float64).reshape(1, 1, 5, 1)
+    np.testing.assert_array_equal(oracle.pool_blocks(x, 2)[0, 0, :, 0], [0.5, 2.5, 4.0])
+
+
+def pin_topk_ties_brute_force():
+    A = np.array([[[[1.0, 3.0, 2.0, 3.0, 0.0, 2.0]]]])
+    rp, ci = oracle.select_topk(A, 0.5)
+    best = min(itertools.combinations(range(6), 3), key=lambda S: (-sum(A[0, 0, 0, list(S)]), S))
+    assert list(ci) == list(best)
+
+
+def pin_mass_exact_hit():
+    # cumulative masses 0.5, 0.75, 0.875, 1: tau = 0.75 is reached by 2 blocks
+    A = np.array([[[[0.125, 0.5, 0.25, 0.125]]]])
+    rp, ci, _ = oracle.select_mass_cap(A, 0.75, 1.0)
+    assert list(ci) == [1, 2]
+
+
+def pin_column_sum_total():
+    x = _x(3, Hq=6, Hkv=2)
+    _, lse = oracle.dense_attention(x["q"], x["k"], x["v"])
+    C = oracle.column_scores(x["q"], x["k"], lse)
+    np.testing.assert_allclose(C.sum(-1), 3 * 13, rtol=1e-12)
+
+
+def pin_topk_count():
+    A = np.random.default_rng(0).random((1, 1, 2, 256))
+    rp, _ = oracle.select_topk(A, 0.10)
+    assert np.all(np.diff(rp) == 26)
+
+
+def test_pins_pass_on_the_real_oracle():
+    for pin in (pin_dense_vs_torch, pin_pooling_closed_form, pin_topk_ties_brute_force,
+                pin_mass_exact_hit, pin_column_sum_total, pin_topk_count):
+        pin()
+
+
+def _fails(pin):
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_transposed_gqa_map_is_caught(monkeypatch):
+    bad = lambda hq, hkv: np.arange(hq) % hkv  # noqa: E731  interleaved instead of consecutive groups
+    monkeypatch.setattr(oatt, "head_group", bad)
+    _fails(pin_dense_vs_torch)
+
+
+def test_dropped_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(oatt, "default_scale", lambda d: 1.0)
+    _fails(pin_dense_vs_torch)
+
+
+def test_lse_sign_error_is_caught(monkeypatch):
+    real = oatt._attend
+
+    def bad(s, v):
+        o, lse = real(s, v)
+        m = s.max(axis=-1)
+        return o, m - (lse - m)
+    monkeypatch.setattr(oatt, "_attend", bad)
+    _fails(pin_dense_vs_torch)
+
+
+def test_value_operand_transposed_is_caught(monkeypatch):
+    real = oatt._attend
+    monkeypatch.setattr(oatt, "_attend", lambda s, v: real(s.T.copy() if s.shape[0] == s.shape[1] else s, v))
+    _fails(pin_dense_vs_torch)
+
+
+def test_pooling_off_by_one_is_caught(monkeypatch):
+    def bad(x, block):
+        x = oatt.as_f64(x)
+        B, H, L, d = x.shape
+        nb = -(-L // block)
+        out = np.zeros((B, H, nb, d))
+        for I in range(nb):
+            seg = x[:, :, I * block + 1:min(L, (I + 1) * block + 1)]
+            out[:, :, I] = seg.sum(axis=2) / max(1, seg.shape[2])
+        return out
+    monkeypatch.setattr(osel, "pool_blocks", bad)
+    monkeypatch.setattr(oracle, "pool_blocks", bad)
+    _fails(pin_pooling_closed_form)
+
+
+def test_tie_break_toward_higher_index_is_caught(monkeypatch):
+    monkeypatch.setattr(osel, "rank_order", lambda a: np.lexsort((-np.arange(len(a)), -np.asarray(a))))
+    _fails(pin_topk_ties_brute_force)
+
+
+def test_strict_mass_comparison_is_caught(monkeypatch):
+    def bad(A, tau):
+        n = A.shape[-1]
+        out = []
+        for a in A.reshape(-1, n):
+            c = np.cumsum(a[osel.rank_order(a)])
+            hit = np.nonzero(c > tau)[0]
+            out.append(hit[0] + 1 if len(hit) else n)
+        return np.array(out)
+    monkeypatch.setattr(osel, "mass_prefix_counts", bad)
+    _fails(pin_mass_exact_hit)
+
+
+def test_missing_group_head_in_column_scores_is_caught(monkeypatch):
+    real = osel.head_group
+    monkeypatch.setattr(osel, "head_group", lambda hq, hkv: np.where(np.arange(hq) % (hq // hkv) == 0, -10**6,
+                                                                     real(hq, hkv)))
+    with pytest.raises((AssertionError, IndexError)):
+        pin_column_sum_total()
+
+
+def test_floor_instead_of_ceil_count_is_caught(monkeypatch):
+    monkeypatch.setattr(osel, "count_from_fraction",
+                        lambda f, n: max(1, int(Fraction(str(f)) * n)))
+    _fails(pin_topk_count)

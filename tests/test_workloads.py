@@ -1,0 +1,48 @@
+"""The seeded input generator: determinism, rounding, planted structure (CPU)."""
+
+import hashlib
+
+import numpy as np
+import torch
+
+from workloads import WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits, make_base, make_step
+from workloads.configs import scaled
+
+
+def _h(a):
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def test_bf16_rounding_matches_torch_rne():
+    x = np.random.default_rng(0).standard_normal(10000).astype(np.float32) * 100
+    x[:4] = [1.00390625, 1.01171875, -3.0078125, 0.0]  # exact ties in bf16
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(f32_to_bf16_bits(x), ref)
+    np.testing.assert_array_equal(bf16_bits_to_f32(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_generator_is_deterministic_and_step_dependent():
+    w = scaled(WORKLOADS["llada8b_8k"], seq_len=512, q_heads=4, kv_heads=4)
+    a, b = make_step(w, 3), make_step(w, 3)
+    for n in "qkv":
+        assert _h(a[n]) == _h(b[n])
+        assert a[n].dtype == np.uint16 and a[n].shape == (1, 4, 512, 128)
+    c = make_step(w, 4)
+    assert _h(a["q"]) != _h(c["q"]) and _h(a["k"]) != _h(c["k"])
+    assert _h(a["v"]) == _h(c["v"])  # the walk leaves V fixed
+
+
+def test_fresh_qv_noise_keeps_k():
+    w = WORKLOADS["tiny_fp32_h4_l512"]
+    base = make_base(w)
+    s1, s2 = make_step(w, 1, base), make_step(w, 2, base)
+    assert np.array_equal(s1["k"], s2["k"]) and not np.array_equal(s1["q"], s2["q"])
+    assert abs(float((s1["q"] - base["q"]).std()) - 0.05) < 0.005
+
+
+def test_columns_pattern_plants_shared_stripes():
+    w = scaled(WORKLOADS["pulsecol_dream7b_16k"], seq_len=1024, q_heads=8, kv_heads=2, n_stripe_columns=16)
+    x = make_base(w)
+    # a stripe key has a much larger norm than a plain N(0,1) key of d=128 ... on average over stripes
+    norms = np.linalg.norm(x["k"][0, 0], axis=-1)
+    assert (norms > np.sqrt(128) + 1.5).sum() >= 8

@@ -1,0 +1,16 @@
+"""Seeded synthetic workloads for sparse bidirectional attention.
+
+This package holds the workload descriptions (shapes, step schedules and
+budgets, as plain parameters) and the seeded input generator.  It is the one
+module shared by the GPU library's tests and benchmark and by the fp64 oracle;
+it contains none of the attention or selection arithmetic of the method.
+"""
+
+from .configs import WORKLOADS, Workload, get_workload  # noqa: F401
+from .generate import (  # noqa: F401
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    make_base,
+    make_step,
+    tiny_random,
+)

@@ -1,0 +1,180 @@
+"""Seeded synthetic Q/K/V with planted, head-varying structure.
+
+The pages measure on activations of real diffusion LMs, which are not
+available.  These tensors stand in for them: N(0, 1) entries at the model
+shapes, plus planted structure that mimics what the pages observe (patterns
+differ across heads and stay similar across steps; heads concentrate their
+attention to different extents; SparseD and Step-dLLM abstracts).
+
+Recipe (all draws from numpy PCG64 seeded by SeedSequence):
+  * base tensors  : SeedSequence([wid, 0, tensor]) standard normal, fp32.
+  * head types    : round-robin by h mod 4 -> sink, local, stripes, none.
+      sink    : K of tokens 0..63 += 3u and every Q of the head += 3u.
+      local   : unit e_b per 64-token unit; q_i += 3 e_{i//64};
+                k_j += 3 normalize(sum_{|c - j//64| <= 2} e_c)  (a +-128 band).
+      stripes : K of 4 random 64-token units += 3u and every Q += 3u.
+  * extra pairs   : a fraction of (I, J) block pairs per head gets its own unit
+                    w; q in block I += 2w, k in block J += 2w.
+  * columns       : per kv head g, n random single tokens get K += 3u_g and
+                    every Q of the group's query heads += 3u_g.
+  * steps         : "fresh_qv": Q_t = Q_0 + s N_t, V_t = V_0 + s N_t, K fixed.
+                    "walk": Q_t = Q_0 + s sqrt(t) N_t, K_t likewise, V fixed
+                    (the marginal of a random walk with step s, so any step
+                    can be produced without replaying the earlier ones).
+  * bf16          : the fp32 step tensor rounded to nearest-even.
+
+Tensors are returned as numpy arrays of shape [B, H, L, d]: float32 for the
+fp32 workloads, uint16 bf16 bit patterns for the bf16 workloads.
+"""
+
+import numpy as np
+
+from .configs import Workload
+
+_T_Q, _T_K, _T_V = 0, 1, 2
+UNIT = 64  # token unit of the planted sink/local/stripe patterns
+
+
+def _rng(*key):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def _unit(rng, d):
+    x = rng.standard_normal(d)
+    return (x / np.linalg.norm(x)).astype(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round to nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _plant_mix(w: Workload, q, k):
+    """Round-robin head types sink / local / stripes / none (in place, fp32)."""
+    B, H, L, d = q.shape
+    n_units = -(-L // UNIT)
+    for h in range(H):
+        kind = h % 4
+        r = _rng(w.wid, 100, h)
+        if kind == 0:  # sink
+            u = _unit(r, d)
+            k[:, h, :min(UNIT, L)] += 3.0 * u
+            q[:, h] += 3.0 * u
+        elif kind == 1:  # local band of +-2 units
+            e = np.stack([_unit(r, d) for _ in range(n_units)])
+            band = np.zeros_like(e)
+            for c in range(n_units):
+                lo, hi = max(0, c - 2), min(n_units, c + 3)
+                s = e[lo:hi].sum(axis=0)
+                band[c] = s / np.linalg.norm(s)
+            tok_unit = np.arange(L) // UNIT
+            q[:, h] += 3.0 * e[tok_unit]
+            k[:, h] += 3.0 * band[tok_unit]
+        elif kind == 2:  # vertical stripes: 4 random 64-token units
+            u = _unit(r, d)
+            units = r.choice(n_units, size=min(4, n_units), replace=False)
+            for c in units:
+                k[:, h, c * UNIT:min(L, (c + 1) * UNIT)] += 3.0 * u
+            q[:, h] += 3.0 * u
+
+
+def _plant_pairs(w: Workload, q, k):
+    """Extra alignment on a random fraction of (I, J) block pairs per head."""
+    B, H, L, d = q.shape
+    nb = -(-L // w.block)
+    n_pairs = int(round(w.extra_pair_frac * nb * nb))
+    if n_pairs == 0:
+        return
+    for h in range(H):
+        r = _rng(w.wid, 200, h)
+        flat = r.choice(nb * nb, size=n_pairs, replace=False)
+        wv = r.standard_normal((n_pairs, d))
+        wv = (wv / np.linalg.norm(wv, axis=1, keepdims=True)).astype(np.float32)
+        qadd = np.zeros((nb, d), np.float32)
+        kadd = np.zeros((nb, d), np.float32)
+        np.add.at(qadd, flat // nb, 2.0 * wv)
+        np.add.at(kadd, flat % nb, 2.0 * wv)
+        tok_blk = np.arange(L) // w.block
+        q[:, h] += qadd[tok_blk]
+        k[:, h] += kadd[tok_blk]
+
+
+def _plant_columns(w: Workload, q, k):
+    """Per kv head, single-token key columns aligned with the group's queries."""
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    for g in range(Hkv):
+        r = _rng(w.wid, 300, g)
+        u = _unit(r, d)
+        cols = r.choice(L, size=min(w.n_stripe_columns, L), replace=False)
+        k[:, g, cols] += 3.0 * u
+        q[:, g * G:(g + 1) * G] += 3.0 * u
+
+
+def make_base(w: Workload):
+    """Step-0 tensors in fp32 (before rounding): dict q, k, v."""
+    B, Hq, Hkv, L, d = w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim
+    q = _rng(w.wid, 0, _T_Q).standard_normal((B, Hq, L, d), dtype=np.float32)
+    k = _rng(w.wid, 0, _T_K).standard_normal((B, Hkv, L, d), dtype=np.float32)
+    v = _rng(w.wid, 0, _T_V).standard_normal((B, Hkv, L, d), dtype=np.float32)
+    if w.pattern == "mix":
+        _plant_mix(w, q, k)
+    elif w.pattern == "columns":
+        _plant_columns(w, q, k)
+    if w.extra_pair_frac > 0:
+        _plant_pairs(w, q, k)
+    return {"q": q, "k": k, "v": v}
+
+
+def _noise(w: Workload, step: int, tensor: int, shape, scale: float, out):
+    n = _rng(w.wid, 1 + step, tensor).standard_normal(shape, dtype=np.float32)
+    n *= np.float32(scale)
+    n += out
+    return n
+
+
+def make_step(w: Workload, step: int, base=None, as_float: bool = False):
+    """Inputs of denoising step `step`: dict q, k, v as stored (f32 or bf16 bits).
+
+    With as_float=True the bf16 tensors are returned decoded to float32.
+    """
+    if base is None:
+        base = make_base(w)
+    q, k, v = base["q"], base["k"], base["v"]
+    if step > 0:
+        if w.step_noise == "fresh_qv":
+            q = _noise(w, step, _T_Q, q.shape, w.step_sigma, q)
+            v = _noise(w, step, _T_V, v.shape, w.step_sigma, v)
+        elif w.step_noise == "walk":
+            s = w.step_sigma * float(np.sqrt(step))
+            q = _noise(w, step, _T_Q, q.shape, s, q)
+            k = _noise(w, step, _T_K, k.shape, s, k)
+        else:
+            raise ValueError(w.step_noise)
+    out = {"q": q, "k": k, "v": v}
+    if w.dtype == "bf16":
+        out = {n: f32_to_bf16_bits(x) for n, x in out.items()}
+        if as_float:
+            out = {n: bf16_bits_to_f32(x) for n, x in out.items()}
+    else:
+        out = {n: np.ascontiguousarray(x, dtype=np.float32) for n, x in out.items()}
+    return out
+
+
+def tiny_random(seed: int, B, Hq, Hkv, L, d, dtype="f32", scale=1.0):
+    """Plain N(0, scale^2) Q/K/V for small parity cases (no planted structure)."""
+    r = _rng(9000, seed)
+    q = (r.standard_normal((B, Hq, L, d)) * scale).astype(np.float32)
+    k = (r.standard_normal((B, Hkv, L, d)) * scale).astype(np.float32)
+    v = r.standard_normal((B, Hkv, L, d)).astype(np.float32)
+    out = {"q": q, "k": k, "v": v}
+    if dtype == "bf16":
+        out = {n: f32_to_bf16_bits(x) for n, x in out.items()}
+    return out
