@@ -1,0 +1,362 @@
+"""Benchmark: ms per denoising step over a whole sparse-attention schedule.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one denoising step of the workload's schedule, run through the
+library's schedule driver (C ABI): dense warm-up steps, the pattern
+selection step, then sparse steps reusing the pattern (refreshes where the
+schedule has them).  K steps form one schedule: with K equal to the
+workload's step count it is exactly that schedule; otherwise the schedule is
+rescaled to K steps with the same warm-up fraction and refresh spacing.
+
+Inputs are the seeded synthetic tensors of the workload (planted per-head
+structure), resident in HBM before timing starts: the step-0 tensors serve
+the dense steps and the selection step's tensors serve the selection and
+sparse steps (kernel time does not depend on the drift between steps; the
+pattern does, and it is computed from the real selection-step inputs).
+
+The JSON line reports the whole-schedule ms per step (value), per-phase
+medians, effective TFLOP/s of the sparse steps on kept-block FLOPs, the dense
+schedule on the same GPU, a roofline object for the kernel that takes most
+of the timed time, and the oracle timed on the host on a bounded sample.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/denoise step + effective TFLOP/s (MFMA %) of sparse attn at 8K–64K vs dense"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rescaled(w, K):
+    """The workload's schedule stretched or shrunk to K steps."""
+    from workloads.configs import scaled
+    if K == w.total_steps:
+        return w
+    f = K / w.total_steps
+    dense = min(K, int(math.ceil(w.dense_steps * f)))
+    sel = min(dense, int(math.ceil(w.select_step * f))) if w.select_step else 0
+    sel = min(sel, K - 1)
+    interval = max(1, int(round(w.refresh_interval * f))) if w.refresh_interval else 0
+    refresh = tuple(sorted({min(K - 1, int(round(t * f))) for t in w.refresh_steps} - {sel}))
+    return scaled(w, total_steps=K, dense_steps=dense, select_step=sel, refresh_interval=interval,
+                  refresh_steps=refresh)
+
+
+def schedule_desc(sd, w):
+    sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
+    budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
+    return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
+                            w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac)
+
+
+def to_dev(x):
+    import numpy as np
+    import torch
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_bidirectional_attention_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or
+    None if there is none for the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, acts, base_step, sel_step_inputs):
+    """The oracle (fp64 numpy) on a bounded sample of the same work, scaled
+    to ms per denoising step of the same schedule."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    cores = len(os.sched_getaffinity(0))
+    L, H, d = w.seq_len, w.q_heads, w.head_dim
+    G = w.q_heads // w.kv_heads
+    x0 = base_step
+    xs = sel_step_inputs
+    t_budget = 20.0
+    samples = {}
+    # dense step: a few query rows of one head, scaled to all rows and heads
+    rows = np.arange(0, L, max(1, L // 64))[:64]
+    t0 = time.perf_counter()
+    oracle.dense_attention(x0["q"][:, :1], x0["k"][:, :1], x0["v"][:, :1], rows=rows)
+    t_dense = (time.perf_counter() - t0) * (L / len(rows)) * H
+    samples["dense"] = f"{len(rows)} query rows of 1 head, x{L / len(rows) * H:.0f}"
+    # selection: pooling + pooled mass + budget for one kv group, scaled to all groups
+    t0 = time.perf_counter()
+    if w.selector == "blocks":
+        A = oracle.pooled_mass(xs["q"][:, :G], xs["k"][:, :1], w.block, w.block)
+        if w.budget == "topk":
+            oracle.select_topk(A, w.keep_frac)
+        else:
+            oracle.select_mass_cap(A, w.mass, w.max_mean_density)
+        t_sel = (time.perf_counter() - t0) * w.kv_heads
+        samples["select"] = f"1 of {w.kv_heads} kv groups, x{w.kv_heads}"
+        # sparse step: a few query blocks of one head, gather form
+        nqb = -(-L // w.block)
+        A1 = oracle.pooled_mass(xs["q"][:, :1], xs["k"][:, :1], w.block, w.block)
+        if w.budget == "topk":
+            rp, ci = oracle.select_topk(A1, w.keep_frac)
+        else:
+            rp, ci, _ = oracle.select_mass_cap(A1, w.mass, w.max_mean_density)
+        qb = np.arange(0, nqb, max(1, nqb // 16))[:16]
+        t0 = time.perf_counter()
+        oracle.block_sparse_attention(xs["q"][:, :1], xs["k"][:, :1], xs["v"][:, :1], rp, ci, w.block, w.block,
+                                      qblocks=qb)
+        t_sparse = (time.perf_counter() - t0) * (nqb / len(qb)) * H
+        samples["sparse"] = f"{len(qb)} query blocks of 1 head, x{nqb / len(qb) * H:.0f}"
+    else:
+        kcol = oracle.count_from_fraction(w.column_keep_frac, L)
+        qrows = np.arange(0, L, max(1, L // 16))[:16]
+        _, lse = oracle.dense_attention(xs["q"][:, :1], xs["k"][:, :1], xs["v"][:, :1], rows=qrows)
+        t0 = time.perf_counter()
+        s = (xs["q"][0, 0, qrows].astype(np.float64) @ oracle.attention.as_f64(xs["k"][0, 0]).T) / np.sqrt(d)
+        np.exp(s - lse[0, 0][:, None]).sum(axis=0)
+        t_sel = (time.perf_counter() - t0) * (L / len(qrows)) * H
+        samples["select"] = f"column scores of {len(qrows)} query rows of 1 head, x{L / len(qrows) * H:.0f}"
+        cols = np.sort(np.random.default_rng(0).choice(L, kcol, replace=False))[None, None].repeat(w.kv_heads, 1)
+        t0 = time.perf_counter()
+        oracle.column_sparse_attention(xs["q"][:, :1], xs["k"][:, :1], xs["v"][:, :1], cols[:, :1], rows=qrows)
+        t_sparse = (time.perf_counter() - t0) * (L / len(qrows)) * H
+        samples["sparse"] = f"{len(qrows)} query rows of 1 head, x{L / len(qrows) * H:.0f}"
+    n = {a: acts.count(a) for a in ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE")}
+    total = (n["DENSE"] * t_dense + n["DENSE_SELECT"] * (t_dense + t_sel) + n["SELECT_SPARSE"] * (t_sel + t_sparse)
+             + n["SPARSE"] * t_sparse)
+    ms = 1e3 * total / len(acts)
+    return {"value": round(ms, 3), "unit": "ms/denoise step", "cores": threads, "host_cores": cores,
+            "kind": "oracle",
+            "sample": ("fp64 numpy oracle, extrapolated from timed samples: " + "; ".join(
+                f"{k}: {v}" for k, v in samples.items()) + "; weighted by the schedule's action counts"),
+            "per_step_ms": {"dense": round(1e3 * t_dense, 1), "select": round(1e3 * t_sel, 1),
+                            "sparse": round(1e3 * t_sparse, 1)}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="sparsed_64k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(sharding the heads across GPUs is not implemented); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_bidirectional_attention_amd as sd
+    from workloads import get_workload, make_base, make_step
+    import oracle
+
+    w0 = get_workload(args.workload)
+    K = args.steps if args.steps is not None else w0.total_steps
+    w = rescaled(w0, K)
+    acts = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
+                                   w.refresh_steps, w.refresh_dense)
+    torch.cuda.set_device(0)
+    log(f"workload {w.name}: L={w.seq_len} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} {w.dtype} "
+        f"block={w.block}; schedule of {K} steps: " + ", ".join(f"{a} x{acts.count(a)}" for a in sorted(set(acts))))
+    t0 = time.time()
+    base = make_base(w0)
+    x0h = make_step(w0, 0, base)
+    xsh = make_step(w0, w0.select_step, base) if w0.select_step else x0h
+    del base
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    x0 = {n: to_dev(a) for n, a in x0h.items()}
+    xs = {n: to_dev(a) for n, a in xsh.items()}
+    o = torch.empty_like(x0["q"])
+    lse = torch.empty(x0["q"].shape[:3], dtype=torch.float32, device="cuda")
+    p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
+
+    def inputs_for(t, a):
+        return x0 if a == "DENSE" else xs
+
+    # warm-up: W untimed steps of a schedule of the same shape
+    if args.warmup > 0:
+        ww = rescaled(w0, max(2, args.warmup))
+        hw = sd.sdattn_schedule_create(p, schedule_desc(sd, ww))
+        acts_w = oracle.schedule_actions(ww.total_steps, ww.dense_steps, ww.select_step, ww.refresh_interval,
+                                         ww.refresh_steps, ww.refresh_dense)
+        for t in range(args.warmup):
+            x = inputs_for(t, acts_w[t])
+            sd.sdattn_schedule_step(hw, t, x["q"], x["k"], x["v"], o, lse)
+        torch.cuda.synchronize()
+        sd.sdattn_schedule_destroy(hw)
+
+    h = sd.sdattn_schedule_create(p, schedule_desc(sd, w))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for t in range(K):
+        x = inputs_for(t, acts[t])
+        ev[t][0].record()
+        sd.sdattn_schedule_step(h, t, x["q"], x["k"], x["v"], o, lse)
+        ev[t][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    stats, last_sel = sd.sdattn_schedule_stats(h)
+
+    # pattern size for the kept-FLOP count
+    L, H, Hkv, d = w.seq_len, w.q_heads, w.kv_heads, w.head_dim
+    kept_flops = None
+    if w.selector == "blocks":
+        rp_ptr, ci_ptr, cap = sd.sdattn_schedule_mask(h)
+        rows = w.batch * H * (-(-L // w.block))
+        last = torch.empty(1, dtype=torch.int32, device="cuda")
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        nnz = np.zeros(1, np.int32)
+        hip.hipMemcpy(nnz.ctypes.data, rp_ptr + 4 * rows, 4, 2)
+        nnz = int(nnz[0])
+        kept_flops = 4.0 * d * w.block * w.block * nnz
+        density = nnz / (rows * (-(-L // w.block)))
+    else:
+        kcol = oracle.count_from_fraction(w.column_keep_frac, L)
+        kept_flops = 4.0 * d * L * kcol * H * w.batch
+        nnz = kcol * Hkv
+        density = kcol / L
+    sd.sdattn_schedule_destroy(h)
+    dense_flops = 4.0 * w.batch * H * L * L * d
+
+    def med(a):
+        return float(np.median(a)) if len(a) else None
+
+    idx = {a: [t for t in range(K) if acts[t] == a] for a in set(acts)}
+    dense_ms = med(step_ms[idx.get("DENSE", []) + idx.get("DENSE_SELECT", [])]) if (
+        idx.get("DENSE") or idx.get("DENSE_SELECT")) else None
+    sparse_ms = med(step_ms[idx["SPARSE"]]) if idx.get("SPARSE") else None
+    select_ms = med(step_ms[idx.get("SELECT_SPARSE", [])]) if idx.get("SELECT_SPARSE") else None
+    if idx.get("DENSE") and idx.get("DENSE_SELECT"):
+        dsel = med(step_ms[idx["DENSE_SELECT"]])
+        select_ms = dsel - dense_ms
+    elif idx.get("DENSE_SELECT") and not idx.get("DENSE"):
+        dense_only = None
+        select_ms = None
+    if select_ms is not None and sparse_ms is not None and idx.get("SELECT_SPARSE"):
+        select_ms = select_ms - sparse_ms
+
+    # dense baseline on the same GPU: the dense forward for every step
+    pd = sd.problem(w.batch, H, Hkv, L, d, w.dtype)
+    nd = 3 if L >= 32768 else 10
+    for _ in range(1):
+        sd.sdattn_forward_dense(pd, x0["q"], x0["k"], x0["v"], o, lse)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nd):
+        sd.sdattn_forward_dense(pd, x0["q"], x0["k"], x0["v"], o, lse)
+    e1.record()
+    torch.cuda.synchronize()
+    dense_base_ms = e0.elapsed_time(e1) / nd
+
+    ms_per_step = total_ms / K
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    sparse_tflops = kept_flops / (sparse_ms * 1e9) if sparse_ms else None
+    dense_tflops = dense_flops / (dense_base_ms * 1e9)
+    # kernel with the largest share of the timed region
+    n_sparse = len(idx.get("SPARSE", [])) + len(idx.get("SELECT_SPARSE", []))
+    n_dense = len(idx.get("DENSE", [])) + len(idx.get("DENSE_SELECT", []))
+    share_sparse = n_sparse * (sparse_ms or 0)
+    share_dense = n_dense * dense_base_ms
+    kernels = {
+        "flash_fwd_bf16_sparse" if w.selector == "blocks" else "flash_fwd_bf16_column": {
+            "bound": "mfma", "achieved": round(sparse_tflops, 1) if sparse_tflops else None, "peak": peak,
+            "unit": "TFLOP/s", "frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
+            "launch_ms": round(sparse_ms, 4) if sparse_ms else None,
+            "flops_per_launch": kept_flops,
+            "traffic": load_traffic("flash_sparse", w0.name)},
+        "flash_fwd_bf16_dense": {
+            "bound": "mfma", "achieved": round(dense_tflops, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(dense_tflops / peak, 4), "launch_ms": round(dense_base_ms, 3),
+            "flops_per_launch": dense_flops, "traffic": load_traffic("flash_dense", w0.name)},
+    }
+    dom = max(kernels, key=lambda k: share_sparse if "dense" not in k else share_dense)
+    roof = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = dom
+
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 4),
+        "unit": "ms/denoise step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w0.name, "batch": w.batch, "q_heads": H, "kv_heads": Hkv, "seq_len": L,
+                   "head_dim": d, "block": w.block,
+                   "selector": w.selector, "budget": (f"top-{w.keep_frac:g}" if w.budget == "topk" and w.selector == "blocks"
+                                                      else f"mass {w.mass:g} cap {w.max_mean_density:g}"
+                                                      if w.selector == "blocks" else f"columns {w.column_keep_frac:g}"),
+                   "schedule": {a: acts.count(a) for a in sorted(set(acts))}},
+        "roofline": roof,
+        "phases": {"dense_step_ms": round(dense_ms, 3) if dense_ms else None,
+                   "select_ms": round(select_ms, 3) if select_ms else None,
+                   "sparse_step_ms": round(sparse_ms, 4) if sparse_ms else None,
+                   "sparse_effective_tflops": round(sparse_tflops, 1) if sparse_tflops else None,
+                   "sparse_mfma_frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
+                   "kept_density": round(density, 5), "kept_nnz": nnz},
+        "dense_baseline": {"ms_per_step": round(dense_base_ms, 3), "tflops": round(dense_tflops, 1),
+                           "mfma_frac": round(dense_tflops / peak, 4),
+                           "schedule_speedup": round(dense_base_ms / ms_per_step, 3),
+                           "sparse_step_speedup": round(dense_base_ms / sparse_ms, 3) if sparse_ms else None},
+        "kernels": kernels,
+        "wall_s": round(wall, 2),
+        "schedule_stats": stats,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline(w0, acts, x0h, xsh)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+/*
+ * sdattn.h — sparse bidirectional attention for diffusion-LM denoising,
+ * MI355X (gfx950) HIP library, C ABI.
+ *
+ * What the library computes (the pages' problem statement):
+ *   - Diffusion LMs recompute full bidirectional attention at every denoising
+ *     step because no KV cache applies (Step-dLLM, Abstract; PulseCol,
+ *     Abstract).  sdattn_forward_dense is that non-causal attention.
+ *   - Head-specific sparse patterns are computed once after full-attention
+ *     warm-up steps and reused at the later steps (SparseD, abstract), or
+ *     refreshed at anchor steps with a head-adaptive global budget
+ *     (Step-dLLM, Abstract): sdattn_select_blocks builds per-head block lists
+ *     from mean-pooled query/key block scores with a top-k or a cumulative
+ *     pooled-mass budget, and sdattn_forward_block_sparse attends over them.
+ *   - Column-sparse attention keeps individual key columns chosen from
+ *     column-summed attention at an early step, refreshed at a few
+ *     intermediate steps (PulseCol, Abstract): sdattn_select_columns and
+ *     sdattn_forward_column_sparse.
+ *   - A host-side schedule handle runs warm-up, reuse and refresh.
+ *
+ * Conventions for every call
+ *   Tensors.   Caller-owned device buffers, contiguous.  q and o are
+ *              [B][Hq][L][d]; k and v are [B][Hkv][L][d]; lse is
+ *              [B][Hq][L] float32 natural-log log-sum-exp.  Element type is
+ *              the problem's dtype (float32 or bfloat16); o has the input
+ *              dtype.  Query head h reads kv head h / (Hq / Hkv).
+ *   Scale.     softmax_scale <= 0 selects 1/sqrt(d).
+ *   Shapes.    B, Hq, Hkv >= 1; Hq % Hkv == 0; L >= 0 (L == 0 is a no-op that
+ *              returns SDATTN_OK); d in {64, 128}.  Any L is accepted: a
+ *              last, partial query or key block is handled (a partial block is
+ *              pooled as the mean of the tokens it has).
+ *   Blocks.    block_q, block_k in {64, 128}.  Block row r = (b*Hq + h)*nQB + I
+ *              with nQB = ceil(L / block_q), nKB = ceil(L / block_k).
+ *   CSR.       row_ptr[B*Hq*nQB + 1] int32, col_idx[nnz] int32; each row lists
+ *              its kept key blocks in ascending order without duplicates.
+ *   Streams.   `stream` is a hipStream_t (NULL = the null stream).  Compute
+ *              calls enqueue kernels and return without synchronising; a
+ *              fault inside a kernel surfaces at the caller's next sync.
+ *   Errors.    Arguments are validated on the host before anything is
+ *              enqueued, so a call that returns an error has written nothing.
+ *              sdattn_last_error() returns a thread-local detail string for
+ *              the last failing call on this thread.  No C++ exception
+ *              crosses the ABI.
+ *   Memory.    Stateless calls allocate nothing: workspace is passed in and
+ *              sized by the *_workspace queries.  Only a schedule handle
+ *              allocates (in create) and frees (in destroy).
+ *   Threads.   Stateless calls are reentrant.  A schedule handle must not be
+ *              used from two threads at once.
+ */
+#ifndef SDATTN_H
+#define SDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDATTN_ABI_VERSION 1
+
+/* Exported entry points (the library is built with hidden visibility). */
+#define SDATTN_API __attribute__((visibility("default")))
+
+typedef enum {
+    SDATTN_OK = 0,
+    SDATTN_ERR_NULL = 1,        /* a required pointer is NULL                 */
+    SDATTN_ERR_SHAPE = 2,       /* sizes out of range or inconsistent         */
+    SDATTN_ERR_DTYPE = 3,       /* unsupported element type                   */
+    SDATTN_ERR_BUDGET = 4,      /* budget parameters out of range             */
+    SDATTN_ERR_WORKSPACE = 5,   /* workspace smaller than the query returned  */
+    SDATTN_ERR_CAPACITY = 6,    /* output index buffer too small              */
+    SDATTN_ERR_HIP = 7,         /* a HIP runtime call failed (see last_error) */
+    SDATTN_ERR_UNSUPPORTED = 8, /* valid request this build does not support  */
+    SDATTN_ERR_STATE = 9        /* schedule misuse (e.g. sparse step, no mask) */
+} sdattn_status;
+
+typedef enum { SDATTN_F32 = 0, SDATTN_BF16 = 1 } sdattn_dtype;
+
+typedef struct {
+    int32_t batch;       /* B   */
+    int32_t q_heads;     /* Hq  */
+    int32_t kv_heads;    /* Hkv */
+    int32_t seq_len;     /* L   */
+    int32_t head_dim;    /* d   */
+    sdattn_dtype dtype;
+    float softmax_scale; /* <= 0: 1/sqrt(d) */
+} sdattn_problem;
+
+typedef enum { SDATTN_BUDGET_TOPK = 0, SDATTN_BUDGET_MASS = 1 } sdattn_budget_kind;
+
+/*
+ * Block budget.
+ *   TOPK: every row keeps k = max(1, ceil(keep_frac * nKB - 1e-9)) blocks
+ *         (clamped to nKB), the blocks of largest pooled mass, ties toward
+ *         the lower block index.  0 < keep_frac <= 1.
+ *   MASS: every row keeps the shortest prefix of its blocks, ordered by
+ *         (pooled mass desc, index asc), whose cumulative mass reaches tau*;
+ *         tau* = mass unless that would make the mean kept fraction over all
+ *         rows exceed max_mean_density, in which case tau* is the largest
+ *         cumulative-mass value of any row, not above `mass`, that keeps the
+ *         mean within the cap; every row keeps at least one block.
+ *         0 < mass <= 1, 0 < max_mean_density <= 1 (1 = no cap).  The number
+ *         of kept blocks is at most max(rows, floor(max_mean_density *
+ *         rows * nKB + 1e-9)).
+ * Pooled mass of row (b, h, I): softmax over J of scale * <Qp[I], Kp[J]>,
+ * with Qp, Kp the means of the query / key tokens of each block.
+ */
+typedef struct {
+    sdattn_budget_kind kind;
+    double keep_frac;
+    double mass;
+    double max_mean_density;
+} sdattn_budget;
+
+/* ABI version of the loaded library (SDATTN_ABI_VERSION). */
+SDATTN_API int sdattn_abi_version(void);
+
+/* Static name of a status code ("SDATTN_OK", ...); never NULL. */
+SDATTN_API const char* sdattn_status_string(sdattn_status s);
+
+/* Thread-local detail of the last failing call on this thread ("" if none).
+ * The pointer stays valid until the next failing call on the same thread. */
+SDATTN_API const char* sdattn_last_error(void);
+
+/*
+ * Dense bidirectional attention (SparseD, abstract: full attention in the
+ * early denoising steps; the FlashAttention baseline of all three methods).
+ * For every query row i of head h over all L keys of kv head g(h):
+ *   o_i = sum_j softmax_j(scale * q_i . k_j) v_j,  lse_i = ln sum_j exp(scale * q_i . k_j).
+ * q, k, v, o: required device pointers (layout above).  lse: optional
+ * (NULL = not written).  bf16 uses bf16 MFMA with fp32 accumulation and
+ * bf16 probabilities; fp32 uses fp32 arithmetic throughout.
+ */
+SDATTN_API sdattn_status sdattn_forward_dense(const sdattn_problem* p, const void* q, const void* k,
+                                   const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Workspace bytes and the worst-case number of kept blocks (col_idx
+ * capacity) for sdattn_select_blocks with this problem, block shape and
+ * budget.  Host only; synchronous.
+ */
+SDATTN_API sdattn_status sdattn_select_blocks_workspace(const sdattn_problem* p, int32_t block_q,
+                                             int32_t block_k, const sdattn_budget* budget,
+                                             size_t* ws_bytes, int64_t* max_nnz);
+
+/*
+ * Head-specific block pattern from pooled scores (SparseD, abstract;
+ * Step-dLLM, Abstract): mean-pool query and key blocks, score every (I, J)
+ * pair, softmax over J, and keep blocks under the budget.  Writes row_ptr
+ * [rows + 1] and col_idx [nnz] (CSR above, rows ascending).  col_capacity
+ * is the number of int32 slots in col_idx; it must be >= max_nnz from the
+ * workspace query.  block_mass (optional, [B][Hq][nQB][nKB] float32)
+ * receives the pooled mass.  ws/ws_bytes: device workspace from
+ * sdattn_select_blocks_workspace (ws may be NULL when ws_bytes is 0).
+ * Selection is made in fp32: candidates whose mass lies within ~1e-6
+ * relative of a row's cut may differ from an exact-arithmetic selection.
+ * Limit: nKB <= 1024 (SDATTN_ERR_UNSUPPORTED beyond).
+ */
+SDATTN_API sdattn_status sdattn_select_blocks(const sdattn_problem* p, const void* q, const void* k,
+                                   int32_t block_q, int32_t block_k, const sdattn_budget* budget,
+                                   int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                   float* block_mass, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block-sparse attention (Step-dLLM, Abstract: block-sparse attention with a
+ * reused mask).  Query block I of head h attends only the key tokens of the
+ * key blocks listed in its CSR row; an empty row gives o = 0 and
+ * lse = -inf.  row_ptr/col_idx: device CSR (above), not modified.
+ */
+SDATTN_API sdattn_status sdattn_forward_block_sparse(const sdattn_problem* p, const void* q, const void* k,
+                                          const void* v, int32_t block_q, int32_t block_k,
+                                          const int32_t* row_ptr, const int32_t* col_idx,
+                                          void* o, float* lse, void* stream);
+
+/* Workspace bytes for sdattn_select_columns.  Host only. */
+SDATTN_API sdattn_status sdattn_select_columns_workspace(const sdattn_problem* p, int32_t kcol,
+                                              size_t* ws_bytes);
+
+/*
+ * Column pattern from column-summed attention (PulseCol, Abstract).  For kv
+ * head g: C[g, j] = sum over the query heads h of group g and all query rows
+ * i of exp(scale * q_i . k_j - lse_i), lse from the full attention of the
+ * same q, k (sdattn_forward_dense).  Keeps the kcol columns of largest C
+ * (ties toward the lower index), 1 <= kcol <= L, written ascending to
+ * col_idx [B][Hkv][kcol].  col_scores (optional, [B][Hkv][L] float64)
+ * receives C.  Column sums are accumulated in fp64.
+ */
+SDATTN_API sdattn_status sdattn_select_columns(const sdattn_problem* p, const void* q, const void* k,
+                                    const float* lse, int32_t kcol, int32_t* col_idx,
+                                    double* col_scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Column-sparse attention (PulseCol, Abstract): every query of every query
+ * head of group g attends exactly the key tokens col_idx[b][g][0..kcol-1]
+ * (ascending, distinct, each < L).  1 <= kcol <= L.
+ */
+SDATTN_API sdattn_status sdattn_forward_column_sparse(const sdattn_problem* p, const void* q, const void* k,
+                                           const void* v, const int32_t* col_idx, int32_t kcol,
+                                           void* o, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side step-schedule driver.                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef enum { SDATTN_SEL_BLOCKS = 0, SDATTN_SEL_COLUMNS = 1 } sdattn_sel_kind;
+
+typedef enum {
+    SDATTN_ACT_DENSE = 0,         /* dense attention                          */
+    SDATTN_ACT_DENSE_SELECT = 1,  /* dense attention, then a new pattern      */
+    SDATTN_ACT_SELECT_SPARSE = 2, /* new pattern from this step, then sparse  */
+    SDATTN_ACT_SPARSE = 3         /* sparse attention with the cached pattern */
+} sdattn_action;
+
+/*
+ * Schedule (SparseD, abstract: full attention early, pattern computed once
+ * and reused; Step-dLLM, Abstract: refresh at anchor steps; PulseCol,
+ * Abstract: refresh at a few intermediate steps).  Selection steps
+ *   S = {select_step} u {select_step + m*refresh_interval, m >= 1}
+ *       u refresh_steps[0..n_refresh_steps-1], all < total_steps.
+ * Step t in S is DENSE_SELECT if t < dense_steps or (refresh_dense and
+ * t > select_step), else SELECT_SPARSE.  Step t not in S is DENSE if
+ * t < dense_steps, else SPARSE.  Requires select_step <= dense_steps.
+ * Columns (sel = SDATTN_SEL_COLUMNS) need refresh_dense = 1, because the
+ * column scores use the dense pass's lse; kcol = max(1, ceil(
+ * column_keep_frac * L - 1e-9)).  A new pattern applies from the step that
+ * builds it (SELECT_SPARSE) or from the next step (DENSE_SELECT).
+ */
+typedef struct {
+    int32_t total_steps;
+    int32_t dense_steps;
+    int32_t select_step;
+    int32_t refresh_interval;       /* 0 = none */
+    const int32_t* refresh_steps;   /* host array, copied at create; may be NULL */
+    int32_t n_refresh_steps;
+    int32_t refresh_dense;
+    sdattn_sel_kind sel;
+    int32_t block_q, block_k;       /* blocks only */
+    sdattn_budget budget;           /* blocks only */
+    double column_keep_frac;        /* columns only */
+} sdattn_schedule_desc;
+
+typedef struct sdattn_schedule sdattn_schedule; /* opaque */
+
+/* Validates, copies the descriptor and allocates the pattern buffers and
+ * workspace on the current device.  *out = NULL on error. */
+SDATTN_API sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_schedule_desc* desc,
+                                     sdattn_schedule** out);
+
+/* Action of step `step` (0 <= step < total_steps).  Pure host. */
+SDATTN_API sdattn_status sdattn_schedule_action(const sdattn_schedule* s, int32_t step, sdattn_action* out);
+
+/*
+ * Runs denoising step `step`: enqueues the step's kernels on `stream`.
+ * o required; lse optional (the handle keeps its own buffer when NULL).
+ * Steps may be run in any order, but a SPARSE step fails with
+ * SDATTN_ERR_STATE if no pattern has been built yet; a failed step leaves
+ * the cached pattern and step counters unchanged.
+ */
+SDATTN_API sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void* q,
+                                   const void* k, const void* v, void* o, float* lse,
+                                   void* stream);
+
+/* Borrowed device pointers of the cached pattern (valid until destroy):
+ * blocks -> CSR row_ptr and col_idx; columns -> row_ptr = NULL and col_idx
+ * [B][Hkv][kcol].  *nnz_capacity = int32 slots of col_idx.  Fails with
+ * SDATTN_ERR_STATE before the first selection. */
+SDATTN_API sdattn_status sdattn_schedule_mask(const sdattn_schedule* s, const int32_t** row_ptr,
+                                   const int32_t** col_idx, int64_t* nnz_capacity);
+
+/* Counters: number of steps run by action (4 entries, indexed by
+ * sdattn_action) and the step of the last selection (-1 if none). */
+SDATTN_API sdattn_status sdattn_schedule_stats(const sdattn_schedule* s, int64_t counts[4],
+                                    int32_t* last_select_step);
+
+/* Frees the handle and its device buffers (NULL is a no-op).  The caller
+ * must make sure no enqueued step still uses them (synchronise first). */
+SDATTN_API void sdattn_schedule_destroy(sdattn_schedule* s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDATTN_H */

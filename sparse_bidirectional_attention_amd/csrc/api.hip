@@ -1,0 +1,224 @@
+// C ABI of the library: argument checks on the host, then kernel launches on
+// the caller's stream.  Also provides the HIP backend of the schedule driver.
+
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "host_common.h"
+#include "launch.h"
+#include "schedule.h"
+
+using namespace sdattn;
+
+namespace {
+
+sdattn_status hip_fail(hipError_t e, const char* what) {
+    std::string m = what;
+    m += ": ";
+    m += hipGetErrorString(e);
+    return fail(SDATTN_ERR_HIP, m);
+}
+
+AttnShape shape_of(const Problem& pr) { return AttnShape{pr.B, pr.Hq, pr.Hkv, pr.L, pr.D, pr.scale}; }
+
+sdattn_status check_tensors(const Problem& pr, const void* q, const void* k, const void* v, const void* o) {
+    if (pr.L == 0) return SDATTN_OK;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return fail(SDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+    return SDATTN_OK;
+}
+
+sdattn_status run_attention(AttnMode mode, const Problem& pr, const void* q, const void* k, const void* v,
+                            void* o, float* lse, const SparseIndex& ix, void* stream, const char* name) {
+    if (pr.L == 0) return SDATTN_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = pr.dtype == SDATTN_BF16 ? launch_flash_bf16(mode, shape_of(pr), q, k, v, o, lse, ix, st)
+                                           : launch_flash_f32(mode, shape_of(pr), q, k, v, o, lse, ix, st);
+    if (e != hipSuccess) return hip_fail(e, name);
+    return SDATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sdattn_status sdattn_forward_dense(const sdattn_problem* p, const void* q, const void* k, const void* v,
+                                   void* o, float* lse, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    s = check_tensors(pr, q, k, v, o);
+    if (s != SDATTN_OK) return s;
+    return run_attention(MODE_DENSE, pr, q, k, v, o, lse, SparseIndex{}, stream, "sdattn_forward_dense");
+}
+
+sdattn_status sdattn_select_blocks_workspace(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                             const sdattn_budget* budget, size_t* ws_bytes, int64_t* max_nnz) {
+    if (ws_bytes == nullptr || max_nnz == nullptr) return fail(SDATTN_ERR_NULL, "ws_bytes and max_nnz must be non-NULL");
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    BlockPlan plan;
+    s = check_blocks(pr, block_q, block_k, budget, &plan);
+    if (s != SDATTN_OK) return s;
+    *ws_bytes = pr.L == 0 ? 0 : select_blocks_ws_layout(shape_of(pr), block_q, block_k, plan.mass).total;
+    *max_nnz = plan.max_nnz;
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_select_blocks(const sdattn_problem* p, const void* q, const void* k, int32_t block_q,
+                                   int32_t block_k, const sdattn_budget* budget, int32_t* row_ptr,
+                                   int32_t* col_idx, int64_t col_capacity, float* block_mass, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    BlockPlan plan;
+    s = check_blocks(pr, block_q, block_k, budget, &plan);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (q == nullptr || k == nullptr || row_ptr == nullptr || col_idx == nullptr)
+        return fail(SDATTN_ERR_NULL, "q, k, row_ptr and col_idx must be non-NULL");
+    if (col_capacity < plan.max_nnz) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "col_capacity %lld < worst-case kept blocks %lld", static_cast<long long>(col_capacity),
+                 static_cast<long long>(plan.max_nnz));
+        return fail(SDATTN_ERR_CAPACITY, buf);
+    }
+    const size_t need = select_blocks_ws_layout(shape_of(pr), block_q, block_k, plan.mass).total;
+    if (ws_bytes < need || (need > 0 && ws == nullptr)) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "workspace of %zu bytes < required %zu", ws_bytes, need);
+        return fail(SDATTN_ERR_WORKSPACE, buf);
+    }
+    hipError_t e = launch_select_blocks(shape_of(pr), pr.dtype == SDATTN_BF16, q, k, block_q, block_k, plan.mass,
+                                        static_cast<int>(plan.topk), static_cast<float>(budget->mass),
+                                        plan.cap_extra, row_ptr, col_idx, block_mass, ws,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdattn_select_blocks");
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_forward_block_sparse(const sdattn_problem* p, const void* q, const void* k, const void* v,
+                                          int32_t block_q, int32_t block_k, const int32_t* row_ptr,
+                                          const int32_t* col_idx, void* o, float* lse, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if ((block_q != 64 && block_q != 128) || (block_k != 64 && block_k != 128))
+        return fail(SDATTN_ERR_UNSUPPORTED, "block_q and block_k must be 64 or 128");
+    s = check_tensors(pr, q, k, v, o);
+    if (s != SDATTN_OK) return s;
+    if (pr.L > 0 && (row_ptr == nullptr || col_idx == nullptr))
+        return fail(SDATTN_ERR_NULL, "row_ptr and col_idx must be non-NULL");
+    SparseIndex ix;
+    ix.block_q = block_q;
+    ix.block_k = block_k;
+    ix.row_ptr = row_ptr;
+    ix.col_idx = col_idx;
+    return run_attention(MODE_BLOCK, pr, q, k, v, o, lse, ix, stream, "sdattn_forward_block_sparse");
+}
+
+sdattn_status sdattn_select_columns_workspace(const sdattn_problem* p, int32_t kcol, size_t* ws_bytes) {
+    if (ws_bytes == nullptr) return fail(SDATTN_ERR_NULL, "ws_bytes must be non-NULL");
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if (pr.L > 0 && (kcol < 1 || kcol > pr.L)) return fail(SDATTN_ERR_BUDGET, "kcol must be in [1, seq_len]");
+    *ws_bytes = pr.L == 0 ? 0 : select_columns_ws_bytes(shape_of(pr));
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_select_columns(const sdattn_problem* p, const void* q, const void* k, const float* lse,
+                                    int32_t kcol, int32_t* col_idx, double* col_scores, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (kcol < 1 || kcol > pr.L) return fail(SDATTN_ERR_BUDGET, "kcol must be in [1, seq_len]");
+    if (q == nullptr || k == nullptr || lse == nullptr || col_idx == nullptr)
+        return fail(SDATTN_ERR_NULL, "q, k, lse and col_idx must be non-NULL");
+    const size_t need = select_columns_ws_bytes(shape_of(pr));
+    if (ws_bytes < need || ws == nullptr) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "workspace of %zu bytes < required %zu", ws_bytes, need);
+        return fail(SDATTN_ERR_WORKSPACE, buf);
+    }
+    hipError_t e = launch_select_columns(shape_of(pr), pr.dtype == SDATTN_BF16, q, k, lse, kcol, col_idx, col_scores,
+                                         ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdattn_select_columns");
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_forward_column_sparse(const sdattn_problem* p, const void* q, const void* k, const void* v,
+                                           const int32_t* col_idx, int32_t kcol, void* o, float* lse,
+                                           void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (kcol < 1 || kcol > pr.L) return fail(SDATTN_ERR_BUDGET, "kcol must be in [1, seq_len]");
+    s = check_tensors(pr, q, k, v, o);
+    if (s != SDATTN_OK) return s;
+    if (col_idx == nullptr) return fail(SDATTN_ERR_NULL, "col_idx must be non-NULL");
+    SparseIndex ix;
+    ix.col_idx = col_idx;
+    ix.kcol = kcol;
+    return run_attention(MODE_COLUMN, pr, q, k, v, o, lse, ix, stream, "sdattn_forward_column_sparse");
+}
+
+}  // extern "C"
+
+// ---- HIP backend of the schedule driver ------------------------------------
+
+namespace {
+
+sdattn_status be_dense(void*, const sdattn_problem* p, const void* q, const void* k, const void* v, void* o,
+                       float* lse, void* st) {
+    return sdattn_forward_dense(p, q, k, v, o, lse, st);
+}
+sdattn_status be_select_blocks(void*, const sdattn_problem* p, const void* q, const void* k, int32_t bq, int32_t bk,
+                               const sdattn_budget* b, int32_t* rp, int32_t* ci, int64_t cap, void* ws, size_t wsb,
+                               void* st) {
+    return sdattn_select_blocks(p, q, k, bq, bk, b, rp, ci, cap, nullptr, ws, wsb, st);
+}
+sdattn_status be_block_sparse(void*, const sdattn_problem* p, const void* q, const void* k, const void* v, int32_t bq,
+                              int32_t bk, const int32_t* rp, const int32_t* ci, void* o, float* lse, void* st) {
+    return sdattn_forward_block_sparse(p, q, k, v, bq, bk, rp, ci, o, lse, st);
+}
+sdattn_status be_select_columns(void*, const sdattn_problem* p, const void* q, const void* k, const float* lse,
+                                int32_t kcol, int32_t* ci, void* ws, size_t wsb, void* st) {
+    return sdattn_select_columns(p, q, k, lse, kcol, ci, nullptr, ws, wsb, st);
+}
+sdattn_status be_column_sparse(void*, const sdattn_problem* p, const void* q, const void* k, const void* v,
+                               const int32_t* ci, int32_t kcol, void* o, float* lse, void* st) {
+    return sdattn_forward_column_sparse(p, q, k, v, ci, kcol, o, lse, st);
+}
+sdattn_status be_ws_blocks(void*, const sdattn_problem* p, int32_t bq, int32_t bk, const sdattn_budget* b, size_t* ws,
+                           int64_t* nnz) {
+    return sdattn_select_blocks_workspace(p, bq, bk, b, ws, nnz);
+}
+sdattn_status be_ws_columns(void*, const sdattn_problem* p, int32_t kcol, size_t* ws) {
+    return sdattn_select_columns_workspace(p, kcol, ws);
+}
+sdattn_status be_alloc(void*, size_t bytes, void** out) {
+    hipError_t e = hipMalloc(out, bytes ? bytes : 1);
+    if (e != hipSuccess) {
+        *out = nullptr;
+        return hip_fail(e, "hipMalloc");
+    }
+    return SDATTN_OK;
+}
+void be_release(void*, void* ptr) { (void)hipFree(ptr); }
+
+const Backend kHipBackend = {nullptr,          be_dense,        be_select_blocks, be_block_sparse, be_select_columns,
+                             be_column_sparse, be_ws_blocks,    be_ws_columns,    be_alloc,        be_release};
+
+}  // namespace
+
+namespace sdattn {
+const Backend& default_backend() { return kHipBackend; }
+}  // namespace sdattn

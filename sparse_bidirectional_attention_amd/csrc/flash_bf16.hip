@@ -1,0 +1,373 @@
+// Bidirectional flash-style attention forward for bf16 inputs on gfx950.
+//
+// One kernel template serves the three attention forms of the library:
+//   dense         every query attends all L keys (SparseD, abstract: full
+//                 attention in the early steps);
+//   block-sparse  query block I of head h attends the key tokens of the key
+//                 blocks in its CSR row (Step-dLLM, Abstract);
+//   column-sparse every query of group g attends a shared list of key
+//                 tokens (PulseCol, Abstract).
+// Each form streams 64-key tiles; only where the tile's rows come from
+// differs.
+//
+// Work decomposition: one workgroup per (batch, head, tile of BQ queries),
+// NW = BQ/32 waves, each wave owning 32 query rows.  Per 64-key tile:
+//   * K (64 x d) and V (64 x d) are read from HBM with 16-byte coalesced
+//     loads into registers one tile ahead, then written to LDS: K row-major,
+//     V transposed (d x 64) so both MFMA operands are 16-byte LDS reads.
+//     Double-buffered LDS, one barrier per tile.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (two 32x32 blocks per wave);
+//     computing the transpose puts one query per lane, so the online
+//     softmax max needs a single cross-half exchange and the row sums none.
+//   * P^T is packed to bf16 straight from the MFMA accumulator layout; the
+//     V^T tile is stored in LDS in the matching key order, so
+//     O^T += V^T P^T needs no register shuffles.
+//   * The running max is only raised when it grows by more than 2^8 in
+//     probability units (rescaling O is skipped otherwise; exact, since the
+//     final normalisation uses the same reference max).
+// The log-sum-exp (natural log) is written per query row.
+
+#include "common.h"
+#include "launch.h"
+
+namespace sdattn {
+namespace {
+
+struct FlashParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* o;
+    float* lse;
+    const int32_t* row_ptr;
+    const int32_t* col_idx;
+    int Hq, Hkv, L, group, n_qtiles, n_items, block_k, kcol, xcd_group;
+    float c;      // scale * log2(e)
+    float scale;  // softmax scale
+    float thr;    // lazy-rescale threshold in raw score units
+};
+
+__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+
+template <int D, int NW, int MODE>
+__global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
+    constexpr int KT = 64;
+    constexpr int T = NW * 64;
+    constexpr int DK = D / 16;
+    constexpr int ND = D / 32;
+    constexpr int KROW = D * 2;
+    constexpr int KBYTES = KT * KROW;
+    constexpr int VROW = KT * 2;
+    constexpr int VBYTES = D * VROW;
+    constexpr int BUF = KBYTES + VBYTES;
+    constexpr int KUNITS = D / 8;
+    constexpr int KMASK = KUNITS - 1;
+    constexpr int K_LOADS = KT * KUNITS / T;
+    constexpr int V_GROUPS = (KT / 4) * KUNITS;
+    constexpr int V_LOADS = (V_GROUPS + T - 1) / T;
+    constexpr int OPITCH = D * 2 + 16;
+    static_assert(K_LOADS * T == KT * KUNITS, "K tile must split evenly");
+    static_assert(NW * 32 * OPITCH <= 2 * BUF, "epilogue staging fits in LDS");
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hl = lane >> 5;
+
+    const int item = xcd_remap(blockIdx.x, p.n_items, p.xcd_group);
+    const int qt = item % p.n_qtiles;
+    const int bh = item / p.n_qtiles;
+    const int h = bh % p.Hq;
+    const int b = bh / p.Hq;
+    const int g = h / p.group;
+    const int L = p.L;
+    const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * L * D;
+    const uint16_t* __restrict__ kh = p.k + kvoff;
+    const uint16_t* __restrict__ vh = p.v + kvoff;
+    const int q0 = qt * (NW * 32);
+
+    // ---- tile source ------------------------------------------------------
+    int n_tiles = 0, e0 = 0, sub_shift = 0;
+    const int32_t* cb = nullptr;
+    if constexpr (MODE == MODE_DENSE) {
+        n_tiles = (L + KT - 1) / KT;
+    } else if constexpr (MODE == MODE_BLOCK) {
+        const int r = bh * p.n_qtiles + qt;
+        e0 = p.row_ptr[r];
+        sub_shift = p.block_k == 128 ? 1 : 0;
+        n_tiles = (p.row_ptr[r + 1] - e0) << sub_shift;
+    } else {
+        cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
+        n_tiles = (p.kcol + KT - 1) / KT;
+    }
+    // base key of tile t (dense / block) or its first column entry (column);
+    // nvalid = number of real keys in the tile.
+    auto tile_base = [&](int t, int& nvalid) -> int {
+        if constexpr (MODE == MODE_COLUMN) {
+            nvalid = min(KT, p.kcol - t * KT);
+            return t * KT;
+        } else {
+            int base;
+            if constexpr (MODE == MODE_DENSE) {
+                base = t * KT;
+            } else {
+                const int J = p.col_idx[e0 + (t >> sub_shift)];
+                base = J * p.block_k + ((t & sub_shift) ? KT : 0);
+            }
+            nvalid = max(0, min(KT, L - base));
+            return base;
+        }
+    };
+    auto key_row = [&](int base, int nvalid, int i) -> int {
+        // clamped so that any index stays inside the tensor
+        if constexpr (MODE == MODE_COLUMN) {
+            return min(max(cb[base + min(i, nvalid - 1)], 0), L - 1);
+        } else {
+            return min(max(base + i, 0), L - 1);
+        }
+    };
+
+    u32x4 kreg[K_LOADS];
+    u32x4 vreg[V_LOADS][4];
+    auto load_tile = [&](int t) {
+        int nv;
+        const int base = tile_base(t, nv);
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) {
+            const int cid = tid + i * T;
+            const int r = cid / KUNITS, u = cid % KUNITS;
+            kreg[i] = *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(key_row(base, nv, r)) * D + u * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) {
+            const int gid = tid + i * T;
+            if (V_GROUPS % T == 0 || gid < V_GROUPS) {
+                const int kg = gid / KUNITS, u = gid % KUNITS;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    vreg[i][c] = *reinterpret_cast<const u32x4*>(
+                        vh + static_cast<size_t>(key_row(base, nv, 4 * kg + c)) * D + u * 8);
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        char* Kb = smem + buf * BUF;
+        char* Vb = Kb + KBYTES;
+#pragma unroll
+        for (int i = 0; i < K_LOADS; ++i) {
+            const int cid = tid + i * T;
+            const int r = cid / KUNITS, u = cid % KUNITS;
+            *reinterpret_cast<u32x4*>(Kb + r * KROW + ((u ^ (r & KMASK)) << 4)) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < V_LOADS; ++i) {
+            const int gid = tid + i * T;
+            if (V_GROUPS % T == 0 || gid < V_GROUPS) {
+                const int kg = gid / KUNITS, u = gid % KUNITS;
+                // keys 4kg..4kg+3 go to consecutive LDS positions; inside each
+                // 16-key chunk the two 4-key halves of each 8-key run are
+                // interleaved to match the MFMA accumulator's key order.
+                const int kk = kg & 3;
+                const int unit_v = (kg >> 2) * 2 + (kk & 1);
+                const int half = kk >> 1;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int d = u * 8 + j;
+                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = __builtin_amdgcn_perm(vreg[i][1][j >> 1], vreg[i][0][j >> 1], sel);
+                    const uint32_t hi = __builtin_amdgcn_perm(vreg[i][3][j >> 1], vreg[i][2][j >> 1], sel);
+                    u32x2 w = {lo, hi};
+                    *reinterpret_cast<u32x2*>(Vb + d * VROW + ((unit_v ^ vswz(d)) << 4) + half * 8) = w;
+                }
+            }
+        }
+    };
+
+    // ---- Q operand (registers, whole kernel) -------------------------------
+    bf16x8 qreg[DK];
+    {
+        const int qrow = min(q0 + wave * 32 + l32, L - 1);
+        const uint16_t* qp = p.q + (static_cast<size_t>(b) * p.Hq + h) * L * D + static_cast<size_t>(qrow) * D;
+#pragma unroll
+        for (int st = 0; st < DK; ++st)
+            qreg[st] = *reinterpret_cast<const bf16x8*>(qp + 16 * st + 8 * hl);
+    }
+
+    f32x16 oacc[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+    float m_used = -kInf;
+    float l_acc = 0.f;
+    const float c = p.c;
+
+    if (n_tiles > 0) {
+        load_tile(0);
+        store_tile(0);
+    }
+    __syncthreads();
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int buf = t & 1;
+        const bool has_next = t + 1 < n_tiles;
+        if (has_next) load_tile(t + 1);
+        int nvalid;
+        tile_base(t, nvalid);
+
+        const char* Kb = smem + buf * BUF;
+        const char* Vb = Kb + KBYTES;
+
+        // S^T = K Q^T : two 32-key x 32-query blocks
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < DK; ++st) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int row = kb * 32 + l32;
+                const int unit = 2 * st + hl;
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + row * KROW + ((unit ^ (row & KMASK)) << 4));
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[kb], 0, 0, 0);
+            }
+        }
+        if (nvalid < KT) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    if (key >= nvalid) sacc[kb][r] = -kInf;
+                }
+        }
+
+        // online softmax (one query per lane; partner lane ^32 holds the rest)
+        float mt = -kInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+        mt = max_with_half_swap(mt);
+        const float mnew = fmaxf(m_used, mt);
+        const bool need = mnew > m_used + p.thr;
+        if (__any(need)) {
+            const float alpha = need ? exp2_fast((m_used - mnew) * c) : 1.f;
+            m_used = need ? mnew : m_used;
+            l_acc *= alpha;
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float mc = (m_used > -kInf) ? m_used * c : 0.f;
+        uint32_t pk[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = exp2_fast(fmaf(sacc[kb][r], c, -mc));
+                const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], c, -mc));
+                l_acc += p0 + p1;
+                pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+            }
+
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+            const int drow = db * 32 + l32;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int unit = 2 * (2 * kb + m) + hl;
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + drow * VROW + ((unit ^ vswz(drow)) << 4));
+                    u32x4 bb = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bb), oacc[db], 0, 0, 0);
+                }
+        }
+
+        if (has_next) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
+    const float lt = sum_with_half_swap(l_acc);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    char* ob = smem + wave * 32 * OPITCH;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = db * 32 + 8 * rq + 4 * hl;
+            u32x2 w = {pack_bf16x2(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv),
+                       pack_bf16x2(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv)};
+            *reinterpret_cast<u32x2*>(ob + l32 * OPITCH + d0 * 2) = w;
+        }
+    __syncthreads();
+    const size_t obase = (static_cast<size_t>(b) * p.Hq + h) * L;
+    constexpr int CHUNKS = 32 * D * 2 / 16;
+#pragma unroll
+    for (int i = 0; i < CHUNKS / 64; ++i) {
+        const int cid = lane + 64 * i;
+        const int row = cid / KUNITS, u = cid % KUNITS;
+        const int qi = q0 + wave * 32 + row;
+        if (qi < L) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + u * 16);
+            *reinterpret_cast<u32x4*>(p.o + (obase + qi) * D + u * 8) = val;
+        }
+    }
+    if (p.lse != nullptr && hl == 0) {
+        const int qi = q0 + wave * 32 + l32;
+        if (qi < L) p.lse[obase + qi] = lt > 0.f ? m_used * p.scale + __logf(lt) : -kInf;
+    }
+}
+
+template <int D, int NW>
+hipError_t launch_mode(AttnMode mode, const FlashParams& fp, hipStream_t st) {
+    dim3 grid(fp.n_items), block(NW * 64);
+    switch (mode) {
+        case MODE_DENSE: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, MODE_DENSE>), grid, block, 0, st, fp); break;
+        case MODE_BLOCK: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, MODE_BLOCK>), grid, block, 0, st, fp); break;
+        case MODE_COLUMN: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, MODE_COLUMN>), grid, block, 0, st, fp); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, const void* k,
+                             const void* v, void* o, float* lse, const SparseIndex& ix,
+                             hipStream_t st) {
+    const int bq = mode == MODE_BLOCK ? ix.block_q : 128;
+    FlashParams fp{};
+    fp.q = static_cast<const uint16_t*>(q);
+    fp.k = static_cast<const uint16_t*>(k);
+    fp.v = static_cast<const uint16_t*>(v);
+    fp.o = static_cast<uint16_t*>(o);
+    fp.lse = lse;
+    fp.row_ptr = ix.row_ptr;
+    fp.col_idx = ix.col_idx;
+    fp.Hq = s.Hq;
+    fp.Hkv = s.Hkv;
+    fp.L = s.L;
+    fp.group = s.Hq / s.Hkv;
+    fp.n_qtiles = (s.L + bq - 1) / bq;
+    fp.n_items = s.B * s.Hq * fp.n_qtiles;
+    fp.block_k = ix.block_k;
+    fp.kcol = ix.kcol;
+    fp.xcd_group = (fp.n_qtiles % 8 == 0) ? fp.n_qtiles : 0;
+    fp.scale = s.scale;
+    fp.c = s.scale * kLog2e;
+    fp.thr = 8.0f / fp.c;
+    if (fp.n_items == 0) return hipSuccess;
+    if (s.D == 128) return bq == 64 ? launch_mode<128, 2>(mode, fp, st) : launch_mode<128, 4>(mode, fp, st);
+    return bq == 64 ? launch_mode<64, 2>(mode, fp, st) : launch_mode<64, 4>(mode, fp, st);
+}
+
+}  // namespace sdattn

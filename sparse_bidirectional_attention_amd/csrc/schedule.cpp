@@ -1,0 +1,243 @@
+// Host-side step-schedule driver (SparseD, abstract: full attention in the
+// early steps, then a pattern computed once and reused; Step-dLLM, Abstract:
+// refresh at anchor steps, reuse within each interval; PulseCol, Abstract:
+// column pattern refreshed at a few intermediate steps).
+//
+// The handle owns two pattern buffers: a selection always writes the buffer
+// not in use and the handle switches to it only when every call of the step
+// was accepted, so a failed step leaves the cached pattern untouched.
+
+#include <math.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "schedule.h"
+
+struct sdattn_schedule {
+    sdattn::Backend be;
+    sdattn_problem prob;
+    sdattn::Problem pr;
+    sdattn_schedule_desc desc;
+    std::vector<int32_t> refresh;  // owned copy of desc.refresh_steps
+    // pattern buffers (device)
+    int32_t* row_ptr[2] = {nullptr, nullptr};
+    int32_t* col_idx[2] = {nullptr, nullptr};
+    int64_t nnz_cap = 0;
+    int32_t kcol = 0;
+    int active = -1;  // -1: no pattern yet
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    float* lse = nullptr;  // own lse buffer (columns)
+    int64_t counts[4] = {0, 0, 0, 0};
+    int32_t last_select = -1;
+};
+
+namespace sdattn {
+
+sdattn_action schedule_action_of(const sdattn_schedule_desc& d, int32_t t) {
+    bool in_s = t == d.select_step;
+    if (!in_s && d.refresh_interval > 0 && t > d.select_step)
+        in_s = (t - d.select_step) % d.refresh_interval == 0;
+    if (!in_s && d.refresh_steps != nullptr)
+        for (int i = 0; i < d.n_refresh_steps; ++i) in_s = in_s || d.refresh_steps[i] == t;
+    if (in_s) {
+        const bool dense = t < d.dense_steps || (d.refresh_dense && t > d.select_step);
+        return dense ? SDATTN_ACT_DENSE_SELECT : SDATTN_ACT_SELECT_SPARSE;
+    }
+    return t < d.dense_steps ? SDATTN_ACT_DENSE : SDATTN_ACT_SPARSE;
+}
+
+namespace {
+
+sdattn_status check_desc(const Problem& pr, const sdattn_schedule_desc* d) {
+    if (d == nullptr) return fail(SDATTN_ERR_NULL, "schedule descriptor is NULL");
+    if (d->total_steps < 1) return fail(SDATTN_ERR_SHAPE, "total_steps must be >= 1");
+    if (d->dense_steps < 0 || d->dense_steps > d->total_steps)
+        return fail(SDATTN_ERR_SHAPE, "dense_steps must be in [0, total_steps]");
+    if (d->select_step < 0 || d->select_step >= d->total_steps)
+        return fail(SDATTN_ERR_SHAPE, "select_step must be in [0, total_steps)");
+    if (d->select_step > d->dense_steps)
+        return fail(SDATTN_ERR_SHAPE, "select_step > dense_steps: a sparse step would run before any pattern exists");
+    if (d->refresh_interval < 0) return fail(SDATTN_ERR_SHAPE, "refresh_interval must be >= 0");
+    if (d->n_refresh_steps < 0 || (d->n_refresh_steps > 0 && d->refresh_steps == nullptr))
+        return fail(SDATTN_ERR_NULL, "refresh_steps is NULL but n_refresh_steps > 0");
+    if (d->sel != SDATTN_SEL_BLOCKS && d->sel != SDATTN_SEL_COLUMNS)
+        return fail(SDATTN_ERR_SHAPE, "unknown selector kind");
+    if (d->sel == SDATTN_SEL_COLUMNS) {
+        if (!d->refresh_dense)
+            return fail(SDATTN_ERR_SHAPE, "column selection needs refresh_dense = 1 (scores use the dense lse)");
+        if (!(d->column_keep_frac > 0.0 && d->column_keep_frac <= 1.0))
+            return fail(SDATTN_ERR_BUDGET, "column_keep_frac must be in (0, 1]");
+        // the first column selection needs a dense pass for its lse
+        if (d->select_step >= d->dense_steps)
+            return fail(SDATTN_ERR_SHAPE, "column selection step must be a dense step (select_step < dense_steps)");
+    }
+    (void)pr;
+    return SDATTN_OK;
+}
+
+}  // namespace
+}  // namespace sdattn
+
+using namespace sdattn;
+
+extern "C" {
+
+sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_schedule_desc* desc,
+                                     sdattn_schedule** out) {
+    if (out == nullptr) return fail(SDATTN_ERR_NULL, "out is NULL");
+    *out = nullptr;
+    Problem pr;
+    sdattn_status st = check_problem(p, &pr);
+    if (st != SDATTN_OK) return st;
+    st = check_desc(pr, desc);
+    if (st != SDATTN_OK) return st;
+    sdattn_schedule* s = new (std::nothrow) sdattn_schedule();
+    if (s == nullptr) return fail(SDATTN_ERR_SHAPE, "out of host memory");
+    s->be = default_backend();
+    s->prob = *p;
+    s->pr = pr;
+    s->desc = *desc;
+    if (desc->n_refresh_steps > 0) s->refresh.assign(desc->refresh_steps, desc->refresh_steps + desc->n_refresh_steps);
+    s->desc.refresh_steps = s->refresh.empty() ? nullptr : s->refresh.data();
+    s->desc.n_refresh_steps = static_cast<int32_t>(s->refresh.size());
+
+    auto cleanup_fail = [&](sdattn_status e) {
+        sdattn_schedule_destroy(s);
+        return e;
+    };
+    size_t rp_bytes = 0, ci_bytes = 0;
+    if (desc->sel == SDATTN_SEL_BLOCKS) {
+        BlockPlan plan;
+        st = check_blocks(pr, desc->block_q, desc->block_k, &desc->budget, &plan);
+        if (st != SDATTN_OK) return cleanup_fail(st);
+        int64_t max_nnz = 0;
+        st = s->be.workspace_blocks(s->be.ctx, p, desc->block_q, desc->block_k, &desc->budget, &s->ws_bytes, &max_nnz);
+        if (st != SDATTN_OK) return cleanup_fail(st);
+        s->nnz_cap = std::max<int64_t>(max_nnz, 1);
+        rp_bytes = static_cast<size_t>(plan.rows + 1) * sizeof(int32_t);
+        ci_bytes = static_cast<size_t>(s->nnz_cap) * sizeof(int32_t);
+    } else {
+        s->kcol = static_cast<int32_t>(count_from_fraction(desc->column_keep_frac, std::max(pr.L, 1)));
+        st = s->be.workspace_columns(s->be.ctx, p, s->kcol, &s->ws_bytes);
+        if (st != SDATTN_OK) return cleanup_fail(st);
+        s->nnz_cap = static_cast<int64_t>(pr.B) * pr.Hkv * s->kcol;
+        ci_bytes = static_cast<size_t>(std::max<int64_t>(s->nnz_cap, 1)) * sizeof(int32_t);
+        const size_t lse_bytes = static_cast<size_t>(pr.B) * pr.Hq * std::max(pr.L, 1) * sizeof(float);
+        st = s->be.alloc(s->be.ctx, lse_bytes, reinterpret_cast<void**>(&s->lse));
+        if (st != SDATTN_OK) return cleanup_fail(st);
+    }
+    for (int i = 0; i < 2; ++i) {
+        if (rp_bytes) {
+            st = s->be.alloc(s->be.ctx, rp_bytes, reinterpret_cast<void**>(&s->row_ptr[i]));
+            if (st != SDATTN_OK) return cleanup_fail(st);
+        }
+        st = s->be.alloc(s->be.ctx, ci_bytes, reinterpret_cast<void**>(&s->col_idx[i]));
+        if (st != SDATTN_OK) return cleanup_fail(st);
+    }
+    if (s->ws_bytes) {
+        st = s->be.alloc(s->be.ctx, s->ws_bytes, &s->ws);
+        if (st != SDATTN_OK) return cleanup_fail(st);
+    }
+    *out = s;
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_schedule_action(const sdattn_schedule* s, int32_t step, sdattn_action* out) {
+    if (s == nullptr || out == nullptr) return fail(SDATTN_ERR_NULL, "schedule or out is NULL");
+    if (step < 0 || step >= s->desc.total_steps) return fail(SDATTN_ERR_SHAPE, "step outside [0, total_steps)");
+    *out = schedule_action_of(s->desc, step);
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void* q, const void* k,
+                                   const void* v, void* o, float* lse, void* stream) {
+    if (s == nullptr) return fail(SDATTN_ERR_NULL, "schedule is NULL");
+    if (step < 0 || step >= s->desc.total_steps) return fail(SDATTN_ERR_SHAPE, "step outside [0, total_steps)");
+    const sdattn_action act = schedule_action_of(s->desc, step);
+    const Backend& be = s->be;
+    const sdattn_problem* p = &s->prob;
+    const bool blocks = s->desc.sel == SDATTN_SEL_BLOCKS;
+    const int next = s->active < 0 ? 0 : 1 - s->active;
+    sdattn_status st = SDATTN_OK;
+    switch (act) {
+        case SDATTN_ACT_DENSE:
+            st = be.dense(be.ctx, p, q, k, v, o, lse, stream);
+            break;
+        case SDATTN_ACT_DENSE_SELECT:
+            if (blocks) {
+                st = be.dense(be.ctx, p, q, k, v, o, lse, stream);
+                if (st == SDATTN_OK)
+                    st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
+                                          s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
+            } else {
+                float* l = lse != nullptr ? lse : s->lse;
+                st = be.dense(be.ctx, p, q, k, v, o, l, stream);
+                if (st == SDATTN_OK)
+                    st = be.select_columns(be.ctx, p, q, k, l, s->kcol, s->col_idx[next], s->ws, s->ws_bytes, stream);
+            }
+            if (st == SDATTN_OK) {
+                s->active = next;
+                s->last_select = step;
+            }
+            break;
+        case SDATTN_ACT_SELECT_SPARSE:
+            if (!blocks) return fail(SDATTN_ERR_STATE, "column selection needs a dense step");
+            st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
+                                  s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
+            if (st == SDATTN_OK)
+                st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[next],
+                                     s->col_idx[next], o, lse, stream);
+            if (st == SDATTN_OK) {
+                s->active = next;
+                s->last_select = step;
+            }
+            break;
+        case SDATTN_ACT_SPARSE:
+            if (s->active < 0) return fail(SDATTN_ERR_STATE, "sparse step before any pattern was selected");
+            if (blocks)
+                st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[s->active],
+                                     s->col_idx[s->active], o, lse, stream);
+            else
+                st = be.column_sparse(be.ctx, p, q, k, v, s->col_idx[s->active], s->kcol, o, lse, stream);
+            break;
+    }
+    if (st == SDATTN_OK) s->counts[act] += 1;
+    return st;
+}
+
+sdattn_status sdattn_schedule_mask(const sdattn_schedule* s, const int32_t** row_ptr, const int32_t** col_idx,
+                                   int64_t* nnz_capacity) {
+    if (s == nullptr || row_ptr == nullptr || col_idx == nullptr || nnz_capacity == nullptr)
+        return fail(SDATTN_ERR_NULL, "schedule or an output pointer is NULL");
+    if (s->active < 0) return fail(SDATTN_ERR_STATE, "no pattern has been selected yet");
+    *row_ptr = s->row_ptr[s->active];
+    *col_idx = s->col_idx[s->active];
+    *nnz_capacity = s->nnz_cap;
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_schedule_stats(const sdattn_schedule* s, int64_t counts[4], int32_t* last_select_step) {
+    if (s == nullptr || counts == nullptr || last_select_step == nullptr)
+        return fail(SDATTN_ERR_NULL, "schedule or an output pointer is NULL");
+    for (int i = 0; i < 4; ++i) counts[i] = s->counts[i];
+    *last_select_step = s->last_select;
+    return SDATTN_OK;
+}
+
+void sdattn_schedule_destroy(sdattn_schedule* s) {
+    if (s == nullptr) return;
+    const Backend& be = s->be;
+    for (int i = 0; i < 2; ++i) {
+        if (s->row_ptr[i]) be.release(be.ctx, s->row_ptr[i]);
+        if (s->col_idx[i]) be.release(be.ctx, s->col_idx[i]);
+    }
+    if (s->ws) be.release(be.ctx, s->ws);
+    if (s->lse) be.release(be.ctx, s->lse);
+    delete s;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+// Recording fake backend for CPU tests of the schedule driver.
+//
+// Built (with the driver and the argument checks, no HIP) into
+// libsdattn_fake.so.  Every backend call appends a line to a log; a call can
+// be made to fail on purpose; "device" buffers are host allocations whose
+// count is tracked so leaks show up.
+
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <string>
+#include <vector>
+
+#include "schedule.h"
+
+namespace {
+
+std::vector<std::string> g_log;
+int g_calls = 0;
+int g_fail_at = -1;  // 0-based index of the backend compute call that fails
+sdattn_status g_fail_status = SDATTN_ERR_HIP;
+int g_live = 0;
+
+std::string ptr(const void* p) {
+    char b[32];
+    snprintf(b, sizeof b, "%p", p);
+    return b;
+}
+
+sdattn_status record(const std::string& line) {
+    const int idx = g_calls++;
+    if (idx == g_fail_at) {
+        g_log.push_back("FAIL " + line);
+        return sdattn::fail(g_fail_status, "injected failure");
+    }
+    g_log.push_back(line);
+    return SDATTN_OK;
+}
+
+sdattn_status f_dense(void*, const sdattn_problem*, const void*, const void*, const void*, void* o, float* lse,
+                      void*) {
+    return record("dense o=" + ptr(o) + " lse=" + ptr(lse));
+}
+sdattn_status f_select_blocks(void*, const sdattn_problem*, const void*, const void*, int32_t bq, int32_t bk,
+                              const sdattn_budget*, int32_t* rp, int32_t* ci, int64_t cap, void* ws, size_t wsb,
+                              void*) {
+    return record("select_blocks rp=" + ptr(rp) + " ci=" + ptr(ci) + " cap=" + std::to_string(cap) +
+                  " bq=" + std::to_string(bq) + " bk=" + std::to_string(bk));
+}
+sdattn_status f_block_sparse(void*, const sdattn_problem*, const void*, const void*, const void*, int32_t,
+                             int32_t, const int32_t* rp, const int32_t* ci, void* o, float*, void*) {
+    return record("block_sparse rp=" + ptr(rp) + " ci=" + ptr(ci) + " o=" + ptr(o));
+}
+sdattn_status f_select_columns(void*, const sdattn_problem*, const void*, const void*, const float* lse, int32_t kcol,
+                               int32_t* ci, void*, size_t, void*) {
+    return record("select_columns lse=" + ptr(lse) + " ci=" + ptr(ci) + " kcol=" + std::to_string(kcol));
+}
+sdattn_status f_column_sparse(void*, const sdattn_problem*, const void*, const void*, const void*, const int32_t* ci,
+                              int32_t kcol, void* o, float*, void*) {
+    return record("column_sparse ci=" + ptr(ci) + " kcol=" + std::to_string(kcol) + " o=" + ptr(o));
+}
+sdattn_status f_ws_blocks(void*, const sdattn_problem* p, int32_t bq, int32_t bk, const sdattn_budget* b, size_t* ws,
+                          int64_t* nnz) {
+    sdattn::Problem pr;
+    sdattn_status st = sdattn::check_problem(p, &pr);
+    if (st != SDATTN_OK) return st;
+    sdattn::BlockPlan plan;
+    st = sdattn::check_blocks(pr, bq, bk, b, &plan);
+    if (st != SDATTN_OK) return st;
+    *ws = 4096;
+    *nnz = plan.max_nnz;
+    return SDATTN_OK;
+}
+sdattn_status f_ws_columns(void*, const sdattn_problem*, int32_t, size_t* ws) {
+    *ws = 1024;
+    return SDATTN_OK;
+}
+sdattn_status f_alloc(void*, size_t bytes, void** out) {
+    *out = malloc(bytes ? bytes : 1);
+    ++g_live;
+    return SDATTN_OK;
+}
+void f_release(void*, void* p) {
+    free(p);
+    --g_live;
+}
+
+const sdattn::Backend kFake = {nullptr,         f_dense,      f_select_blocks, f_block_sparse, f_select_columns,
+                               f_column_sparse, f_ws_blocks,  f_ws_columns,    f_alloc,        f_release};
+
+}  // namespace
+
+namespace sdattn {
+const Backend& default_backend() { return kFake; }
+}  // namespace sdattn
+
+#define FAKE_API __attribute__((visibility("default")))
+
+extern "C" {
+FAKE_API void sdattn_fake_reset(int fail_at_call, int fail_status) {
+    g_log.clear();
+    g_calls = 0;
+    g_fail_at = fail_at_call;
+    g_fail_status = static_cast<sdattn_status>(fail_status);
+}
+FAKE_API int sdattn_fake_log_size(void) { return static_cast<int>(g_log.size()); }
+FAKE_API const char* sdattn_fake_log_entry(int i) { return g_log.at(static_cast<size_t>(i)).c_str(); }
+FAKE_API int sdattn_fake_live_allocs(void) { return g_live; }
+}

@@ -1,0 +1,125 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, and rejects invalid arguments on the host before touching a GPU."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_bidirectional_attention_amd as sd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdattn.h")
+
+BAD = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SDATTN_API\s+[\w\s\*]*?\b(sdattn_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) == 16
+    out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
+    assert set(names) == exported  # nothing missing, nothing extra
+    lib = ctypes.CDLL(sd.LIB_PATH)
+    for n in names:
+        assert getattr(lib, n) is not None
+    assert set(names) == set(sd._SIGS)  # the binding declares all of them
+
+
+def test_version_and_status_strings():
+    assert sd.sdattn_abi_version() == 1
+    for i, name in enumerate(sd.STATUS_NAMES):
+        assert sd.sdattn_status_string(i) == name
+
+
+def _st(fn, *args):
+    return getattr(sd.lib(), fn)(*args)
+
+
+def test_problem_validation():
+    lib = sd.lib()
+    assert lib.sdattn_forward_dense(None, BAD, BAD, BAD, BAD, None, None) == 1  # NULL problem
+    cases = [
+        (sd.problem(1, 4, 3, 64, 64, "f32"), 2),    # Hq % Hkv
+        (sd.problem(0, 4, 4, 64, 64, "f32"), 2),    # batch
+        (sd.problem(1, 4, 4, -1, 64, "f32"), 2),    # seq_len
+        (sd.problem(1, 4, 4, 64, 96, "f32"), 8),    # head_dim unsupported
+        (sd.Problem(1, 4, 4, 64, 64, 7, 0.0), 3),   # dtype
+        (sd.problem(1, 4, 4, 64, 64, "f32", float("nan")), 2),
+    ]
+    for p, code in cases:
+        assert lib.sdattn_forward_dense(ctypes.byref(p), BAD, BAD, BAD, BAD, None, None) == code, sd.sdattn_last_error()
+    p = sd.problem(1, 4, 4, 64, 64, "bf16")
+    assert lib.sdattn_forward_dense(ctypes.byref(p), None, BAD, BAD, BAD, None, None) == 1
+    assert "non-NULL" in sd.sdattn_last_error()
+    # L == 0 is a no-op that succeeds without touching memory
+    p0 = sd.problem(1, 4, 4, 0, 64, "bf16")
+    assert lib.sdattn_forward_dense(ctypes.byref(p0), None, None, None, None, None, None) == 0
+
+
+def test_block_select_validation_and_workspace():
+    p = sd.problem(1, 32, 32, 65536, 128, "bf16")
+    ws, nnz = sd.sdattn_select_blocks_workspace(p, 128, 128, sd.topk_budget(0.05))
+    assert nnz == 32 * 512 * 26 and ws > 0
+    p8 = sd.problem(1, 32, 32, 8192, 128, "bf16")
+    ws, nnz = sd.sdattn_select_blocks_workspace(p8, 64, 64, sd.mass_budget(0.95, 0.10))
+    assert nnz == 52428
+    p3 = sd.problem(1, 32, 32, 32768, 128, "bf16")
+    assert sd.sdattn_select_blocks_workspace(p3, 128, 128, sd.topk_budget(0.10))[1] == 32 * 256 * 26
+    lib = sd.lib()
+    with pytest.raises(sd.SdattnError, match="BUDGET"):
+        sd.sdattn_select_blocks_workspace(p, 128, 128, sd.topk_budget(0.0))
+    with pytest.raises(sd.SdattnError, match="BUDGET"):
+        sd.sdattn_select_blocks_workspace(p, 128, 128, sd.mass_budget(1.5))
+    with pytest.raises(sd.SdattnError, match="UNSUPPORTED"):
+        sd.sdattn_select_blocks_workspace(p, 32, 128, sd.topk_budget(0.1))
+    with pytest.raises(sd.SdattnError, match="UNSUPPORTED"):  # nKB = 2048 > 1024
+        sd.sdattn_select_blocks_workspace(sd.problem(1, 1, 1, 131072, 128, "bf16"), 64, 64, sd.topk_budget(0.1))
+    b = sd.topk_budget(0.05)
+    ws, nnz = sd.sdattn_select_blocks_workspace(p, 128, 128, b)
+    r = lib.sdattn_select_blocks(ctypes.byref(p), BAD, BAD, 128, 128, ctypes.byref(b), BAD, BAD, nnz - 1, None,
+                                 BAD, ws, None)
+    assert r == 6 and "col_capacity" in sd.sdattn_last_error()
+    r = lib.sdattn_select_blocks(ctypes.byref(p), BAD, BAD, 128, 128, ctypes.byref(b), BAD, BAD, nnz, None,
+                                 BAD, ws - 1, None)
+    assert r == 5
+    r = lib.sdattn_select_blocks(ctypes.byref(p), BAD, BAD, 128, 128, ctypes.byref(b), None, BAD, nnz, None,
+                                 BAD, ws, None)
+    assert r == 1
+
+
+def test_sparse_and_column_validation():
+    lib = sd.lib()
+    p = sd.problem(1, 28, 4, 16384, 128, "bf16")
+    assert lib.sdattn_forward_block_sparse(ctypes.byref(p), BAD, BAD, BAD, 96, 128, BAD, BAD, BAD, None, None) == 8
+    assert lib.sdattn_forward_block_sparse(ctypes.byref(p), BAD, BAD, BAD, 64, 64, None, BAD, BAD, None, None) == 1
+    assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, BAD, 0, BAD, None, None) == 4
+    assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, BAD, 16385, BAD, None, None) == 4
+    assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, None, 492, BAD, None, None) == 1
+    ws = sd.sdattn_select_columns_workspace(p, 492)
+    assert ws >= 28 * 16384 * 8 + 4 * 16384 * 8
+    assert lib.sdattn_select_columns(ctypes.byref(p), BAD, BAD, None, 492, BAD, None, BAD, ws, None) == 1
+    assert lib.sdattn_select_columns(ctypes.byref(p), BAD, BAD, BAD, 492, BAD, None, BAD, ws - 8, None) == 5
+    with pytest.raises(sd.SdattnError, match="BUDGET"):
+        sd.sdattn_select_columns_workspace(p, 0)
+
+
+def test_schedule_descriptor_validation():
+    p = sd.problem(1, 4, 4, 512, 64, "f32")
+    bad = [
+        sd.schedule_desc(10, 2, 5),                                 # select after the warm-up ends
+        sd.schedule_desc(0, 0, 0),                                  # no steps
+        sd.schedule_desc(10, 1, 0, sel=sd.SDATTN_SEL_COLUMNS, column_keep_frac=0.1),  # columns need refresh_dense
+        sd.schedule_desc(10, 0, 0, refresh_dense=True, sel=sd.SDATTN_SEL_COLUMNS, column_keep_frac=0.1),
+        sd.schedule_desc(10, 1, 0, block_q=32, block_k=64, budget=sd.topk_budget(0.25)),
+    ]
+    for d in bad:
+        with pytest.raises(sd.SdattnError):
+            sd.sdattn_schedule_create(p, d)

@@ -1,0 +1,182 @@
+"""The schedule driver on the CPU, against a recording fake backend.
+
+libsdattn_fake.so links the driver and the argument checks (plain C++) with
+a backend that logs every call and can fail on purpose; no GPU is used.
+The action table is compared with the oracle's, which is written
+independently from the same rule.
+"""
+
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import oracle
+import sparse_bidirectional_attention_amd as sd
+from sparse_bidirectional_attention_amd import build as sdbuild
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def fake():
+    if not os.path.exists(sdbuild.FAKE_LIB):
+        sdbuild.build_fake()
+    lib = sd.declare(ctypes.CDLL(sdbuild.FAKE_LIB), required=False)
+    lib.sdattn_fake_log_entry.restype = ctypes.c_char_p
+    lib.sdattn_fake_log_entry.argtypes = [ctypes.c_int]
+    lib.sdattn_fake_reset.argtypes = [ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+def _desc_of(w):
+    sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
+    budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
+    return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
+                            w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac)
+
+
+def _prob_of(w):
+    return sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
+
+
+def _create(lib, p, d):
+    h = ctypes.c_void_p(None)
+    st = lib.sdattn_schedule_create(ctypes.byref(p), ctypes.byref(d), ctypes.byref(h))
+    assert st == 0, lib.sdattn_last_error()
+    return h
+
+
+def _actions(lib, h, n):
+    out = []
+    for t in range(n):
+        a = ctypes.c_int(-1)
+        assert lib.sdattn_schedule_action(h, t, ctypes.byref(a)) == 0
+        out.append(sd.ACTIONS[a.value])
+    return out
+
+
+def _log(lib):
+    return [lib.sdattn_fake_log_entry(i).decode() for i in range(lib.sdattn_fake_log_size())]
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_action_table_matches_oracle(fake, name):
+    w = WORKLOADS[name]
+    h = _create(fake, _prob_of(w), _desc_of(w))
+    try:
+        ref = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
+                                      w.refresh_steps, w.refresh_dense)
+        assert _actions(fake, h, w.total_steps) == ref
+    finally:
+        fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def test_random_schedules_match_oracle(fake):
+    rng = random.Random(0)
+    p = sd.problem(1, 2, 2, 256, 64, "bf16")
+    for _ in range(200):
+        T = rng.randint(1, 60)
+        dense = rng.randint(0, T)
+        sel = rng.randint(0, min(dense, T - 1))
+        interval = rng.choice([0, 0, 1, 3, 7])
+        refresh = tuple(sorted(rng.sample(range(T), rng.randint(0, min(4, T)))))
+        rdense = rng.random() < 0.5
+        d = sd.schedule_desc(T, dense, sel, interval, list(refresh), rdense, budget=sd.topk_budget(0.5))
+        h = _create(fake, p, d)
+        ref = oracle.schedule_actions(T, dense, sel, interval, refresh, rdense)
+        assert _actions(fake, h, T) == ref
+        fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def _step(lib, h, t, o=0x5000, lse=None):
+    return lib.sdattn_schedule_step(h, t, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
+                                    ctypes.c_void_p(0x3000), ctypes.c_void_p(o), lse, None)
+
+
+def test_block_schedule_reuses_and_refreshes(fake):
+    w = WORKLOADS["llada8b_8k"]
+    h = _create(fake, _prob_of(w), _desc_of(w))
+    fake.sdattn_fake_reset(-1, 0)
+    for t in range(w.total_steps):
+        assert _step(fake, h, t) == 0
+    log = _log(fake)
+    sel = [l for l in log if l.startswith("select_blocks")]
+    sparse = [l for l in log if l.startswith("block_sparse")]
+    assert len(sel) == 8 and len(sparse) == 255 and log[0].startswith("dense")
+    assert all("cap=52428" in l for l in sel)
+    # every sparse step uses the CSR of the most recent selection; buffers alternate
+    cur = None
+    bufs = []
+    for l in log:
+        if l.startswith("select_blocks"):
+            cur = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
+            bufs.append(cur)
+        elif l.startswith("block_sparse"):
+            assert re.search(r"rp=(\S+) ci=(\S+)", l).groups() == cur
+    assert bufs[0] != bufs[1] and bufs[0] == bufs[2]
+    counts = (ctypes.c_int64 * 4)()
+    last = ctypes.c_int32(0)
+    assert fake.sdattn_schedule_stats(h, counts, ctypes.byref(last)) == 0
+    assert list(counts) == [0, 1, 7, 248] and last.value == 224
+    fake.sdattn_schedule_destroy(h)
+
+
+def test_failed_selection_keeps_the_cached_pattern(fake):
+    w = WORKLOADS["llada8b_8k"]
+    h = _create(fake, _prob_of(w), _desc_of(w))
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 0) == 0
+    rp, ci, cap = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int64()
+    assert fake.sdattn_schedule_mask(h, ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(cap)) == 0
+    before = (rp.value, ci.value)
+    fake.sdattn_fake_reset(0, 7)  # the next backend call (the step-32 selection) fails
+    assert _step(fake, h, 32) == 7
+    assert "injected" in fake.sdattn_last_error().decode()
+    assert fake.sdattn_schedule_mask(h, ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(cap)) == 0
+    assert (rp.value, ci.value) == before
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 33) == 0
+    assert re.search(r"rp=(\S+)", _log(fake)[0]).group(1) == hex(before[0])
+    counts = (ctypes.c_int64 * 4)()
+    last = ctypes.c_int32(0)
+    fake.sdattn_schedule_stats(h, counts, ctypes.byref(last))
+    assert list(counts) == [0, 1, 0, 1] and last.value == 0
+    fake.sdattn_schedule_destroy(h)
+
+
+def test_sparse_step_before_any_pattern_is_a_state_error(fake):
+    w = WORKLOADS["sparsed_64k"]
+    h = _create(fake, _prob_of(w), _desc_of(w))
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 500) == 9
+    assert _log(fake) == []
+    rp, ci, cap = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int64()
+    assert fake.sdattn_schedule_mask(h, ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(cap)) == 9
+    assert _step(fake, h, 10) == 0 and _log(fake)[0].startswith("dense")
+    assert _step(fake, h, 205) == 0
+    assert _step(fake, h, 500) == 0
+    assert _step(fake, h, 1024) == 2 and _step(fake, h, -1) == 2
+    fake.sdattn_schedule_destroy(h)
+
+
+def test_column_schedule_uses_own_lse_buffer(fake):
+    w = WORKLOADS["pulsecol_dream7b_16k"]
+    h = _create(fake, _prob_of(w), _desc_of(w))
+    fake.sdattn_fake_reset(-1, 0)
+    for t in range(w.total_steps):
+        assert _step(fake, h, t) == 0
+    log = _log(fake)
+    dense = [l for l in log if l.startswith("dense")]
+    sel = [l for l in log if l.startswith("select_columns")]
+    assert len(dense) == 3 and len(sel) == 3 and all("kcol=492" in l for l in sel)
+    for d, s in zip(dense, sel):  # dense writes the lse that the selection reads
+        assert re.search(r"lse=(\S+)", d).group(1) == re.search(r"lse=(\S+)", s).group(1) != "(nil)"
+    assert sum(l.startswith("column_sparse") for l in log) == 189
+    fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
