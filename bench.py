@@ -108,7 +108,6 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
     G = w.q_heads // w.kv_heads
     x0 = base_step
     xs = sel_step_inputs
-    t_budget = 20.0
     samples = {}
     # dense step: a few query rows of one head, scaled to all rows and heads
     rows = np.arange(0, L, max(1, L // 64))[:64]
@@ -144,7 +143,7 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
         qrows = np.arange(0, L, max(1, L // 16))[:16]
         _, lse = oracle.dense_attention(xs["q"][:, :1], xs["k"][:, :1], xs["v"][:, :1], rows=qrows)
         t0 = time.perf_counter()
-        s = (xs["q"][0, 0, qrows].astype(np.float64) @ oracle.attention.as_f64(xs["k"][0, 0]).T) / np.sqrt(d)
+        s = (oracle.attention.as_f64(xs["q"][0, 0, qrows]) @ oracle.attention.as_f64(xs["k"][0, 0]).T) / np.sqrt(d)
         np.exp(s - lse[0, 0][:, None]).sum(axis=0)
         t_sel = (time.perf_counter() - t0) * (L / len(qrows)) * H
         samples["select"] = f"column scores of {len(qrows)} query rows of 1 head, x{L / len(qrows) * H:.0f}"
