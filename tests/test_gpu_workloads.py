@@ -1,0 +1,117 @@
+"""Full-size parity on the five workloads, through the schedule driver (the
+launch configuration bench.py times).
+
+Masks are checked in full (top-k / mass-cap rules, exact up to near-cut
+candidates).  Outputs are checked element by element on sampled query rows
+or query blocks (always including the first and the last), which the fp64
+oracle computes one by one: dense rows against all keys, sparse rows in
+gather form under the GPU's pattern.  The checked steps follow each
+schedule; skipped steps never select, so the pattern in force is the one a
+full run would have.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_bidirectional_attention_amd as sd
+from gpu_util import check_out, check_topk_rows, csr_rows, host_inputs, say, to_dev, to_np
+from test_gpu_schedule import _d2h, _desc
+from test_gpu_select import _check_mass_rows
+from workloads import WORKLOADS, make_base, make_step
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(n, k):
+    s = np.unique(np.concatenate([np.linspace(0, n - 1, k).astype(int), [0, n - 1]]))
+    return s
+
+
+def _run_steps(w, steps, n_qblocks=8, n_rows=32, col_groups=None):
+    base = make_base(w)
+    p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
+    acts = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
+                                   w.refresh_steps, w.refresh_dense)
+    h = sd.sdattn_schedule_create(p, _desc(w))
+    L, H = w.seq_len, w.q_heads
+    nqb = -(-L // w.block)
+    rows = w.batch * H * nqb
+    kcol = oracle.count_from_fraction(w.column_keep_frac, L) if w.selector == "columns" else 0
+    pattern, pending = None, None
+    try:
+        for t in steps:
+            act = acts[t]
+            say(f"{w.name} step {t} {act}")
+            xh = make_step(w, t, base)
+            x = {n: to_dev(a) for n, a in xh.items()}
+            o = torch.empty_like(x["q"])
+            lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device="cuda")
+            assert sd.sdattn_schedule_action(h, t) == act
+            sd.sdattn_schedule_step(h, t, x["q"], x["k"], x["v"], o, lse)
+            torch.cuda.synchronize()
+            og, lg = to_np(o), to_np(lse)
+            del x, o, lse
+            if act in ("DENSE_SELECT", "SELECT_SPARSE"):
+                rp_ptr, ci_ptr, _ = sd.sdattn_schedule_mask(h)
+                if w.selector == "blocks":
+                    rp = _d2h(rp_ptr, rows + 1)
+                    ci = _d2h(ci_ptr, int(rp[-1]))
+                    A4 = oracle.pooled_mass(xh["q"], xh["k"], w.block, w.block)
+                    A = A4.reshape(rows, -1)
+                    if w.budget == "topk":
+                        n_ex = check_topk_rows(csr_rows(rp, ci), A, oracle.count_from_fraction(w.keep_frac, nqb))
+                    else:
+                        _, _, tau = oracle.select_mass_cap(A4, w.mass, w.max_mean_density)
+                        _check_mass_rows(rp, ci, A, tau, w.mass, w.max_mean_density)
+                        n_ex = None
+                    say(f"  mask: nnz={rp[-1]} density={rp[-1] / A.size:.4f} exempt rows={n_ex}")
+                    pattern = (rp, ci)
+                else:
+                    cols = _d2h(ci_ptr, w.batch * w.kv_heads * kcol).reshape(w.batch, w.kv_heads, kcol)
+                    G = H // w.kv_heads
+                    for g in (col_groups if col_groups is not None else range(w.kv_heads)):
+                        sl = slice(g * G, (g + 1) * G)
+                        _, rl = oracle.dense_attention(xh["q"][:, sl], xh["k"][:, g:g + 1], xh["v"][:, g:g + 1])
+                        C = oracle.column_scores(xh["q"][:, sl], xh["k"][:, g:g + 1], rl)
+                        n_ex = check_topk_rows(cols[0, g:g + 1], C[0], kcol, f"columns g={g}")
+                        say(f"  columns g={g}: exempt={n_ex}")
+                    pending = cols
+            # outputs on samples
+            if act in ("DENSE", "DENSE_SELECT"):
+                r = _sample(L, n_rows)
+                ro, rl = oracle.dense_attention(xh["q"], xh["k"], xh["v"], rows=r)
+                check_out(og[:, :, r], ro, lg[:, :, r], rl, w.dtype, f"step {t} dense rows")
+            elif w.selector == "blocks":
+                qb = _sample(nqb, n_qblocks)
+                ro, rl = oracle.block_sparse_attention(xh["q"], xh["k"], xh["v"], pattern[0], pattern[1], w.block,
+                                                       w.block, qblocks=qb)
+                toks = np.concatenate([np.arange(I * w.block, min(L, (I + 1) * w.block)) for I in qb])
+                e = check_out(og[:, :, toks], ro, lg[:, :, toks], rl, w.dtype, f"step {t} sparse blocks")
+                say(f"  O max-abs {e[0]:.2e} mean-abs {e[1]:.2e}")
+            else:
+                r = _sample(L, n_rows)
+                ro, rl = oracle.column_sparse_attention(xh["q"], xh["k"], xh["v"], pattern, rows=r)
+                e = check_out(og[:, :, r], ro, lg[:, :, r], rl, w.dtype, f"step {t} column rows")
+                say(f"  O max-abs {e[0]:.2e} mean-abs {e[1]:.2e}")
+            if act == "DENSE_SELECT" and w.selector == "columns":
+                pattern = pending
+    finally:
+        sd.sdattn_schedule_destroy(h)
+
+
+def test_llada8b_8k_mass_cap_refresh():
+    _run_steps(WORKLOADS["llada8b_8k"], [0, 1, 31, 32, 33, 224, 255], n_qblocks=16)
+
+
+def test_sparsed_32k_topk():
+    _run_steps(WORKLOADS["sparsed_32k"], [25, 26, 127], n_qblocks=16)
+
+
+def test_sparsed_64k_topk():
+    _run_steps(WORKLOADS["sparsed_64k"], [204, 205, 1023], n_qblocks=8, n_rows=16)
+
+
+def test_pulsecol_16k_columns():
+    _run_steps(WORKLOADS["pulsecol_dream7b_16k"], [0, 1, 63, 64, 65, 191], n_rows=64, col_groups=[0])
