@@ -171,6 +171,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="sparsed_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a known-size "
+                         "kernel that scales the profiler's HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
@@ -218,6 +221,16 @@ def main():
             sd.sdattn_schedule_step(hw, t, x["q"], x["k"], x["v"], o, lse)
         torch.cuda.synchronize()
         sd.sdattn_schedule_destroy(hw)
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_calibration_mib} MiB read + {args.copy_calibration_mib} MiB written")
+        del src, dst
 
     h = sd.sdattn_schedule_create(p, schedule_desc(sd, w))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]

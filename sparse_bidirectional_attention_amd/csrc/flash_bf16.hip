@@ -27,6 +27,8 @@
 //     final normalisation uses the same reference max).
 // The log-sum-exp (natural log) is written per query row.
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -47,26 +49,30 @@ struct FlashParams {
     float thr;    // lazy-rescale threshold in raw score units
 };
 
-__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 3)) & 7; }
+// Raw buffer descriptor word 3 for gfx9-family parts: 32-bit data format,
+// offsets checked against num_records (loads past it return zero).
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
-    constexpr int KT = 64;
+    constexpr int KT = 64;                 // keys per tile
     constexpr int T = NW * 64;
     constexpr int DK = D / 16;
     constexpr int ND = D / 32;
-    constexpr int KROW = D * 2;
-    constexpr int KBYTES = KT * KROW;
-    constexpr int VROW = KT * 2;
-    constexpr int VBYTES = D * VROW;
+    constexpr int KROW = D * 2;            // bytes of one K / V row in HBM
+    constexpr int KPITCH = KROW + 16;      // padded K row in LDS
+    constexpr int KBYTES = KT * KPITCH;
+    constexpr int VPITCH = KT * 2 + 16;    // padded V^T row (d) in LDS
+    constexpr int VBYTES = D * VPITCH;
     constexpr int BUF = KBYTES + VBYTES;
-    constexpr int KUNITS = D / 8;
-    constexpr int KMASK = KUNITS - 1;
+    constexpr int KUNITS = D / 8;          // 16-byte units per row
     constexpr int K_LOADS = KT * KUNITS / T;
-    constexpr int V_GROUPS = (KT / 4) * KUNITS;
-    constexpr int V_LOADS = (V_GROUPS + T - 1) / T;
+    constexpr int ROWS_PER_PASS = T / KUNITS;
+    constexpr int V_PAIRS = (KT / 4) * KUNITS;      // (4-key group, unit) pairs per tile
+    constexpr int V_LOADS = (V_PAIRS + T - 1) / T;
     constexpr int OPITCH = D * 2 + 16;
     static_assert(K_LOADS * T == KT * KUNITS, "K tile must split evenly");
+    static_assert(T % KUNITS == 0 && T % 16 == 0, "threads cover whole rows");
     static_assert(NW * 32 * OPITCH <= 2 * BUF, "epilogue staging fits in LDS");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
@@ -85,8 +91,9 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int g = h / p.group;
     const int L = p.L;
     const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * L * D;
-    const uint16_t* __restrict__ kh = p.k + kvoff;
-    const uint16_t* __restrict__ vh = p.v + kvoff;
+    const uint32_t head_bytes = static_cast<uint32_t>(L) * KROW;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + kvoff), 0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + kvoff), 0, head_bytes, kRsrcWord3);
     const int q0 = qt * (NW * 32);
 
     // ---- tile source ------------------------------------------------------
@@ -103,8 +110,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
         n_tiles = (p.kcol + KT - 1) / KT;
     }
-    // base key of tile t (dense / block) or its first column entry (column);
-    // nvalid = number of real keys in the tile.
+    // first key of tile t (dense / block: a token index; column: an entry of
+    // the column list) and the number of real keys in it
     auto tile_base = [&](int t, int& nvalid) -> int {
         if constexpr (MODE == MODE_COLUMN) {
             nvalid = min(KT, p.kcol - t * KT);
@@ -121,35 +128,49 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             return base;
         }
     };
-    auto key_row = [&](int base, int nvalid, int i) -> int {
-        // clamped so that any index stays inside the tensor
-        if constexpr (MODE == MODE_COLUMN) {
-            return min(max(cb[base + min(i, nvalid - 1)], 0), L - 1);
-        } else {
-            return min(max(base + i, 0), L - 1);
-        }
-    };
+
+    // K: thread -> (row kr0 + i*ROWS_PER_PASS, 16-byte unit ku), coalesced rows.
+    const int kr0 = tid / KUNITS, ku = tid % KUNITS;
+    // V: thread -> (4-key group vg, unit vu + i*T/16), key group fastest so that
+    // the transposed LDS writes of 16 neighbouring lanes hit distinct banks.
+    const int vg = tid & 15, vu = tid >> 4;
 
     u32x4 kreg[K_LOADS];
     u32x4 vreg[V_LOADS][4];
     auto load_tile = [&](int t) {
         int nv;
         const int base = tile_base(t, nv);
+        if constexpr (MODE == MODE_COLUMN) {
+            // gathered rows; entries past the list repeat its last entry (masked later)
 #pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int cid = tid + i * T;
-            const int r = cid / KUNITS, u = cid % KUNITS;
-            kreg[i] = *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(key_row(base, nv, r)) * D + u * 8);
-        }
+            for (int i = 0; i < K_LOADS; ++i) {
+                const int row = cb[base + min(kr0 + i * ROWS_PER_PASS, nv - 1)];
+                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, row * KROW + ku * 16, 0, 0);
+            }
 #pragma unroll
-        for (int i = 0; i < V_LOADS; ++i) {
-            const int gid = tid + i * T;
-            if (V_GROUPS % T == 0 || gid < V_GROUPS) {
-                const int kg = gid / KUNITS, u = gid % KUNITS;
+            for (int i = 0; i < V_LOADS; ++i) {
+                if (V_PAIRS % T == 0 || tid + i * T < V_PAIRS) {
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    vreg[i][c] = *reinterpret_cast<const u32x4*>(
-                        vh + static_cast<size_t>(key_row(base, nv, 4 * kg + c)) * D + u * 8);
+                    for (int c = 0; c < 4; ++c) {
+                        const int row = cb[base + min(4 * vg + c, nv - 1)];
+                        vreg[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rv, row * KROW + (vu + i * (T / 16)) * 16, 0, 0);
+                    }
+                }
+            }
+        } else {
+            // contiguous rows: one scalar tile offset; rows past L read as zero
+            const int soff = base * KROW;
+#pragma unroll
+            for (int i = 0; i < K_LOADS; ++i)
+                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, kr0 * KROW + ku * 16, soff + i * ROWS_PER_PASS * KROW, 0);
+#pragma unroll
+            for (int i = 0; i < V_LOADS; ++i) {
+                if (V_PAIRS % T == 0 || tid + i * T < V_PAIRS) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        vreg[i][c] = __builtin_amdgcn_raw_buffer_load_b128(
+                            rv, (4 * vg + c) * KROW + vu * 16, soff + i * (T / 16) * 16, 0);
+                }
             }
         }
     };
@@ -157,30 +178,24 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         char* Kb = smem + buf * BUF;
         char* Vb = Kb + KBYTES;
 #pragma unroll
-        for (int i = 0; i < K_LOADS; ++i) {
-            const int cid = tid + i * T;
-            const int r = cid / KUNITS, u = cid % KUNITS;
-            *reinterpret_cast<u32x4*>(Kb + r * KROW + ((u ^ (r & KMASK)) << 4)) = kreg[i];
-        }
+        for (int i = 0; i < K_LOADS; ++i)
+            *reinterpret_cast<u32x4*>(Kb + (kr0 + i * ROWS_PER_PASS) * KPITCH + ku * 16) = kreg[i];
+        // keys 4vg..4vg+3 go to consecutive LDS positions; inside each 16-key
+        // chunk the two 4-key halves of each 8-key run are interleaved to
+        // match the MFMA accumulator's key order.
+        const int kk = vg & 3;
+        const int vpos = ((vg >> 2) * 16 + 8 * (kk & 1) + 4 * (kk >> 1)) * 2;  // byte offset in a V^T row
 #pragma unroll
         for (int i = 0; i < V_LOADS; ++i) {
-            const int gid = tid + i * T;
-            if (V_GROUPS % T == 0 || gid < V_GROUPS) {
-                const int kg = gid / KUNITS, u = gid % KUNITS;
-                // keys 4kg..4kg+3 go to consecutive LDS positions; inside each
-                // 16-key chunk the two 4-key halves of each 8-key run are
-                // interleaved to match the MFMA accumulator's key order.
-                const int kk = kg & 3;
-                const int unit_v = (kg >> 2) * 2 + (kk & 1);
-                const int half = kk >> 1;
+            if (V_PAIRS % T == 0 || tid + i * T < V_PAIRS) {
+                char* vrow = Vb + (vu + i * (T / 16)) * 8 * VPITCH + vpos;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int d = u * 8 + j;
                     const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
                     const uint32_t lo = __builtin_amdgcn_perm(vreg[i][1][j >> 1], vreg[i][0][j >> 1], sel);
                     const uint32_t hi = __builtin_amdgcn_perm(vreg[i][3][j >> 1], vreg[i][2][j >> 1], sel);
                     u32x2 w = {lo, hi};
-                    *reinterpret_cast<u32x2*>(Vb + d * VROW + ((unit_v ^ vswz(d)) << 4) + half * 8) = w;
+                    *reinterpret_cast<u32x2*>(vrow + j * VPITCH) = w;
                 }
             }
         }
@@ -204,11 +219,18 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     float m_used = -kInf;
     float l_acc = 0.f;
     const float c = p.c;
+    // per-lane LDS read offsets (the tile's buffer adds a uniform base)
+    const int k_rd = l32 * KPITCH + hl * 16;   // + kb*32*KPITCH + st*32
+    const int v_rd = l32 * VPITCH + hl * 16;   // + db*32*VPITCH + chunk*32
 
     if (n_tiles > 0) {
         load_tile(0);
         store_tile(0);
     }
+    // every load issued so far (Q operand, first tile) has landed; without this
+    // the loop's wait counting cannot tell the Q loads from the next tile's
+    // prefetch and would stall each tile's MFMAs on that prefetch
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int t = 0; t < n_tiles; ++t) {
@@ -217,9 +239,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         if (has_next) load_tile(t + 1);
         int nvalid;
         tile_base(t, nvalid);
-
-        const char* Kb = smem + buf * BUF;
-        const char* Vb = Kb + KBYTES;
+        const char* Kb = smem + buf * BUF + k_rd;
+        const char* Vb = smem + buf * BUF + KBYTES + v_rd;
 
         // S^T = K Q^T : two 32-key x 32-query blocks
         f32x16 sacc[2];
@@ -231,9 +252,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         for (int st = 0; st < DK; ++st) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const int row = kb * 32 + l32;
-                const int unit = 2 * st + hl;
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + row * KROW + ((unit ^ (row & KMASK)) << 4));
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * KPITCH + st * 32);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[kb], 0, 0, 0);
             }
         }
@@ -280,13 +299,11 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         // O^T += V^T P^T
 #pragma unroll
         for (int db = 0; db < ND; ++db) {
-            const int drow = db * 32 + l32;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    const int unit = 2 * (2 * kb + m) + hl;
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + drow * VROW + ((unit ^ vswz(drow)) << 4));
+                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + db * 32 * VPITCH + (2 * kb + m) * 32);
                     u32x4 bb = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bb), oacc[db], 0, 0, 0);
                 }
