@@ -53,29 +53,36 @@ struct FlashParams {
 // offsets checked against num_records (loads past it return zero).
 constexpr int kRsrcWord3 = 0x00020000;
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// 8-byte transposing LDS read: in each group of 16 lanes, lane 4s+e receives
+// element e of the 8-byte chunks addressed by lanes s, s+4, s+8, s+12.
+__device__ __forceinline__ s16x4 lds_read_tr(const char* base, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS s16x4*)((LDS_AS char*)(base) + off));
+}
+
 template <int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
-    constexpr int KT = 64;                 // keys per tile
+    constexpr int KT = 64;                  // keys per tile
     constexpr int T = NW * 64;
     constexpr int DK = D / 16;
     constexpr int ND = D / 32;
-    constexpr int KROW = D * 2;            // bytes of one K / V row in HBM
-    constexpr int KPITCH = KROW + 16;      // padded K row in LDS
-    constexpr int KBYTES = KT * KPITCH;
-    constexpr int VPITCH = KT * 2 + 16;    // padded V^T row (d) in LDS
-    constexpr int VBYTES = D * VPITCH;
-    constexpr int BUF = KBYTES + VBYTES;
-    constexpr int KUNITS = D / 8;          // 16-byte units per row
-    constexpr int K_LOADS = KT * KUNITS / T;
-    constexpr int ROWS_PER_PASS = T / KUNITS;
-    constexpr int V_PAIRS = (KT / 4) * KUNITS;      // (4-key group, unit) pairs per tile
-    constexpr int V_LOADS = (V_PAIRS + T - 1) / T;
-    constexpr int OPITCH = D * 2 + 16;
-    static_assert(K_LOADS * T == KT * KUNITS, "K tile must split evenly");
-    static_assert(T % KUNITS == 0 && T % 16 == 0, "threads cover whole rows");
-    static_assert(NW * 32 * OPITCH <= 2 * BUF, "epilogue staging fits in LDS");
+    constexpr int ROWB = D * 2;             // bytes of one K / V row (HBM and LDS)
+    constexpr int TILEB = KT * ROWB;        // one K or V tile
+    constexpr int UNITS = D / 8;            // 16-byte units per row
+    constexpr int SLOTS = KT * UNITS;       // 16-byte slots per tile
+    constexpr int NDMA = SLOTS / T;         // DMA instructions per thread per tile (K; same for V)
+    constexpr int ROWS_PER_DMA = T / UNITS;
+    constexpr int OPITCH = D * 2;           // epilogue staging row (one-time, conflicts tolerated)
+    static_assert(NDMA * T == SLOTS && T % UNITS == 0 && ROWS_PER_DMA % 4 == 0, "DMA tiling");
+    static_assert(NW * 32 * OPITCH <= 2 * TILEB, "epilogue staging fits in one stage");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+    // Two stages (K tile then V tile each), separate objects so that reads of
+    // one stage are not ordered behind the DMA filling the other.
+    __shared__ __attribute__((aligned(16))) char stage0[2 * TILEB];
+    __shared__ __attribute__((aligned(16))) char stage1[2 * TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -91,7 +98,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int g = h / p.group;
     const int L = p.L;
     const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * L * D;
-    const uint32_t head_bytes = static_cast<uint32_t>(L) * KROW;
+    const uint32_t head_bytes = static_cast<uint32_t>(L) * ROWB;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + kvoff), 0, head_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + kvoff), 0, head_bytes, kRsrcWord3);
     const int q0 = qt * (NW * 32);
@@ -129,74 +136,31 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         }
     };
 
-    // K: thread -> (row kr0 + i*ROWS_PER_PASS, 16-byte unit ku), coalesced rows.
-    const int kr0 = tid / KUNITS, ku = tid % KUNITS;
-    // V: thread -> (4-key group vg, unit vu + i*T/16), key group fastest so that
-    // the transposed LDS writes of 16 neighbouring lanes hit distinct banks.
-    const int vg = tid & 15, vu = tid >> 4;
-
-    u32x4 kreg[K_LOADS];
-    u32x4 vreg[V_LOADS][4];
-    auto load_tile = [&](int t) {
+    // LDS layouts (16-byte units, XOR-swizzled so that reads hit distinct banks):
+    //   K tile: row r (key), unit u stored at unit u ^ (r & (UNITS-1));
+    //   V tile: row r (key), unit u stored at unit u ^ (4 (r & 3)) mod UNITS.
+    // The DMA writes 16 bytes per lane at consecutive LDS slots; each lane
+    // fetches the HBM chunk that belongs at its slot.
+    const int dr0 = tid / UNITS, dpu = tid % UNITS;  // row / physical unit of slot `tid`
+    auto issue_dma = [&](char* stage, int t) {
         int nv;
         const int base = tile_base(t, nv);
-        if constexpr (MODE == MODE_COLUMN) {
-            // gathered rows; entries past the list repeat its last entry (masked later)
 #pragma unroll
-            for (int i = 0; i < K_LOADS; ++i) {
-                const int row = cb[base + min(kr0 + i * ROWS_PER_PASS, nv - 1)];
-                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, row * KROW + ku * 16, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < V_LOADS; ++i) {
-                if (V_PAIRS % T == 0 || tid + i * T < V_PAIRS) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const int row = cb[base + min(4 * vg + c, nv - 1)];
-                        vreg[i][c] = __builtin_amdgcn_raw_buffer_load_b128(rv, row * KROW + (vu + i * (T / 16)) * 16, 0, 0);
-                    }
-                }
-            }
-        } else {
-            // contiguous rows: one scalar tile offset; rows past L read as zero
-            const int soff = base * KROW;
-#pragma unroll
-            for (int i = 0; i < K_LOADS; ++i)
-                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, kr0 * KROW + ku * 16, soff + i * ROWS_PER_PASS * KROW, 0);
-#pragma unroll
-            for (int i = 0; i < V_LOADS; ++i) {
-                if (V_PAIRS % T == 0 || tid + i * T < V_PAIRS) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        vreg[i][c] = __builtin_amdgcn_raw_buffer_load_b128(
-                            rv, (4 * vg + c) * KROW + vu * 16, soff + i * (T / 16) * 16, 0);
-                }
-            }
-        }
-    };
-    auto store_tile = [&](int buf) {
-        char* Kb = smem + buf * BUF;
-        char* Vb = Kb + KBYTES;
-#pragma unroll
-        for (int i = 0; i < K_LOADS; ++i)
-            *reinterpret_cast<u32x4*>(Kb + (kr0 + i * ROWS_PER_PASS) * KPITCH + ku * 16) = kreg[i];
-        // keys 4vg..4vg+3 go to consecutive LDS positions; inside each 16-key
-        // chunk the two 4-key halves of each 8-key run are interleaved to
-        // match the MFMA accumulator's key order.
-        const int kk = vg & 3;
-        const int vpos = ((vg >> 2) * 16 + 8 * (kk & 1) + 4 * (kk >> 1)) * 2;  // byte offset in a V^T row
-#pragma unroll
-        for (int i = 0; i < V_LOADS; ++i) {
-            if (V_PAIRS % T == 0 || tid + i * T < V_PAIRS) {
-                char* vrow = Vb + (vu + i * (T / 16)) * 8 * VPITCH + vpos;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t lo = __builtin_amdgcn_perm(vreg[i][1][j >> 1], vreg[i][0][j >> 1], sel);
-                    const uint32_t hi = __builtin_amdgcn_perm(vreg[i][3][j >> 1], vreg[i][2][j >> 1], sel);
-                    u32x2 w = {lo, hi};
-                    *reinterpret_cast<u32x2*>(vrow + j * VPITCH) = w;
-                }
+        for (int i = 0; i < NDMA; ++i) {
+            const int row = dr0 + i * ROWS_PER_DMA;
+            const int uk = dpu ^ (row & (UNITS - 1));
+            const int uv = dpu ^ ((4 * (row & 3)) & (UNITS - 1));
+            LDS_AS char* kdst = (LDS_AS char*)(stage) + (i * T + wave * 64) * 16;
+            LDS_AS char* vdst = kdst + TILEB;
+            if constexpr (MODE == MODE_COLUMN) {
+                const int key = cb[base + min(row, nv - 1)];
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, key * ROWB + uk * 16, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, key * ROWB + uv * 16, 0, 0, 0);
+            } else {
+                // rows past L read as zero (buffer range check)
+                const int soff = (base + i * ROWS_PER_DMA) * ROWB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, dr0 * ROWB + uk * 16, soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, dr0 * ROWB + uv * 16, soff, 0, 0);
             }
         }
     };
@@ -211,37 +175,35 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             qreg[st] = *reinterpret_cast<const bf16x8*>(qp + 16 * st + 8 * hl);
     }
 
+    // per-lane LDS read offsets inside a stage
+    //   K operand (row l32 + 32 kb, unit 2 st + hl)
+    int koff[DK];
+#pragma unroll
+    for (int st = 0; st < DK; ++st) koff[st] = l32 * ROWB + (((2 * st + hl) ^ (l32 & (UNITS - 1))) << 4);
+    //   V^T operand by transposing reads: source lane q of 16-lane group g names
+    //   key row 4 (g/2) + q/4 (+ 16 m + 8 rd + 32 kb) and the 4 columns
+    //   32 db + 16 (g & 1) + 4 (q & 3) ...
+    const int gq = lane & 15, gg = lane >> 4;
+    int voff[ND];
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+        const int u = 2 * (gg & 1) + ((gq & 3) >> 1) + 4 * db;
+        const int x = (4 * ((gq >> 2) & 3)) & (UNITS - 1);
+        voff[db] = TILEB + (4 * (gg >> 1) + (gq >> 2)) * ROWB + ((u ^ x) << 4) + (gq & 1) * 8;
+    }
+
     f32x16 oacc[ND];
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
     float m_used = -kInf;
-    float l_acc = 0.f;
+    float l_part[2] = {0.f, 0.f};
     const float c = p.c;
-    // per-lane LDS read offsets (the tile's buffer adds a uniform base)
-    const int k_rd = l32 * KPITCH + hl * 16;   // + kb*32*KPITCH + st*32
-    const int v_rd = l32 * VPITCH + hl * 16;   // + db*32*VPITCH + chunk*32
 
-    if (n_tiles > 0) {
-        load_tile(0);
-        store_tile(0);
-    }
-    // every load issued so far (Q operand, first tile) has landed; without this
-    // the loop's wait counting cannot tell the Q loads from the next tile's
-    // prefetch and would stall each tile's MFMAs on that prefetch
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int buf = t & 1;
-        const bool has_next = t + 1 < n_tiles;
-        if (has_next) load_tile(t + 1);
+    auto compute = [&](const char* stg, int t) {
         int nvalid;
         tile_base(t, nvalid);
-        const char* Kb = smem + buf * BUF + k_rd;
-        const char* Vb = smem + buf * BUF + KBYTES + v_rd;
-
         // S^T = K Q^T : two 32-key x 32-query blocks
         f32x16 sacc[2];
 #pragma unroll
@@ -252,7 +214,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         for (int st = 0; st < DK; ++st) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kb + kb * 32 * KPITCH + st * 32);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(stg + koff[st] + kb * 32 * ROWB);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[kb], 0, 0, 0);
             }
         }
@@ -278,13 +240,16 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         if (__any(need)) {
             const float alpha = need ? exp2_fast((m_used - mnew) * c) : 1.f;
             m_used = need ? mnew : m_used;
-            l_acc *= alpha;
+            l_part[0] *= alpha;
+            l_part[1] *= alpha;
 #pragma unroll
             for (int db = 0; db < ND; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
         const float mc = (m_used > -kInf) ? m_used * c : 0.f;
+        // P^T in bf16 for the PV product; the row sum stays in fp32 (it sets
+        // the log-sum-exp, which the column scores need to ~1e-6)
         uint32_t pk[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -292,31 +257,54 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = exp2_fast(fmaf(sacc[kb][r], c, -mc));
                 const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], c, -mc));
-                l_acc += p0 + p1;
                 pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+                l_part[kb] += p0 + p1;
             }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T; the V^T operand of MFMA (kb, m) over keys
+        // 32 kb + 16 m + [0, 16) is two transposing reads (slots 0-3, 4-7)
 #pragma unroll
-        for (int db = 0; db < ND; ++db) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int m = 0; m < 2; ++m) {
+                u32x4 bb = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vb + db * 32 * VPITCH + (2 * kb + m) * 32);
-                    u32x4 bb = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, bb), oacc[db], 0, 0, 0);
+                for (int db = 0; db < ND; ++db) {
+                    const int roff = (32 * kb + 16 * m) * ROWB;
+                    const s16x4 lo = lds_read_tr(stg, voff[db] + roff);
+                    const s16x4 hi = lds_read_tr(stg, voff[db] + roff + 8 * ROWB);
+                    const s16x4 a4[2] = {lo, hi};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                                      __builtin_bit_cast(bf16x8, bb), oacc[db], 0, 0, 0);
                 }
-        }
+            }
+    };
 
-        if (has_next) store_tile(buf ^ 1);
+    if (n_tiles > 0) issue_dma(stage0, 0);
+    // every load issued so far (Q operand, first tile) has landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int t = 0;
+    for (; t + 2 <= n_tiles; t += 2) {
+        issue_dma(stage1, t + 1);
+        compute(stage0, t);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (t + 2 < n_tiles) issue_dma(stage0, t + 2);
+        compute(stage1, t + 1);
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
+    if (t < n_tiles) {
+        compute(stage0, t);
+        __syncthreads();
+    }
+    const float l_acc = l_part[0] + l_part[1];
 
     // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
     const float lt = sum_with_half_swap(l_acc);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    char* ob = smem + wave * 32 * OPITCH;
+    char* ob = stage0 + wave * 32 * OPITCH;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -332,7 +320,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
 #pragma unroll
     for (int i = 0; i < CHUNKS / 64; ++i) {
         const int cid = lane + 64 * i;
-        const int row = cid / KUNITS, u = cid % KUNITS;
+        const int row = cid / UNITS, u = cid % UNITS;
         const int qi = q0 + wave * 32 + row;
         if (qi < L) {
             const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + u * 16);
