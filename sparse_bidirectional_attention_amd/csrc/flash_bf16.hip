@@ -63,9 +63,19 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* base, int off) {
         (LDS_AS s16x4*)((LDS_AS char*)(base) + off));
 }
 
-template <int D, int NW, int MODE>
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 0x3) << 14));
+}
+
+template <int D, int NW, int KT, int NST, int MODE>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
-    constexpr int KT = 64;                  // keys per tile
+    // KT keys per tile (32 or 64), NST LDS stages (tiles in flight: NST - 1)
+    constexpr int KB = KT / 32;             // 32-key MFMA blocks per tile
     constexpr int T = NW * 64;
     constexpr int DK = D / 16;
     constexpr int ND = D / 32;
@@ -76,13 +86,11 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     constexpr int NDMA = SLOTS / T;         // DMA instructions per thread per tile (K; same for V)
     constexpr int ROWS_PER_DMA = T / UNITS;
     constexpr int OPITCH = D * 2;           // epilogue staging row (one-time, conflicts tolerated)
+    constexpr int STAGEB = 2 * TILEB;       // K tile then V tile
     static_assert(NDMA * T == SLOTS && T % UNITS == 0 && ROWS_PER_DMA % 4 == 0, "DMA tiling");
-    static_assert(NW * 32 * OPITCH <= 2 * TILEB, "epilogue staging fits in one stage");
+    static_assert(NW * 32 * OPITCH <= NST * STAGEB, "epilogue staging fits in the stages");
 
-    // Two stages (K tile then V tile each), separate objects so that reads of
-    // one stage are not ordered behind the DMA filling the other.
-    __shared__ __attribute__((aligned(16))) char stage0[2 * TILEB];
-    __shared__ __attribute__((aligned(16))) char stage1[2 * TILEB];
+    __shared__ __attribute__((aligned(16))) char smem[NST * STAGEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -111,7 +119,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     } else if constexpr (MODE == MODE_BLOCK) {
         const int r = bh * p.n_qtiles + qt;
         e0 = p.row_ptr[r];
-        sub_shift = p.block_k == 128 ? 1 : 0;
+        // block_k / KT tiles per kept key block (block_k in {64, 128}, KT in {32, 64})
+        sub_shift = (p.block_k == 128 ? 1 : 0) + (KT == 32 ? 1 : 0);
         n_tiles = (p.row_ptr[r + 1] - e0) << sub_shift;
     } else {
         cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
                 base = t * KT;
             } else {
                 const int J = p.col_idx[e0 + (t >> sub_shift)];
-                base = J * p.block_k + ((t & sub_shift) ? KT : 0);
+                base = J * p.block_k + (t & ((1 << sub_shift) - 1)) * KT;
             }
             nvalid = max(0, min(KT, L - base));
             return base;
@@ -205,22 +214,22 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         int nvalid;
         tile_base(t, nvalid);
         // S^T = K Q^T : two 32-key x 32-query blocks
-        f32x16 sacc[2];
+        f32x16 sacc[KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
         for (int st = 0; st < DK; ++st) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(stg + koff[st] + kb * 32 * ROWB);
                 sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[kb], 0, 0, 0);
             }
         }
         if (nvalid < KT) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         // online softmax (one query per lane; partner lane ^32 holds the rest)
         float mt = -kInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
         mt = max_with_half_swap(mt);
@@ -250,21 +259,21 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         const float mc = (m_used > -kInf) ? m_used * c : 0.f;
         // P^T in bf16 for the PV product; the row sum stays in fp32 (it sets
         // the log-sum-exp, which the column scores need to ~1e-6)
-        uint32_t pk[2][8];
+        uint32_t pk[KB][8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = exp2_fast(fmaf(sacc[kb][r], c, -mc));
                 const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], c, -mc));
                 pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-                l_part[kb] += p0 + p1;
+                l_part[kb & 1] += p0 + p1;
             }
 
         // O^T += V^T P^T; the V^T operand of MFMA (kb, m) over keys
         // 32 kb + 16 m + [0, 16) is two transposing reads (slots 0-3, 4-7)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 u32x4 bb = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
@@ -280,31 +289,37 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             }
     };
 
-    if (n_tiles > 0) issue_dma(stage0, 0);
-    // every load issued so far (Q operand, first tile) has landed
-    __builtin_amdgcn_s_waitcnt(0);
+    // prologue: tiles 0 .. NST-2 in flight
+#pragma unroll
+    for (int s0 = 0; s0 < NST - 1; ++s0)
+        if (s0 < n_tiles) issue_dma(smem + s0 * STAGEB, s0);
+    // One barrier per tile: after it, tile t is in LDS for every wave and every
+    // wave has finished tile t-1, whose stage then receives tile t+NST-1.  The
+    // loop is unrolled over the stages so every LDS offset is a constant.
+    for (int t0 = 0; t0 < n_tiles; t0 += NST) {
+#pragma unroll
+        for (int s = 0; s < NST; ++s) {
+            const int t = t0 + s;
+            if (t < n_tiles) {
+                if (t + NST - 2 < n_tiles) {
+                    // DMA of tiles t+1 .. t+NST-2 may still be in flight
+                    wait_vmcnt<(NST - 2) * 2 * NDMA>();
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
+                __syncthreads();
+                if (t + NST - 1 < n_tiles) issue_dma(smem + ((s + NST - 1) % NST) * STAGEB, t + NST - 1);
+                compute(smem + s * STAGEB, t);
+            }
+        }
+    }
     __syncthreads();
-    int t = 0;
-    for (; t + 2 <= n_tiles; t += 2) {
-        issue_dma(stage1, t + 1);
-        compute(stage0, t);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (t + 2 < n_tiles) issue_dma(stage0, t + 2);
-        compute(stage1, t + 1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-    if (t < n_tiles) {
-        compute(stage0, t);
-        __syncthreads();
-    }
     const float l_acc = l_part[0] + l_part[1];
 
     // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
     const float lt = sum_with_half_swap(l_acc);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    char* ob = stage0 + wave * 32 * OPITCH;
+    char* ob = smem + wave * 32 * OPITCH;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -333,15 +348,36 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     }
 }
 
-template <int D, int NW>
+template <int D, int NW, int KT, int NST>
 hipError_t launch_mode(AttnMode mode, const FlashParams& fp, hipStream_t st) {
     dim3 grid(fp.n_items), block(NW * 64);
     switch (mode) {
-        case MODE_DENSE: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, MODE_DENSE>), grid, block, 0, st, fp); break;
-        case MODE_BLOCK: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, MODE_BLOCK>), grid, block, 0, st, fp); break;
-        case MODE_COLUMN: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, MODE_COLUMN>), grid, block, 0, st, fp); break;
+        case MODE_DENSE: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE_DENSE>), grid, block, 0, st, fp); break;
+        case MODE_BLOCK: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE_BLOCK>), grid, block, 0, st, fp); break;
+        case MODE_COLUMN: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE_COLUMN>), grid, block, 0, st, fp); break;
     }
     return hipGetLastError();
+}
+
+#ifndef FLASH_CFG
+#define FLASH_CFG 0
+#endif
+
+// Tile shapes: 4 waves (128 queries) stream 64-key tiles through two LDS
+// stages (64 KiB, two workgroups per CU); 2 waves (64-query blocks) stream
+// 32-key tiles through two stages (32 KiB, four workgroups per CU).
+template <int D>
+hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st) {
+#if FLASH_CFG == 1
+    if (bq == 64) return launch_mode<D, 2, 32, 2>(mode, fp, st);
+    return launch_mode<D, 4, 32, 4>(mode, fp, st);
+#elif FLASH_CFG == 2
+    if (bq == 64) return launch_mode<D, 2, 32, 4>(mode, fp, st);
+    return launch_mode<D, 4, 64, 2>(mode, fp, st);
+#else
+    if (bq == 64) return launch_mode<D, 2, 32, 2>(mode, fp, st);
+    return launch_mode<D, 4, 64, 2>(mode, fp, st);
+#endif
 }
 
 }  // namespace
@@ -371,8 +407,7 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.c = s.scale * kLog2e;
     fp.thr = 8.0f / fp.c;
     if (fp.n_items == 0) return hipSuccess;
-    if (s.D == 128) return bq == 64 ? launch_mode<128, 2>(mode, fp, st) : launch_mode<128, 4>(mode, fp, st);
-    return bq == 64 ? launch_mode<64, 2>(mode, fp, st) : launch_mode<64, 4>(mode, fp, st);
+    return s.D == 128 ? launch_d<128>(mode, fp, bq, st) : launch_d<64>(mode, fp, bq, st);
 }
 
 }  // namespace sdattn

@@ -137,7 +137,10 @@ def test_full_csr_equals_dense_and_ones_v(bq, bk):
     o3, _ = _out(x["q"], "bf16")
     sd.sdattn_forward_block_sparse(p, x["q"], x["k"], ones, bq, bk, drp, dci, o3, None)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)  # same tiles in the same order
+    if bq == 128:
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)  # same tiles in the same order
+    else:  # 64-query blocks stream 32-key tiles: same result up to rounding order
+        check_out(to_np(o1), to_np(o2), to_np(l1), to_np(l2), "bf16", "full CSR vs dense")
     assert torch.all(o3 == 1.0)
 
 
