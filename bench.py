@@ -278,19 +278,8 @@ def main():
         return float(np.median(a)) if len(a) else None
 
     idx = {a: [t for t in range(K) if acts[t] == a] for a in set(acts)}
-    dense_ms = med(step_ms[idx.get("DENSE", []) + idx.get("DENSE_SELECT", [])]) if (
-        idx.get("DENSE") or idx.get("DENSE_SELECT")) else None
     sparse_ms = med(step_ms[idx["SPARSE"]]) if idx.get("SPARSE") else None
-    select_ms = med(step_ms[idx.get("SELECT_SPARSE", [])]) if idx.get("SELECT_SPARSE") else None
-    if idx.get("DENSE") and idx.get("DENSE_SELECT"):
-        dsel = med(step_ms[idx["DENSE_SELECT"]])
-        select_ms = dsel - dense_ms
-    elif idx.get("DENSE_SELECT") and not idx.get("DENSE"):
-        dense_only = None
-        select_ms = None
-    if select_ms is not None and sparse_ms is not None and idx.get("SELECT_SPARSE"):
-        select_ms = select_ms - sparse_ms
-
+    dense_ms = med(step_ms[idx["DENSE"]]) if idx.get("DENSE") else None
     # dense baseline on the same GPU: the dense forward for every step
     pd = sd.problem(w.batch, H, Hkv, L, d, w.dtype)
     nd = 3 if L >= 32768 else 10
@@ -304,6 +293,15 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     dense_base_ms = e0.elapsed_time(e1) / nd
+
+    if dense_ms is None:
+        dense_ms = dense_base_ms
+    # selection time: a selecting step minus the attention it also runs
+    select_ms = None
+    if idx.get("SELECT_SPARSE") and sparse_ms is not None:
+        select_ms = med(step_ms[idx["SELECT_SPARSE"]]) - sparse_ms
+    elif idx.get("DENSE_SELECT"):
+        select_ms = med(step_ms[idx["DENSE_SELECT"]]) - dense_ms
 
     ms_per_step = total_ms / K
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
