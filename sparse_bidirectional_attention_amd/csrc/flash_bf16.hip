@@ -7,24 +7,27 @@
 //                 blocks in its CSR row (Step-dLLM, Abstract);
 //   column-sparse every query of group g attends a shared list of key
 //                 tokens (PulseCol, Abstract).
-// Each form streams 64-key tiles; only where the tile's rows come from
-// differs.
+// Each form streams key tiles; only where the tile's rows come from differs.
 //
-// Work decomposition: one workgroup per (batch, head, tile of BQ queries),
-// NW = BQ/32 waves, each wave owning 32 query rows.  Per 64-key tile:
-//   * K (64 x d) and V (64 x d) are read from HBM with 16-byte coalesced
-//     loads into registers one tile ahead, then written to LDS: K row-major,
-//     V transposed (d x 64) so both MFMA operands are 16-byte LDS reads.
-//     Double-buffered LDS, one barrier per tile.
-//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (two 32x32 blocks per wave);
-//     computing the transpose puts one query per lane, so the online
-//     softmax max needs a single cross-half exchange and the row sums none.
-//   * P^T is packed to bf16 straight from the MFMA accumulator layout; the
-//     V^T tile is stored in LDS in the matching key order, so
-//     O^T += V^T P^T needs no register shuffles.
-//   * The running max is only raised when it grows by more than 2^8 in
-//     probability units (rescaling O is skipped otherwise; exact, since the
-//     final normalisation uses the same reference max).
+// Work decomposition: one workgroup per (batch, head, tile of 32 NW queries),
+// each of the NW waves owning 32 query rows.  Per KT-key tile (KT = 64, or 32
+// for 64-query blocks):
+//   * the K and V rows of the tile go from HBM straight into LDS with the
+//     buffer-to-LDS DMA, NST stages deep (one barrier per tile); each lane
+//     fetches the 16-byte chunk that belongs at its LDS slot, so the tile
+//     lands XOR-swizzled and every MFMA operand read is conflict-free;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16, Q held in registers;
+//     computing the transpose puts one query per lane, so row sums stay
+//     in-lane;
+//   * P^T is packed to bf16 straight from the MFMA accumulator layout and is
+//     the B operand of O^T += V^T P^T, whose A operand comes from the
+//     row-major V tile through the transposing LDS read;
+//   * the softmax reference is the maximum of the first tile, not a running
+//     maximum: the other tiles exponentiate against it without a per-tile
+//     maximum or branch, and a row whose sum leaves a safe range is redone
+//     in a second pass that raises the reference whenever a block's
+//     probabilities grow too large (exact either way: numerator and
+//     denominator share the reference).
 // The log-sum-exp (natural log) is written per query row.
 
 #include <type_traits>
@@ -46,12 +49,21 @@ struct FlashParams {
     int Hq, Hkv, L, group, n_qtiles, n_items, block_k, kcol, xcd_group;
     float c;      // scale * log2(e)
     float scale;  // softmax scale
-    float thr;    // lazy-rescale threshold in raw score units
 };
 
 // Raw buffer descriptor word 3 for gfx9-family parts: 32-bit data format,
 // offsets checked against num_records (loads past it return zero).
 constexpr int kRsrcWord3 = 0x00020000;
+
+// Bound on one lane's sum of 16 probabilities before the reference is raised
+// (checked tiles), and on a lane's whole row sum after an unchecked pass.
+constexpr float kBigSum = 0x1p64f;
+constexpr float kBigRow = 0x1p32f;
+
+// instruction classes for __builtin_amdgcn_sched_group_barrier
+constexpr int SG_VALU = 0x002;
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DSR = 0x100;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -112,23 +124,34 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int q0 = qt * (NW * 32);
 
     // ---- tile source ------------------------------------------------------
-    int n_tiles = 0, e0 = 0, sub_shift = 0;
+    // n_tiles tiles, of which the first n_full hold KT in-range keys; only
+    // the end of the sequence (dense), the last kept block of a row (block:
+    // rows are ascending) or the end of the column list can be partial.
+    int n_tiles = 0, n_full = 0, e0 = 0, sub_shift = 0;
     const int32_t* cb = nullptr;
     if constexpr (MODE == MODE_DENSE) {
         n_tiles = (L + KT - 1) / KT;
+        n_full = L / KT;
     } else if constexpr (MODE == MODE_BLOCK) {
         const int r = bh * p.n_qtiles + qt;
         e0 = p.row_ptr[r];
+        const int ne = p.row_ptr[r + 1] - e0;
         // block_k / KT tiles per kept key block (block_k in {64, 128}, KT in {32, 64})
         sub_shift = (p.block_k == 128 ? 1 : 0) + (KT == 32 ? 1 : 0);
-        n_tiles = (p.row_ptr[r + 1] - e0) << sub_shift;
+        if (ne > 0) {
+            const int rem = L - p.col_idx[e0 + ne - 1] * p.block_k;  // keys of the last block in range
+            const int per = 1 << sub_shift;
+            n_tiles = ((ne - 1) << sub_shift) + min(per, (rem + KT - 1) / KT);
+            n_full = ((ne - 1) << sub_shift) + min(per, rem / KT);
+        }
     } else {
         cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
         n_tiles = (p.kcol + KT - 1) / KT;
+        n_full = p.kcol / KT;
     }
     // first key of tile t (dense / block: a token index; column: an entry of
     // the column list) and the number of real keys in it
-    auto tile_base = [&](int t, int& nvalid) -> int {
+    auto tile_base = [&](int t, int& nvalid) __attribute__((always_inline)) -> int {
         if constexpr (MODE == MODE_COLUMN) {
             nvalid = min(KT, p.kcol - t * KT);
             return t * KT;
@@ -151,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // The DMA writes 16 bytes per lane at consecutive LDS slots; each lane
     // fetches the HBM chunk that belongs at its slot.
     const int dr0 = tid / UNITS, dpu = tid % UNITS;  // row / physical unit of slot `tid`
-    auto issue_dma = [&](char* stage, int t) {
+    auto issue_dma = [&](char* stage, int t) __attribute__((always_inline)) {
         int nv;
         const int base = tile_base(t, nv);
 #pragma unroll
@@ -206,115 +229,196 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m_used = -kInf;
-    float l_part[2] = {0.f, 0.f};
+    // Softmax reference: probabilities are exp2(s c - mc) with mc = m_ref c.
+    // m_ref is not the running maximum; it is only raised when a half tile's
+    // probabilities sum past kBig in some lane (or when no reference exists
+    // yet, mc = -inf, which makes every sum inf or NaN).  Any reference gives
+    // the same normalised result; kBig only keeps O and l finite.
+    float m_ref = -kInf;
+    float mc = -kInf;
+    float l_acc = 0.f;
     const float c = p.c;
 
-    auto compute = [&](const char* stg, int t) {
-        int nvalid;
-        tile_base(t, nvalid);
-        // S^T = K Q^T : two 32-key x 32-query blocks
-        f32x16 sacc[KB];
+    auto qk = [&](const char* stg, int kb, f32x16& acc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int st = 0; st < DK; ++st) {
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(stg + koff[st] + kb * 32 * ROWB);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], sacc[kb], 0, 0, 0);
-            }
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(stg + koff[st] + kb * 32 * ROWB);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[st], acc, 0, 0, 0);
         }
-        if (nvalid < KT) {
+    };
+    auto mask = [&](int kb, int nvalid, f32x16& acc) __attribute__((always_inline)) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (key >= nvalid) sacc[kb][r] = -kInf;
-                }
+        for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (key >= nvalid) acc[r] = -kInf;
         }
-
-        // online softmax (one query per lane; partner lane ^32 holds the rest)
+    };
+    // P^T of one 32-key block in bf16 and its fp32 sum in this lane
+    auto exps = [&](const f32x16& s, float mcu, uint32_t (&pk)[8]) __attribute__((always_inline)) -> float {
+        float pair[8];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2_fast(fmaf(s[r], c, -mcu));
+            const float p1 = exp2_fast(fmaf(s[r + 1], c, -mcu));
+            pk[r >> 1] = pack_bf16x2(p0, p1);
+            pair[r >> 1] = p0 + p1;
+        }
+        return ((pair[0] + pair[1]) + (pair[2] + pair[3])) + ((pair[4] + pair[5]) + (pair[6] + pair[7]));
+    };
+    // raise the reference to this block's maximum, rescale O and l, redo P
+    auto rebase = [&](const f32x16& s, uint32_t (&pk)[8]) __attribute__((always_inline)) -> float {
         float mt = -kInf;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sacc[kb][r]);
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[r]);
         mt = max_with_half_swap(mt);
-        const float mnew = fmaxf(m_used, mt);
-        const bool need = mnew > m_used + p.thr;
-        if (__any(need)) {
-            const float alpha = need ? exp2_fast((m_used - mnew) * c) : 1.f;
-            m_used = need ? mnew : m_used;
-            l_part[0] *= alpha;
-            l_part[1] *= alpha;
+        if (mt > m_ref) {
+            const float alpha = (m_ref > -kInf) ? exp2_fast((m_ref - mt) * c) : 0.f;
+            m_ref = mt;
+            mc = mt * c;
+            l_acc *= alpha;
 #pragma unroll
             for (int db = 0; db < ND; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         }
-        const float mc = (m_used > -kInf) ? m_used * c : 0.f;
-        // P^T in bf16 for the PV product; the row sum stays in fp32 (it sets
-        // the log-sum-exp, which the column scores need to ~1e-6)
-        uint32_t pk[KB][8];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float p0 = exp2_fast(fmaf(sacc[kb][r], c, -mc));
-                const float p1 = exp2_fast(fmaf(sacc[kb][r + 1], c, -mc));
-                pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-                l_part[kb & 1] += p0 + p1;
-            }
-
-        // O^T += V^T P^T; the V^T operand of MFMA (kb, m) over keys
-        // 32 kb + 16 m + [0, 16) is two transposing reads (slots 0-3, 4-7)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                u32x4 bb = {pk[kb][4 * m], pk[kb][4 * m + 1], pk[kb][4 * m + 2], pk[kb][4 * m + 3]};
-#pragma unroll
-                for (int db = 0; db < ND; ++db) {
-                    const int roff = (32 * kb + 16 * m) * ROWB;
-                    const s16x4 lo = lds_read_tr(stg, voff[db] + roff);
-                    const s16x4 hi = lds_read_tr(stg, voff[db] + roff + 8 * ROWB);
-                    const s16x4 a4[2] = {lo, hi};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
-                                                                      __builtin_bit_cast(bf16x8, bb), oacc[db], 0, 0, 0);
-                }
-            }
+        return exps(s, (m_ref > -kInf) ? mc : 0.f, pk);
     };
-
-    // prologue: tiles 0 .. NST-2 in flight
+    auto softmax = [&](const f32x16& s, uint32_t (&pk)[8]) __attribute__((always_inline)) {
+        float ts = exps(s, mc, pk);
+        if (__any(!(ts <= kBigSum))) ts = rebase(s, pk);
+        l_acc += ts;
+    };
+    // O^T += V^T P^T; the V^T operand of MFMA (kb, m) over keys
+    // 32 kb + 16 m + [0, 16) is two transposing reads (slots 0-3, 4-7)
+    auto pv = [&](const char* stg, int kb, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int s0 = 0; s0 < NST - 1; ++s0)
-        if (s0 < n_tiles) issue_dma(smem + s0 * STAGEB, s0);
-    // One barrier per tile: after it, tile t is in LDS for every wave and every
-    // wave has finished tile t-1, whose stage then receives tile t+NST-1.  The
-    // loop is unrolled over the stages so every LDS offset is a constant.
-    for (int t0 = 0; t0 < n_tiles; t0 += NST) {
+        for (int m = 0; m < 2; ++m) {
+            u32x4 bb = {pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
 #pragma unroll
-        for (int s = 0; s < NST; ++s) {
-            const int t = t0 + s;
-            if (t < n_tiles) {
-                if (t + NST - 2 < n_tiles) {
-                    // DMA of tiles t+1 .. t+NST-2 may still be in flight
-                    wait_vmcnt<(NST - 2) * 2 * NDMA>();
-                } else {
-                    __builtin_amdgcn_s_waitcnt(0);
-                }
-                __syncthreads();
-                if (t + NST - 1 < n_tiles) issue_dma(smem + ((s + NST - 1) % NST) * STAGEB, t + NST - 1);
-                compute(smem + s * STAGEB, t);
+            for (int db = 0; db < ND; ++db) {
+                const int roff = (32 * kb + 16 * m) * ROWB;
+                const s16x4 lo = lds_read_tr(stg, voff[db] + roff);
+                const s16x4 hi = lds_read_tr(stg, voff[db] + roff + 8 * ROWB);
+                const s16x4 a4[2] = {lo, hi};
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                                  __builtin_bit_cast(bf16x8, bb), oacc[db], 0, 0, 0);
             }
         }
+    };
+    // One tile.  Program order puts independent MFMA and VALU work side by
+    // side (QK of block 1 with the softmax of block 0, PV of block 0 with the
+    // softmax of block 1) so the scheduler can interleave them.
+    auto compute_tile = [&](const char* stg, int nvalid, auto masked, auto checked) __attribute__((always_inline)) {
+        f32x16 s0, s1;
+        uint32_t pk0[8], pk1[8];
+        qk(stg, 0, s0);
+        if constexpr (masked.value) mask(0, nvalid, s0);
+        if constexpr (KB == 2) {
+            qk(stg, 1, s1);
+            if constexpr (masked.value) mask(1, nvalid, s1);
+        }
+        float ts0 = exps(s0, mc, pk0);
+        if constexpr (KB == 2 && !masked.value) {
+            // K reads four ahead of the QK MFMAs; the softmax of block 0
+            // fills the gaps between the MFMAs of block 1
+            __builtin_amdgcn_sched_group_barrier(SG_DSR, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (i < 4) __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 6, 0);
+            }
+        }
+        if constexpr (checked.value)
+            if (__any(!(ts0 <= kBigSum))) ts0 = rebase(s0, pk0);
+        l_acc += ts0;
+        pv(stg, 0, pk0);
+        if constexpr (KB == 2) {
+            float ts1 = exps(s1, mc, pk1);
+            if constexpr (!masked.value) {
+                // V^T reads four ahead of the PV MFMAs of block 0, with the
+                // softmax of block 1 between them
+                __builtin_amdgcn_sched_group_barrier(SG_DSR, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (i < 6) __builtin_amdgcn_sched_group_barrier(SG_DSR, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+                }
+            }
+            if constexpr (checked.value)
+                if (__any(!(ts1 <= kBigSum))) ts1 = rebase(s1, pk1);
+            l_acc += ts1;
+            pv(stg, 1, pk1);
+            if constexpr (!masked.value) {
+                __builtin_amdgcn_sched_group_barrier(SG_DSR, 4, 0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                    if (i < 6) __builtin_amdgcn_sched_group_barrier(SG_DSR, 2, 0);
+                }
+            }
+        }
+    };
+    // One barrier per tile: after it, tile t is in LDS for every wave and every
+    // wave has finished tile t-1, whose stage then receives tile t+NST-1.
+    auto step = [&](int t, int s, auto masked, auto checked) __attribute__((always_inline)) {
+        if (t + NST - 2 < n_tiles) {
+            // DMA of tiles t+1 .. t+NST-2 may still be in flight
+            wait_vmcnt<(NST - 2) * 2 * NDMA>();
+        } else {
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        __syncthreads();
+        if (t + NST - 1 < n_tiles) issue_dma(smem + ((s + NST - 1) % NST) * STAGEB, t + NST - 1);
+        int nvalid;
+        tile_base(t, nvalid);
+        compute_tile(smem + s * STAGEB, nvalid, masked, checked);
+    };
+    // One pass over the tiles.  Tile 0 is always checked, which sets the
+    // reference to its maximum; the other tiles are checked only in a
+    // checked pass.
+    auto run_pass = [&](auto checked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s0 = 0; s0 < NST - 1; ++s0)
+            if (s0 < n_tiles) issue_dma(smem + s0 * STAGEB, s0);
+        if (n_tiles == 0) return;
+        if (n_full > 0)
+            step(0, 0, std::false_type{}, std::true_type{});
+        else
+            step(0, 0, std::true_type{}, std::true_type{});
+        // full tiles, unrolled over the stages so every LDS offset is a
+        // constant (t = 1 mod NST throughout)
+        int t = 1;
+        for (; t + NST <= n_full; t += NST) {
+#pragma unroll
+            for (int s = 0; s < NST; ++s) step(t + s, (1 + s) % NST, std::false_type{}, checked);
+        }
+        // the rest (at most NST - 1 full tiles and the partial ones), masked
+        for (; t < n_tiles; ++t) step(t, t % NST, std::true_type{}, checked);
+    };
+    // Unchecked pass: probabilities relative to tile 0's maximum are not
+    // bounded, so a lane whose row sum leaves [0, 2^32] (including inf and
+    // NaN) sends the whole workgroup through a second, checked pass.
+    run_pass(std::false_type{});
+    if (__syncthreads_or(!(l_acc <= kBigRow))) {
+        m_ref = -kInf;
+        mc = -kInf;
+        l_acc = 0.f;
+#pragma unroll
+        for (int db = 0; db < ND; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+        run_pass(std::true_type{});
     }
     __syncthreads();
-    const float l_acc = l_part[0] + l_part[1];
 
     // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
     const float lt = sum_with_half_swap(l_acc);
@@ -344,40 +448,35 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     }
     if (p.lse != nullptr && hl == 0) {
         const int qi = q0 + wave * 32 + l32;
-        if (qi < L) p.lse[obase + qi] = lt > 0.f ? m_used * p.scale + __logf(lt) : -kInf;
+        if (qi < L) p.lse[obase + qi] = lt > 0.f ? m_ref * p.scale + __logf(lt) : -kInf;
     }
 }
 
-template <int D, int NW, int KT, int NST>
-hipError_t launch_mode(AttnMode mode, const FlashParams& fp, hipStream_t st) {
-    dim3 grid(fp.n_items), block(NW * 64);
-    switch (mode) {
-        case MODE_DENSE: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE_DENSE>), grid, block, 0, st, fp); break;
-        case MODE_BLOCK: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE_BLOCK>), grid, block, 0, st, fp); break;
-        case MODE_COLUMN: hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE_COLUMN>), grid, block, 0, st, fp); break;
-    }
+template <int D, int NW, int KT, int NST, int MODE>
+hipError_t launch_one(const FlashParams& fp, hipStream_t st) {
+    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE>), dim3(fp.n_items), dim3(NW * 64), 0, st, fp);
     return hipGetLastError();
 }
 
-#ifndef FLASH_CFG
-#define FLASH_CFG 0
-#endif
+// Query tile of a launch: 64- or 128-query blocks for the block-sparse form,
+// 256 queries otherwise.
+inline int query_tile(AttnMode mode, const SparseIndex& ix) { return mode == MODE_BLOCK ? ix.block_q : 256; }
 
-// Tile shapes: 4 waves (128 queries) stream 64-key tiles through two LDS
-// stages (64 KiB, two workgroups per CU); 2 waves (64-query blocks) stream
-// 32-key tiles through two stages (32 KiB, four workgroups per CU).
+// Tile shapes (waves, keys per tile, LDS stages):
+//   256-query tiles (dense, column): 8 waves, 64-key tiles, two stages (64 KiB);
+//   128-query blocks: 4 waves, 64-key tiles, two stages (64 KiB, two
+//   workgroups per CU);
+//   64-query blocks: 2 waves, 32-key tiles, two stages (32 KiB).
 template <int D>
 hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st) {
-#if FLASH_CFG == 1
-    if (bq == 64) return launch_mode<D, 2, 32, 2>(mode, fp, st);
-    return launch_mode<D, 4, 32, 4>(mode, fp, st);
-#elif FLASH_CFG == 2
-    if (bq == 64) return launch_mode<D, 2, 32, 4>(mode, fp, st);
-    return launch_mode<D, 4, 64, 2>(mode, fp, st);
-#else
-    if (bq == 64) return launch_mode<D, 2, 32, 2>(mode, fp, st);
-    return launch_mode<D, 4, 64, 2>(mode, fp, st);
-#endif
+    switch (mode) {
+        case MODE_DENSE: return launch_one<D, 8, 64, 2, MODE_DENSE>(fp, st);
+        case MODE_COLUMN: return launch_one<D, 8, 64, 2, MODE_COLUMN>(fp, st);
+        case MODE_BLOCK:
+            if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK>(fp, st);
+            return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -385,7 +484,7 @@ hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st
 hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, const void* k,
                              const void* v, void* o, float* lse, const SparseIndex& ix,
                              hipStream_t st) {
-    const int bq = mode == MODE_BLOCK ? ix.block_q : 128;
+    const int bq = query_tile(mode, ix);
     FlashParams fp{};
     fp.q = static_cast<const uint16_t*>(q);
     fp.k = static_cast<const uint16_t*>(k);
@@ -405,7 +504,6 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.xcd_group = (fp.n_qtiles % 8 == 0) ? fp.n_qtiles : 0;
     fp.scale = s.scale;
     fp.c = s.scale * kLog2e;
-    fp.thr = 8.0f / fp.c;
     if (fp.n_items == 0) return hipSuccess;
     return s.D == 128 ? launch_d<128>(mode, fp, bq, st) : launch_d<64>(mode, fp, bq, st);
 }
