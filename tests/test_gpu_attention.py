@@ -11,7 +11,7 @@ import torch
 import oracle
 import sparse_bidirectional_attention_amd as sd
 from gpu_util import check_out, dev_csr, host_inputs, say, to_dev, to_np
-from workloads import tiny_random
+from workloads import score_jump, tiny_random
 
 pytestmark = pytest.mark.gpu
 
@@ -162,3 +162,38 @@ def test_zero_length_is_a_noop():
     e = torch.empty(0, device="cuda", dtype=torch.bfloat16)
     sd.sdattn_forward_dense(p, e, e, e, e, None)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("jump", [2.0, 4.0])
+@pytest.mark.parametrize("form", ["dense", "block128", "block64", "column"])
+def test_scores_far_above_the_first_tile(form, jump):
+    """The first keys of every row score about 45 (jump 2) or 90 (jump 4)
+    nats below the largest later keys, so probabilities taken against the
+    first tile's maximum leave the safe range (jump 2) or overflow fp32
+    (jump 4); those rows must come out of the checked pass equal to the
+    oracle."""
+    say(f"score jump {jump} {form}")
+    B, Hq, Hkv, L, d = 1, 2, 1, 300, 128
+    x = {n: to_dev(a) for n, a in score_jump(int(jump), B, Hq, Hkv, L, d, jump).items()}
+    o, lse = _out(x["q"], "bf16")
+    p = sd.problem_of(x["q"], x["k"])
+    hq, hk, hv = (host_inputs(x[n]) for n in "qkv")
+    if form == "dense":
+        sd.sdattn_forward_dense(p, x["q"], x["k"], x["v"], o, lse)
+        ro, rl = oracle.dense_attention(hq, hk, hv)
+    elif form.startswith("block"):
+        bq = int(form[5:])
+        nqb = -(-L // bq)
+        rows = B * Hq * nqb
+        rp = (np.arange(rows + 1) * nqb).astype(np.int32)
+        ci = np.tile(np.arange(nqb), rows).astype(np.int32)
+        drp, dci = dev_csr(rp, ci)
+        sd.sdattn_forward_block_sparse(p, x["q"], x["k"], x["v"], bq, bq, drp, dci, o, lse)
+        ro, rl = oracle.block_sparse_attention(hq, hk, hv, rp, ci, bq, bq)
+    else:
+        cols = np.arange(0, L, 2, dtype=np.int32)[None, None]
+        sd.sdattn_forward_column_sparse(p, x["q"], x["k"], x["v"], torch.from_numpy(cols).cuda(), cols.shape[-1], o, lse)
+        ro, rl = oracle.column_sparse_attention(hq, hk, hv, cols)
+    torch.cuda.synchronize()
+    assert np.isfinite(to_np(o)).all()
+    check_out(to_np(o), ro, to_np(lse), rl, "bf16", f"score jump {jump} {form}")

@@ -12,5 +12,6 @@ from .generate import (  # noqa: F401
     f32_to_bf16_bits,
     make_base,
     make_step,
+    score_jump,
     tiny_random,
 )

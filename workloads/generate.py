@@ -178,3 +178,20 @@ def tiny_random(seed: int, B, Hq, Hkv, L, d, dtype="f32", scale=1.0):
     if dtype == "bf16":
         out = {n: f32_to_bf16_bits(x) for n, x in out.items()}
     return out
+
+
+def score_jump(seed: int, B, Hq, Hkv, L, d, jump, n_low=64, dtype="bf16"):
+    """Q near +1 in every component; the first n_low keys near -jump, every
+    37th later key near +jump and the rest small, so the first keys score
+    about 2 jump sqrt(d) below the largest ones.  V is N(0, 1/4)."""
+    r = _rng(9100, seed)
+    q = (1.0 + 0.1 * r.standard_normal((B, Hq, L, d))).astype(np.float32)
+    k = (0.3 * r.standard_normal((B, Hkv, L, d))).astype(np.float32)
+    k[:, :, :n_low] = -jump * (1.0 + 0.1 * r.standard_normal((B, Hkv, min(n_low, L), d)))
+    hi = np.arange(n_low, L, 37)
+    k[:, :, hi] = jump * (1.0 + 0.1 * r.standard_normal((B, Hkv, len(hi), d)))
+    v = (0.5 * r.standard_normal((B, Hkv, L, d))).astype(np.float32)
+    out = {"q": q, "k": k, "v": v}
+    if dtype == "bf16":
+        out = {n: f32_to_bf16_bits(x) for n, x in out.items()}
+    return out
