@@ -86,6 +86,9 @@ typedef struct {
     sdattn_dtype dtype;
     float softmax_scale; /* <= 0: 1/sqrt(d) */
 } sdattn_problem;
+/* Shape limits (SDATTN_ERR_SHAPE beyond): B * Hq * (L + 63) <= 2e9, and
+ * (L + 128) * d * 4 < 2^32 - 2^16 (one head's K or V rows are addressed with
+ * 32-bit byte offsets). */
 
 typedef enum { SDATTN_BUDGET_TOPK = 0, SDATTN_BUDGET_MASS = 1 } sdattn_budget_kind;
 

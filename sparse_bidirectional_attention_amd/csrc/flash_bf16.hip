@@ -60,6 +60,11 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kBigSum = 0x1p64f;
 constexpr float kBigRow = 0x1p32f;
 
+// A buffer offset at or beyond every valid one (tile past the end): the
+// range check returns zeros.  Valid offsets stay below it while L * 2d bytes
+// fit in kOOB.
+constexpr uint32_t kOOB = 0xFFFF0000u;
+
 // instruction classes for __builtin_amdgcn_sched_group_barrier
 constexpr int SG_VALU = 0x002;
 constexpr int SG_MFMA = 0x008;
@@ -73,6 +78,28 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ s16x4 lds_read_tr(const char* base, int off) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (LDS_AS s16x4*)((LDS_AS char*)(base) + off));
+}
+
+// 32-bit LDS address of a shared-memory pointer, as a wave-uniform value
+__device__ __forceinline__ uint32_t lds_addr(LDS_AS char* ptr) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ptr)));
+}
+
+// 16-byte buffer load of every lane into LDS at lds + 16 * lane (the
+// buffer-to-LDS DMA; offsets at or past the range read as zero).  Issued
+// through asm because the compiler, unable to tell which stage a DMA writes,
+// would otherwise wait for it before every later LDS read; the kernel orders
+// DMA and LDS reads itself (memory-count wait and barrier once per tile).
+__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voffset), "s"(rsrc));
 }
 
 // s_waitcnt until at most N vector-memory operations of this wave are
@@ -127,7 +154,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // n_tiles tiles, of which the first n_full hold KT in-range keys; only
     // the end of the sequence (dense), the last kept block of a row (block:
     // rows are ascending) or the end of the column list can be partial.
-    int n_tiles = 0, n_full = 0, e0 = 0, sub_shift = 0;
+    int n_tiles = 0, n_full = 0, e0 = 0, ne = 0, sub_shift = 0;
     const int32_t* cb = nullptr;
     if constexpr (MODE == MODE_DENSE) {
         n_tiles = (L + KT - 1) / KT;
@@ -135,7 +162,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     } else if constexpr (MODE == MODE_BLOCK) {
         const int r = bh * p.n_qtiles + qt;
         e0 = p.row_ptr[r];
-        const int ne = p.row_ptr[r + 1] - e0;
+        ne = p.row_ptr[r + 1] - e0;
         // block_k / KT tiles per kept key block (block_k in {64, 128}, KT in {32, 64})
         sub_shift = (p.block_k == 128 ? 1 : 0) + (KT == 32 ? 1 : 0);
         if (ne > 0) {
@@ -149,51 +176,75 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         n_tiles = (p.kcol + KT - 1) / KT;
         n_full = p.kcol / KT;
     }
-    // first key of tile t (dense / block: a token index; column: an entry of
-    // the column list) and the number of real keys in it
-    auto tile_base = [&](int t, int& nvalid) __attribute__((always_inline)) -> int {
-        if constexpr (MODE == MODE_COLUMN) {
-            nvalid = min(KT, p.kcol - t * KT);
-            return t * KT;
-        } else {
-            int base;
-            if constexpr (MODE == MODE_DENSE) {
-                base = t * KT;
-            } else {
-                const int J = p.col_idx[e0 + (t >> sub_shift)];
-                base = J * p.block_k + (t & ((1 << sub_shift) - 1)) * KT;
-            }
-            nvalid = max(0, min(KT, L - base));
-            return base;
-        }
+    // first key of tile u (dense / block: a token index; column: an entry of
+    // the column list); J is the tile's kept block (block form)
+    auto tile_key0 = [&](int u, int J) __attribute__((always_inline)) -> int {
+        if constexpr (MODE == MODE_BLOCK)
+            return J * p.block_k + (u & ((1 << sub_shift) - 1)) * KT;
+        else
+            return u * KT;
+    };
+    // number of real keys in the tile that starts at key0
+    auto tile_valid = [&](int key0) __attribute__((always_inline)) -> int {
+        if constexpr (MODE == MODE_COLUMN)
+            return min(KT, p.kcol - key0);
+        else
+            return max(0, min(KT, L - key0));
+    };
+    auto block_of = [&](int u) __attribute__((always_inline)) -> int {
+        return p.col_idx[e0 + min(u >> sub_shift, ne - 1)];
     };
 
     // LDS layouts (16-byte units, XOR-swizzled so that reads hit distinct banks):
     //   K tile: row r (key), unit u stored at unit u ^ (r & (UNITS-1));
     //   V tile: row r (key), unit u stored at unit u ^ (4 (r & 3)) mod UNITS.
     // The DMA writes 16 bytes per lane at consecutive LDS slots; each lane
-    // fetches the HBM chunk that belongs at its slot.
+    // fetches the HBM chunk that belongs at its slot.  All of a chunk's
+    // offset is in the VGPR offset, which the buffer range check covers:
+    // rows past L, and tiles past the last one (offset kOOB), read as zero.
     const int dr0 = tid / UNITS, dpu = tid % UNITS;  // row / physical unit of slot `tid`
-    auto issue_dma = [&](char* stage, int t) __attribute__((always_inline)) {
-        int nv;
-        const int base = tile_base(t, nv);
+    int kslot[NDMA], vslot[NDMA];  // byte offset of this lane's chunks within a tile (column: within a row)
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int row = dr0 + i * ROWS_PER_DMA;
+        const int uk = dpu ^ (row & (UNITS - 1));
+        const int uv = dpu ^ ((4 * (row & 3)) & (UNITS - 1));
+        const int rowb = MODE == MODE_COLUMN ? 0 : row * ROWB;
+        kslot[i] = rowb + uk * 16;
+        vslot[i] = rowb + uv * 16;
+    }
+    // Source of the next tile to fetch, loaded one step ahead so that no index
+    // load sits between a barrier and the DMA it feeds: the kept block (block
+    // form) or this lane's key per DMA row (column form).
+    int jn = 0;
+    int kn[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) kn[i] = 0;
+    constexpr int NPF = MODE == MODE_BLOCK ? 1 : (MODE == MODE_COLUMN ? NDMA : 0);  // loads per prefetch
+    auto prefetch_src = [&](int u) __attribute__((always_inline)) {
+        if constexpr (MODE == MODE_BLOCK) {
+            jn = block_of(u);
+        } else if constexpr (MODE == MODE_COLUMN) {
+#pragma unroll
+            for (int i = 0; i < NDMA; ++i) kn[i] = cb[min(u * KT + dr0 + i * ROWS_PER_DMA, p.kcol - 1)];
+        }
+    };
+    // DMA of tile u into `stage` from the prefetched source
+    auto dma_tile = [&](char* stage, int u) __attribute__((always_inline)) {
+        const bool live = u < n_tiles;
+        const int key0 = tile_key0(u, jn);
+        const int nv = tile_valid(key0);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
-            const int row = dr0 + i * ROWS_PER_DMA;
-            const int uk = dpu ^ (row & (UNITS - 1));
-            const int uv = dpu ^ ((4 * (row & 3)) & (UNITS - 1));
             LDS_AS char* kdst = (LDS_AS char*)(stage) + (i * T + wave * 64) * 16;
             LDS_AS char* vdst = kdst + TILEB;
-            if constexpr (MODE == MODE_COLUMN) {
-                const int key = cb[base + min(row, nv - 1)];
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, key * ROWB + uk * 16, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, key * ROWB + uv * 16, 0, 0, 0);
-            } else {
-                // rows past L read as zero (buffer range check)
-                const int soff = (base + i * ROWS_PER_DMA) * ROWB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, dr0 * ROWB + uk * 16, soff, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, dr0 * ROWB + uv * 16, soff, 0, 0);
-            }
+            uint32_t base;
+            if constexpr (MODE == MODE_COLUMN)
+                base = (live && dr0 + i * ROWS_PER_DMA < nv) ? static_cast<uint32_t>(kn[i]) * ROWB : kOOB;
+            else
+                base = live ? static_cast<uint32_t>(key0) * ROWB : kOOB;
+            dma_load16(rk, lds_addr(kdst), base + kslot[i]);
+            dma_load16(rv, lds_addr(vdst), base + vslot[i]);
         }
     };
 
@@ -368,28 +419,36 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         }
     };
     // One barrier per tile: after it, tile t is in LDS for every wave and every
-    // wave has finished tile t-1, whose stage then receives tile t+NST-1.
+    // wave has finished tile t-1, whose stage then receives tile t+NST-1 (a
+    // DMA is issued every step; past the last tile it reads zeros).
     auto step = [&](int t, int s, auto masked, auto checked) __attribute__((always_inline)) {
-        if (t + NST - 2 < n_tiles) {
-            // DMA of tiles t+1 .. t+NST-2 may still be in flight
-            wait_vmcnt<(NST - 2) * 2 * NDMA>();
-        } else {
-            __builtin_amdgcn_s_waitcnt(0);
-        }
+        // the DMA (and source prefetch) of tiles t+1 .. t+NST-2 may still be in flight
+        wait_vmcnt<(NST - 2) * (2 * NDMA + NPF)>();
         __syncthreads();
-        if (t + NST - 1 < n_tiles) issue_dma(smem + ((s + NST - 1) % NST) * STAGEB, t + NST - 1);
-        int nvalid;
-        tile_base(t, nvalid);
+        dma_tile(smem + ((s + NST - 1) % NST) * STAGEB, t + NST - 1);
+        prefetch_src(t + NST);
+        // keep the DMA issue first: it has one tile of compute to land
+        __builtin_amdgcn_sched_barrier(0);
+        int nvalid = KT;
+        if constexpr (masked.value) {
+            int J = 0;
+            if constexpr (MODE == MODE_BLOCK) J = block_of(t);
+            nvalid = tile_valid(tile_key0(t, J));
+        }
         compute_tile(smem + s * STAGEB, nvalid, masked, checked);
+        __builtin_amdgcn_sched_barrier(0);
     };
     // One pass over the tiles.  Tile 0 is always checked, which sets the
     // reference to its maximum; the other tiles are checked only in a
     // checked pass.
     auto run_pass = [&](auto checked) __attribute__((always_inline)) {
-#pragma unroll
-        for (int s0 = 0; s0 < NST - 1; ++s0)
-            if (s0 < n_tiles) issue_dma(smem + s0 * STAGEB, s0);
         if (n_tiles == 0) return;
+#pragma unroll
+        for (int s0 = 0; s0 < NST - 1; ++s0) {
+            prefetch_src(s0);
+            dma_tile(smem + s0 * STAGEB, s0);
+        }
+        prefetch_src(NST - 1);
         if (n_full > 0)
             step(0, 0, std::false_type{}, std::true_type{});
         else
@@ -403,6 +462,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         }
         // the rest (at most NST - 1 full tiles and the partial ones), masked
         for (; t < n_tiles; ++t) step(t, t % NST, std::true_type{}, checked);
+        // DMA past the last tile (zeros) and the last prefetch
+        __builtin_amdgcn_s_waitcnt(0);
     };
     // Unchecked pass: probabilities relative to tile 0's maximum are not
     // bounded, so a lane whose row sum leaves [0, 2^32] (including inf and

@@ -34,6 +34,10 @@ sdattn_status check_problem(const sdattn_problem* p, Problem* out) {
     // every index the kernels form stays within 32-bit grid / row counts
     const double rows = static_cast<double>(p->batch) * p->q_heads * (p->seq_len + 63.0);
     if (rows > 2.0e9) return fail(SDATTN_ERR_SHAPE, "batch * q_heads * seq_len too large");
+    // one head's K or V slab (plus a tile of rows past its end) is addressed
+    // with 32-bit byte offsets
+    const double slab = (p->seq_len + 128.0) * p->head_dim * 4.0;
+    if (slab >= 4294901760.0) return fail(SDATTN_ERR_SHAPE, "seq_len * head_dim too large");
     out->B = p->batch;
     out->Hq = p->q_heads;
     out->Hkv = p->kv_heads;
