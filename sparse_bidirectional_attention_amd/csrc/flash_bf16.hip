@@ -213,39 +213,53 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         kslot[i] = rowb + uk * 16;
         vslot[i] = rowb + uv * 16;
     }
-    // Source of the next tile to fetch, loaded one step ahead so that no index
-    // load sits between a barrier and the DMA it feeds: the kept block (block
-    // form) or this lane's key per DMA row (column form).
-    int jn = 0;
-    int kn[NDMA];
-#pragma unroll
-    for (int i = 0; i < NDMA; ++i) kn[i] = 0;
-    constexpr int NPF = MODE == MODE_BLOCK ? 1 : (MODE == MODE_COLUMN ? NDMA : 0);  // loads per prefetch
-    auto prefetch_src = [&](int u) __attribute__((always_inline)) {
+    // Source of a tile to fetch, loaded one step before its DMA so that no
+    // index load sits between a barrier and the DMA it feeds: the kept block
+    // (block form) or this lane's key per DMA row (column form).
+    struct Src {
+        int j;
+        int kn[NDMA];
+    };
+    constexpr int NPF = MODE == MODE_BLOCK ? 1 : (MODE == MODE_COLUMN ? NDMA : 0);  // loads per source
+    auto load_src = [&](Src& sr, int u) __attribute__((always_inline)) {
         if constexpr (MODE == MODE_BLOCK) {
-            jn = block_of(u);
+            sr.j = block_of(u);
         } else if constexpr (MODE == MODE_COLUMN) {
 #pragma unroll
-            for (int i = 0; i < NDMA; ++i) kn[i] = cb[min(u * KT + dr0 + i * ROWS_PER_DMA, p.kcol - 1)];
+            for (int i = 0; i < NDMA; ++i) sr.kn[i] = cb[min(u * KT + dr0 + i * ROWS_PER_DMA, p.kcol - 1)];
         }
     };
-    // DMA of tile u into `stage` from the prefetched source
-    auto dma_tile = [&](char* stage, int u) __attribute__((always_inline)) {
+    auto init_src = [&](Src& sr) __attribute__((always_inline)) {
+        sr.j = 0;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i) sr.kn[i] = 0;
+    };
+    // DMA of the K rows (V = false) or V rows (V = true) of tile u into
+    // `stage`, from its source
+    auto dma_rows = [&](char* stage, int u, const Src& sr, auto is_v) __attribute__((always_inline)) {
         const bool live = u < n_tiles;
-        const int key0 = tile_key0(u, jn);
+        const int key0 = tile_key0(u, sr.j);
         const int nv = tile_valid(key0);
 #pragma unroll
         for (int i = 0; i < NDMA; ++i) {
-            LDS_AS char* kdst = (LDS_AS char*)(stage) + (i * T + wave * 64) * 16;
-            LDS_AS char* vdst = kdst + TILEB;
+            LDS_AS char* dst = (LDS_AS char*)(stage) + (is_v.value ? TILEB : 0) + (i * T + wave * 64) * 16;
             uint32_t base;
             if constexpr (MODE == MODE_COLUMN)
-                base = (live && dr0 + i * ROWS_PER_DMA < nv) ? static_cast<uint32_t>(kn[i]) * ROWB : kOOB;
+                base = (live && dr0 + i * ROWS_PER_DMA < nv) ? static_cast<uint32_t>(sr.kn[i]) * ROWB : kOOB;
             else
                 base = live ? static_cast<uint32_t>(key0) * ROWB : kOOB;
-            dma_load16(rk, lds_addr(kdst), base + kslot[i]);
-            dma_load16(rv, lds_addr(vdst), base + vslot[i]);
+            if constexpr (is_v.value)
+                dma_load16(rv, lds_addr(dst), base + vslot[i]);
+            else
+                dma_load16(rk, lds_addr(dst), base + kslot[i]);
         }
+    };
+    Src sn;  // source of the next tile (one-stage-ring passes)
+    init_src(sn);
+    auto prefetch_src = [&](int u) __attribute__((always_inline)) { load_src(sn, u); };
+    auto dma_tile = [&](char* stage, int u) __attribute__((always_inline)) {
+        dma_rows(stage, u, sn, std::false_type{});
+        dma_rows(stage, u, sn, std::true_type{});
     };
 
     // ---- Q operand (registers, whole kernel) -------------------------------
@@ -317,6 +331,20 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             pair[r >> 1] = p0 + p1;
         }
         return ((pair[0] + pair[1]) + (pair[2] + pair[3])) + ((pair[4] + pair[5]) + (pair[6] + pair[7]));
+    };
+    // half H of a 32-key block (accumulator rows 8H .. 8H+7, pk[4H .. 4H+3]);
+    // returns their fp32 sum in this lane
+    auto exps_half = [&](const f32x16& s, auto H, float mcu, uint32_t (&pk)[8]) __attribute__((always_inline)) -> float {
+        float pair[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 8 * H.value + 2 * j;
+            const float p0 = exp2_fast(fmaf(s[r], c, -mcu));
+            const float p1 = exp2_fast(fmaf(s[r + 1], c, -mcu));
+            pk[4 * H.value + j] = pack_bf16x2(p0, p1);
+            pair[j] = p0 + p1;
+        }
+        return (pair[0] + pair[1]) + (pair[2] + pair[3]);
     };
     // raise the reference to this block's maximum, rescale O and l, redo P
     auto rebase = [&](const f32x16& s, uint32_t (&pk)[8]) __attribute__((always_inline)) -> float {
@@ -465,10 +493,127 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         // DMA past the last tile (zeros) and the last prefetch
         __builtin_amdgcn_s_waitcnt(0);
     };
+    // Unchecked pass over 64-key tiles, software-pipelined in units: unit t is
+    // PV of block 0 of tile t, QK of both blocks of tile t+1, PV of block 1 of
+    // tile t, with the softmax of block 1 of tile t and of block 0 of tile
+    // t+1 spread over those four MFMA groups.  K and V each use two stages:
+    // at unit t's barrier every wave is done with K(t) and V(t-1), so V(t+1)
+    // and K(t+2) are fetched into their places.  Tile 0 is computed before
+    // the first unit and sets the reference to its maximum.
+    auto run_pass_piped = [&]() __attribute__((always_inline)) {
+        const int n = n_tiles;
+        Src sv, sk;  // sources of the next V and K fetches
+        init_src(sv);
+        init_src(sk);
+        load_src(sk, 0);
+        dma_rows(smem, 0, sk, std::false_type{});
+        dma_rows(smem, 0, sk, std::true_type{});
+        load_src(sk, 1);
+        dma_rows(smem + STAGEB, 1, sk, std::false_type{});
+        load_src(sv, 1);
+        load_src(sk, 2);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        f32x16 s0, s1;
+        uint32_t pk0[8], pk1[8];
+        qk(smem, 0, s0);
+        qk(smem, 1, s1);
+        if (n_full == 0) {
+            int J = 0;
+            if constexpr (MODE == MODE_BLOCK) J = block_of(0);
+            const int nv0 = tile_valid(tile_key0(0, J));
+            mask(0, nv0, s0);
+            mask(1, nv0, s1);
+        }
+        {
+            float mt = -kInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, fmaxf(s0[r], s1[r]));
+            m_ref = max_with_half_swap(mt);
+            mc = m_ref * c;
+        }
+        l_acc += exps_half(s0, std::integral_constant<int, 0>{}, mc, pk0) +
+                 exps_half(s0, std::integral_constant<int, 1>{}, mc, pk0);
+        // kind: 0 = tile t+1 full; 1 = any (tile t+1 masked to its real keys,
+        // none past the last tile, where its K rows are zeros)
+        auto unit = [&](int t, auto par, auto kind) __attribute__((always_inline)) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            char* st_t = smem + par * STAGEB;
+            char* st_n = smem + (1 - par) * STAGEB;
+            int nvn = KT;
+            if constexpr (kind.value == 1) nvn = t + 1 < n ? tile_valid(tile_key0(t + 1, sv.j)) : 0;
+            dma_rows(st_n, t + 1, sv, std::true_type{});   // V(t+1)
+            dma_rows(st_t, t + 2, sk, std::false_type{});  // K(t+2)
+            load_src(sv, t + 2);
+            load_src(sk, t + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr std::integral_constant<int, 0> lo{};
+            constexpr std::integral_constant<int, 1> hi{};
+            // Each MFMA group is scheduled with a quarter of the softmax work
+            // in a region of its own (sched_barrier), which keeps the live
+            // ranges in program order.
+            auto fence = [&](auto is_pv) __attribute__((always_inline)) {
+                if constexpr (kind.value == 0) {
+                    __builtin_amdgcn_sched_group_barrier(SG_DSR, 4, 0);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                        if (is_pv.value && i < 6) __builtin_amdgcn_sched_group_barrier(SG_DSR, 2, 0);
+                        if (!is_pv.value && i < 4) __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+                        if (i & 1)
+                            __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+                        else
+                            __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            pv(st_t, 0, pk0);                                // P0(t)
+            const float ta = exps_half(s1, lo, mc, pk1);     // S1a(t)
+            fence(std::true_type{});
+            {
+                f32x16 n0, n1;
+                uint32_t q0[8];
+                qk(st_n, 0, n0);                             // Q0(t+1)
+                const float tb = exps_half(s1, hi, mc, pk1); // S1b(t)
+                fence(std::false_type{});
+                if constexpr (kind.value == 1) mask(0, nvn, n0);
+                qk(st_n, 1, n1);                             // Q1(t+1)
+                if constexpr (kind.value == 1) mask(1, nvn, n1);
+                const float ua = exps_half(n0, lo, mc, q0);  // S0a(t+1)
+                fence(std::false_type{});
+                pv(st_t, 1, pk1);                            // P1(t)
+                const float ub = exps_half(n0, hi, mc, q0);  // S0b(t+1)
+                fence(std::true_type{});
+                l_acc += (ta + tb) + (ua + ub);
+                s1 = n1;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pk0[i] = q0[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        int t = 0;
+        // units whose next tile is full, in pairs so the stage parity is a constant
+        for (; t + 3 <= n_full; t += 2) {
+            unit(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
+            unit(t + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+        }
+        // the rest (at most four units), t even on entry
+        for (; t < n; t += 2) {
+            unit(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+            if (t + 1 < n) unit(t + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+    };
     // Unchecked pass: probabilities relative to tile 0's maximum are not
     // bounded, so a lane whose row sum leaves [0, 2^32] (including inf and
     // NaN) sends the whole workgroup through a second, checked pass.
-    run_pass(std::false_type{});
+    if constexpr (KB == 2) {
+        if (n_tiles > 0) run_pass_piped();
+    } else {
+        run_pass(std::false_type{});
+    }
     if (__syncthreads_or(!(l_acc <= kBigRow))) {
         m_ref = -kInf;
         mc = -kInf;
