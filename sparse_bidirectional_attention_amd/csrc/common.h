@@ -119,4 +119,57 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* to
     return res;
 }
 
+
+// ---- LDS and buffer-to-LDS DMA helpers ----------------------------------
+
+// Raw buffer descriptor word 3 for gfx9-family parts: 32-bit data format,
+// offsets checked against num_records (loads past it return zero).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// A buffer offset at or beyond every valid one (tile past the end): the
+// range check returns zeros.  Valid offsets stay below it while L * 2d bytes
+// fit in kOOB.
+constexpr uint32_t kOOB = 0xFFFF0000u;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// 8-byte transposing LDS read: in each group of 16 lanes, lane 4s+e receives
+// element e of the 8-byte chunks addressed by lanes s, s+4, s+8, s+12.
+__device__ __forceinline__ s16x4 lds_read_tr(const char* base, int off) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (LDS_AS s16x4*)((LDS_AS char*)(base) + off));
+}
+
+// 32-bit LDS address of a shared-memory pointer, as a wave-uniform value
+__device__ __forceinline__ uint32_t lds_addr(LDS_AS char* ptr) {
+    return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ptr)));
+}
+
+// 16-byte buffer load of every lane into LDS at lds + 16 * lane (the
+// buffer-to-LDS DMA; offsets at or past the range read as zero).  Issued
+// through asm because the compiler, unable to tell which stage a DMA writes,
+// would otherwise wait for it before every later LDS read; the kernel orders
+// DMA and LDS reads itself (memory-count wait and barrier once per tile).
+__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voffset), "s"(rsrc));
+}
+
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 0x3) << 14));
+}
+
 }  // namespace sdattn

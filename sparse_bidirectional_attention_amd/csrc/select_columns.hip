@@ -4,11 +4,12 @@
 //
 //   colsum kernels  partial[b, h, j] = sum_i exp(scale q_i.k_j - lse_i) over
 //                   all query rows of one query head h: bf16 inputs use
-//                   v_mfma_f32_32x32x16_bf16 for S^T = K Q^T with the 32-key
-//                   K operand kept in registers and Q streamed through
-//                   registers; exponentials in fp32, accumulated per lane
-//                   in fp32 over 16 query tiles, then in fp64.  fp32 inputs
-//                   use exact fp32 FMAs and expf with fp64 accumulation.
+//                   v_mfma_f32_32x32x16_bf16 for S^T = K Q^T with each
+//                   wave's 32-key K operand kept in registers and Q tiles
+//                   streamed through LDS for all waves of a workgroup;
+//                   exponentials in fp32, accumulated per lane in fp32 over
+//                   512 queries, then in fp64.  fp32 inputs use exact fp32
+//                   FMAs and expf with fp64 accumulation.
 //   reduce kernel   C[b, g, j] = sum over the heads of group g, fp64, in a
 //                   fixed order (deterministic, no atomics).
 //   topk kernel     per (b, g): the kcol-th largest C by an 8-pass radix
@@ -33,21 +34,42 @@ struct ColParams {
     float scale;
 };
 
-// bf16: 4 waves x 32 keys = 128 keys per workgroup; all L queries of one head.
+// bf16: 8 waves x 32 keys = 256 keys per workgroup, K in registers.  All L
+// queries of the head stream through LDS in 64-query tiles (buffer-to-LDS
+// DMA, CS_NST stages), shared by the 8 waves; each wave takes S^T = K Q^T for
+// its 32 keys and both 32-query halves of a tile.  exp2(s c - lse log2 e) in
+// fp32, accumulated per lane in fp32 over 8 tiles (512 queries), then in
+// fp64.  Queries past L have lse = +inf and add zero.
+constexpr int CS_NW = 8;
+constexpr int CS_QT = 64;
+constexpr int CS_NST = 3;
+
 template <int D>
-__global__ __launch_bounds__(256) void colsum_bf16_kernel(ColParams p) {
+__global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
     constexpr int DK = D / 16;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int T = CS_NW * 64;
+    constexpr int ROWB = D * 2;
+    constexpr int TILEB = CS_QT * ROWB;
+    constexpr int UNITS = D / 8;
+    constexpr int NDMA = CS_QT * UNITS / T;      // 16-byte DMA chunks per thread per tile
+    constexpr int ROWS_PER_DMA = T / UNITS;
+    static_assert(NDMA * T == CS_QT * UNITS, "DMA tiling");
+    __shared__ __attribute__((aligned(16))) char smem[CS_NST * TILEB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hl = lane >> 5;
     const int kt = blockIdx.x % p.n_ktiles;
     const int bh = blockIdx.x / p.n_ktiles;
     const int h = bh % p.Hq, b = bh / p.Hq;
     const int g = h / p.group;
     const int L = p.L;
-    const int key0 = kt * 128 + wave * 32;
+    const int key0 = kt * (CS_NW * 32) + wave * 32;
     const uint16_t* kh = static_cast<const uint16_t*>(p.k) + (static_cast<size_t>(b) * p.Hkv + g) * L * D;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + static_cast<size_t>(bh) * L * D;
     const float* lh = p.lse + static_cast<size_t>(bh) * L;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qh), 0,
+                                                                        static_cast<uint32_t>(L) * ROWB, kRsrcWord3);
 
     bf16x8 kreg[DK];
     {
@@ -56,6 +78,29 @@ __global__ __launch_bounds__(256) void colsum_bf16_kernel(ColParams p) {
         for (int st = 0; st < DK; ++st)
             kreg[st] = *reinterpret_cast<const bf16x8*>(kh + static_cast<size_t>(kr) * D + 16 * st + 8 * hl);
     }
+    // Q tile in LDS: row r, 16-byte unit u stored at unit u ^ (r mod UNITS);
+    // each DMA lane fetches the chunk that belongs at its slot.
+    const uint32_t smem_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((LDS_AS char*)smem));
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int dr0 = tid / UNITS, dpu = tid % UNITS;
+    int qslot[NDMA];
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+        const int row = dr0 + i * ROWS_PER_DMA;
+        qslot[i] = row * ROWB + ((dpu ^ (row & (UNITS - 1))) << 4);
+    }
+    const int n_qt = (L + CS_QT - 1) / CS_QT;
+    auto dma_tile = [&](int qt, int stage) __attribute__((always_inline)) {
+        const uint32_t base = qt < n_qt ? static_cast<uint32_t>(qt) * TILEB : kOOB;
+#pragma unroll
+        for (int i = 0; i < NDMA; ++i)
+            dma_load16(rq, smem_lds + stage * TILEB + (i * T + wave_u * 64) * 16, base + qslot[i]);
+    };
+    // B operand (query row l32 of half qb, unit 2 st + hl)
+    int qoff[DK];
+#pragma unroll
+    for (int st = 0; st < DK; ++st) qoff[st] = l32 * ROWB + (((2 * st + hl) ^ (l32 & (UNITS - 1))) << 4);
+
     double dacc[16];
     float facc[16];
 #pragma unroll
@@ -63,30 +108,84 @@ __global__ __launch_bounds__(256) void colsum_bf16_kernel(ColParams p) {
         dacc[r] = 0.0;
         facc[r] = 0.f;
     }
-    const int n_qt = (L + 31) / 32;
-    for (int qt = 0; qt < n_qt; ++qt) {
-        const int qi = qt * 32 + l32;
-        const int qr = min(qi, L - 1);
-        bf16x8 qb[DK];
+    auto lse_of = [&](int qi) __attribute__((always_inline)) -> float { return qi < L ? lh[qi] * kLog2e : kInf; };
 #pragma unroll
-        for (int st = 0; st < DK; ++st)
-            qb[st] = *reinterpret_cast<const bf16x8*>(qh + static_cast<size_t>(qr) * D + 16 * st + 8 * hl);
-        const float lsel = qi < L ? lh[qi] * kLog2e : kInf;
-        f32x16 acc;
+    for (int s0 = 0; s0 < CS_NST - 1; ++s0) dma_tile(s0, s0);
+    // Software pipeline: the exponentials of one 32-query half run beside
+    // the MFMAs of the next half (the second half's across the barrier: they
+    // touch no LDS).
+    f32x16 a1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int r = 0; r < 16; ++r) a1[r] = 0.f;
+    float lb = kInf;  // lse of the pending half (none yet: adds exp2(-inf) = 0)
+    float ls0 = lse_of(l32), ls1 = lse_of(32 + l32);
+    auto accumulate = [&](const f32x16& a, float l) __attribute__((always_inline)) {
 #pragma unroll
-        for (int st = 0; st < DK; ++st) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[st], qb[st], acc, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) facc[r] += exp2_fast(fmaf(a[r], p.c, -l));
+    };
+    auto tile = [&](int qt, int stage) __attribute__((always_inline)) {
+        wait_vmcnt<(CS_NST - 2) * NDMA>();
+        __syncthreads();
+        dma_tile(qt + CS_NST - 1, (stage + CS_NST - 1) % CS_NST);
+        const float la = ls0, lnext = ls1;
+        ls0 = lse_of((qt + 1) * CS_QT + l32);
+        ls1 = lse_of((qt + 1) * CS_QT + 32 + l32);
+        __builtin_amdgcn_sched_barrier(0);
+        const char* stg = smem + stage * TILEB;
+        f32x16 a0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) facc[r] += exp2_fast(fmaf(acc[r], p.c, -lsel));
-        if ((qt & 15) == 15) {
+        for (int r = 0; r < 16; ++r) a0[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < DK; ++st) {
+            const bf16x8 q0 = *reinterpret_cast<const bf16x8*>(stg + qoff[st]);
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[st], q0, a0, 0, 0, 0);
+        }
+        accumulate(a1, lb);  // the previous tile's second half
+        if constexpr (DK == 8) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a1[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < DK; ++st) {
+            const bf16x8 q1 = *reinterpret_cast<const bf16x8*>(stg + qoff[st] + 32 * ROWB);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[st], q1, a1, 0, 0, 0);
+        }
+        accumulate(a0, la);
+        lb = lnext;
+        if constexpr (DK == 8) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if ((qt & 7) == 7) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 dacc[r] += static_cast<double>(facc[r]);
                 facc[r] = 0.f;
             }
         }
+    };
+    int qt = 0;
+    for (; qt + CS_NST <= n_qt; qt += CS_NST) {
+#pragma unroll
+        for (int s = 0; s < CS_NST; ++s) tile(qt + s, s);
     }
+    for (; qt < n_qt; ++qt) tile(qt, qt % CS_NST);
+    accumulate(a1, lb);
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         double x = dacc[r] + static_cast<double>(facc[r]);
@@ -241,10 +340,10 @@ hipError_t launch_select_columns(const AttnShape& s, bool bf16, const void* q, c
     const size_t a = static_cast<size_t>(s.B) * s.Hq * s.L * 8;
     double* Cbuf = reinterpret_cast<double*>(static_cast<char*>(ws) + ((a + 255) & ~static_cast<size_t>(255)));
     if (bf16) {
-        cp.n_ktiles = (s.L + 127) / 128;
+        cp.n_ktiles = (s.L + CS_NW * 32 - 1) / (CS_NW * 32);
         const dim3 grid(s.B * s.Hq * cp.n_ktiles);
-        if (s.D == 128) hipLaunchKernelGGL(colsum_bf16_kernel<128>, grid, dim3(256), 0, st, cp);
-        else hipLaunchKernelGGL(colsum_bf16_kernel<64>, grid, dim3(256), 0, st, cp);
+        if (s.D == 128) hipLaunchKernelGGL(colsum_bf16_kernel<128>, grid, dim3(CS_NW * 64), 0, st, cp);
+        else hipLaunchKernelGGL(colsum_bf16_kernel<64>, grid, dim3(CS_NW * 64), 0, st, cp);
     } else {
         cp.n_ktiles = (s.L + 255) / 256;
         const dim3 grid(s.B * s.Hq * cp.n_ktiles);
