@@ -73,11 +73,12 @@ def to_dev(x):
 
 
 def kernel_source_hash():
+    """Hash of the sources the flash-forward kernel is built from (the
+    kernel whose counters the traffic files hold)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_bidirectional_attention_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in ("flash_bf16.hip", "common.h", "launch.h"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
