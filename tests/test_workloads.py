@@ -46,3 +46,29 @@ def test_columns_pattern_plants_shared_stripes():
     # a stripe key has a much larger norm than a plain N(0,1) key of d=128 ... on average over stripes
     norms = np.linalg.norm(x["k"][0, 0], axis=-1)
     assert (norms > np.sqrt(128) + 1.5).sum() >= 8
+
+
+def test_planting_follows_the_kv_groups():
+    """Every pattern builds on a GQA shape with a ragged length, and the query heads of one
+    kv group receive the same planted shift (the shift of their kv head's pattern)."""
+    for name, extra in (("sparsed_64k", 0.02), ("pulsecol_dream7b_16k", 0.0)):
+        w = scaled(WORKLOADS[name], seq_len=1000, q_heads=8, kv_heads=2, extra_pair_frac=extra,
+                   n_stripe_columns=16)
+        planted = make_base(w)
+        plain = make_base(scaled(w, pattern="plain", extra_pair_frac=0.0))
+        np.testing.assert_array_equal(planted["v"], plain["v"])
+        dq = planted["q"] - plain["q"]
+        assert np.linalg.norm(planted["k"] - plain["k"], axis=-1).max() > 1.0
+        for g in range(2):
+            grp = dq[:, 4 * g:4 * (g + 1)]
+            assert np.linalg.norm(grp, axis=-1).max() > 1.0
+            # (q + shift) - q is the shift up to fp32 rounding of the sum
+            np.testing.assert_allclose(grp, np.broadcast_to(grp[:, :1], grp.shape), rtol=0, atol=1e-5)
+        assert not np.array_equal(dq[:, 0], dq[:, 4])
+    # the smoke test's shape: four query heads over two kv heads, three steps after the base
+    w = scaled(WORKLOADS["sparsed_64k"], seq_len=1000, q_heads=4, kv_heads=2, total_steps=4, dense_steps=1,
+               select_step=1, keep_frac=0.25)
+    base = make_base(w)
+    for t in range(w.total_steps):
+        x = make_step(w, t, base)
+        assert x["q"].shape == (1, 4, 1000, 128) and x["k"].shape == (1, 2, 1000, 128)

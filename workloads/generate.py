@@ -56,16 +56,22 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 
 
 def _plant_mix(w: Workload, q, k):
-    """Round-robin head types sink / local / stripes / none (in place, fp32)."""
-    B, H, L, d = q.shape
+    """Round-robin head types sink / local / stripes / none (in place, fp32).
+
+    The type is chosen per kv head; the key planting goes to that kv head and the query
+    planting to every query head of its group (one head per group without GQA)."""
+    B, Hq, L, d = q.shape
+    H = k.shape[1]
+    G = Hq // H
     n_units = -(-L // UNIT)
     for h in range(H):
         kind = h % 4
         r = _rng(w.wid, 100, h)
+        qs = slice(h * G, (h + 1) * G)
         if kind == 0:  # sink
             u = _unit(r, d)
             k[:, h, :min(UNIT, L)] += 3.0 * u
-            q[:, h] += 3.0 * u
+            q[:, qs] += 3.0 * u
         elif kind == 1:  # local band of +-2 units
             e = np.stack([_unit(r, d) for _ in range(n_units)])
             band = np.zeros_like(e)
@@ -74,19 +80,22 @@ def _plant_mix(w: Workload, q, k):
                 s = e[lo:hi].sum(axis=0)
                 band[c] = s / np.linalg.norm(s)
             tok_unit = np.arange(L) // UNIT
-            q[:, h] += 3.0 * e[tok_unit]
+            q[:, qs] += 3.0 * e[tok_unit]
             k[:, h] += 3.0 * band[tok_unit]
         elif kind == 2:  # vertical stripes: 4 random 64-token units
             u = _unit(r, d)
             units = r.choice(n_units, size=min(4, n_units), replace=False)
             for c in units:
                 k[:, h, c * UNIT:min(L, (c + 1) * UNIT)] += 3.0 * u
-            q[:, h] += 3.0 * u
+            q[:, qs] += 3.0 * u
 
 
 def _plant_pairs(w: Workload, q, k):
-    """Extra alignment on a random fraction of (I, J) block pairs per head."""
-    B, H, L, d = q.shape
+    """Extra alignment on a random fraction of (I, J) block pairs per kv head (its query
+    group shares the pairs)."""
+    B, Hq, L, d = q.shape
+    H = k.shape[1]
+    G = Hq // H
     nb = -(-L // w.block)
     n_pairs = int(round(w.extra_pair_frac * nb * nb))
     if n_pairs == 0:
@@ -101,7 +110,7 @@ def _plant_pairs(w: Workload, q, k):
         np.add.at(qadd, flat // nb, 2.0 * wv)
         np.add.at(kadd, flat % nb, 2.0 * wv)
         tok_blk = np.arange(L) // w.block
-        q[:, h] += qadd[tok_blk]
+        q[:, h * G:(h + 1) * G] += qadd[tok_blk][None, None]
         k[:, h] += kadd[tok_blk]
 
 
