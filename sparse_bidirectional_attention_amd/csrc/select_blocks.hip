@@ -271,19 +271,37 @@ __global__ __launch_bounds__(256) void radix_hist_kernel(const float* __restrict
         if (lh[i]) atomicAdd(&hist[pass * kHistBins + i], lh[i]);
 }
 
-__global__ void radix_find_kernel(const uint32_t* hist, int pass, SelState* st) {
-    if (threadIdx.x != 0) return;
+// The bin of this pass's digit that holds the remaining rank: a workgroup
+// prefix sum over the histogram (two bins per thread, 64-bit counts); the one
+// thread whose bins span the rank appends the digit and keeps the rank left
+// inside the bin.  A rank past the total leaves the state unchanged.
+__global__ __launch_bounds__(kHistBins / 2) void radix_find_kernel(const uint32_t* hist, int pass, SelState* st) {
+    __shared__ long long wsum[kHistBins / 2 / 64];
     int shift, width;
     pass_bits(pass, shift, width);
-    long long rank = st->rank;
+    const int nb = 1 << width;
     const uint32_t* hh = hist + pass * kHistBins;
-    for (int bin = 0; bin < (1 << width); ++bin) {
-        if (rank < static_cast<long long>(hh[bin])) {
-            st->prefix |= static_cast<uint32_t>(bin) << shift;
-            st->rank = rank;
-            return;
-        }
-        rank -= hh[bin];
+    const long long rank = st->rank;  // read by every thread before the one write below
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int b0 = 2 * t;
+    const long long h0 = b0 < nb ? hh[b0] : 0;
+    const long long h1 = b0 + 1 < nb ? hh[b0 + 1] : 0;
+    long long x = h0 + h1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    long long base = 0;
+    for (int i = 0; i < w; ++i) base += wsum[i];
+    const long long incl = base + x;        // bins 0 .. b0+1
+    const long long ex = incl - (h0 + h1);  // bins 0 .. b0-1
+    if (rank >= ex && rank < incl) {
+        const bool first = rank < ex + h0;
+        st->prefix |= static_cast<uint32_t>(first ? b0 : b0 + 1) << shift;
+        st->rank = rank - (first ? ex : ex + h0);
     }
 }
 
@@ -439,7 +457,7 @@ hipError_t launch_select_blocks(const AttnShape& s, bool bf16, const void* q, co
         const unsigned hg = static_cast<unsigned>(std::min<long long>(1024, (nvals + 255) / 256));
         for (int pass = 0; pass < 3; ++pass) {
             hipLaunchKernelGGL(radix_hist_kernel, dim3(hg), dim3(256), 0, st, sp.cum, nvals, pass, hist, sst);
-            hipLaunchKernelGGL(radix_find_kernel, dim3(1), dim3(64), 0, st, hist, pass, sst);
+            hipLaunchKernelGGL(radix_find_kernel, dim3(1), dim3(kHistBins / 2), 0, st, hist, pass, sst);
         }
     }
     hipLaunchKernelGGL(mass_count_kernel, dim3(static_cast<unsigned>((rows * 64 + 255) / 256)), dim3(256), 0, st,
