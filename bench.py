@@ -306,23 +306,31 @@ def main():
 
     ms_per_step = total_ms / K
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    sparse_tflops = kept_flops / (sparse_ms * 1e9) if sparse_ms else None
-    dense_tflops = dense_flops / (dense_base_ms * 1e9)
+    # Roofline figures use each kernel's average launch inside the timed region:
+    # a SPARSE step is one sparse forward, a DENSE step one dense forward.
+    def mean(a):
+        return float(np.mean(a)) if len(a) else None
+
+    sparse_launch_ms = mean(step_ms[idx["SPARSE"]]) if idx.get("SPARSE") else sparse_ms
+    dense_launch_ms = mean(step_ms[idx["DENSE"]]) if idx.get("DENSE") else dense_base_ms
+    sparse_tflops = kept_flops / (sparse_launch_ms * 1e9) if sparse_launch_ms else None
+    dense_tflops = dense_flops / (dense_launch_ms * 1e9)
+    dense_base_tflops = dense_flops / (dense_base_ms * 1e9)
     # kernel with the largest share of the timed region
     n_sparse = len(idx.get("SPARSE", [])) + len(idx.get("SELECT_SPARSE", []))
     n_dense = len(idx.get("DENSE", [])) + len(idx.get("DENSE_SELECT", []))
-    share_sparse = n_sparse * (sparse_ms or 0)
-    share_dense = n_dense * dense_base_ms
+    share_sparse = n_sparse * (sparse_launch_ms or 0)
+    share_dense = n_dense * dense_launch_ms
     kernels = {
         "flash_fwd_bf16_sparse" if w.selector == "blocks" else "flash_fwd_bf16_column": {
             "bound": "mfma", "achieved": round(sparse_tflops, 1) if sparse_tflops else None, "peak": peak,
             "unit": "TFLOP/s", "frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
-            "launch_ms": round(sparse_ms, 4) if sparse_ms else None,
+            "launch_ms": round(sparse_launch_ms, 4) if sparse_launch_ms else None,
             "flops_per_launch": kept_flops,
             "traffic": load_traffic("flash_sparse", w0.name)},
         "flash_fwd_bf16_dense": {
             "bound": "mfma", "achieved": round(dense_tflops, 1), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(dense_tflops / peak, 4), "launch_ms": round(dense_base_ms, 3),
+            "frac": round(dense_tflops / peak, 4), "launch_ms": round(dense_launch_ms, 3),
             "flops_per_launch": dense_flops, "traffic": load_traffic("flash_dense", w0.name)},
     }
     dom = max(kernels, key=lambda k: share_sparse if "dense" not in k else share_dense)
@@ -355,8 +363,8 @@ def main():
                    "sparse_effective_tflops": round(sparse_tflops, 1) if sparse_tflops else None,
                    "sparse_mfma_frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
                    "kept_density": round(density, 5), "kept_nnz": nnz},
-        "dense_baseline": {"ms_per_step": round(dense_base_ms, 3), "tflops": round(dense_tflops, 1),
-                           "mfma_frac": round(dense_tflops / peak, 4),
+        "dense_baseline": {"ms_per_step": round(dense_base_ms, 3), "tflops": round(dense_base_tflops, 1),
+                           "mfma_frac": round(dense_base_tflops / peak, 4),
                            "schedule_speedup": round(dense_base_ms / ms_per_step, 3),
                            "sparse_step_speedup": round(dense_base_ms / sparse_ms, 3) if sparse_ms else None},
         "kernels": kernels,
