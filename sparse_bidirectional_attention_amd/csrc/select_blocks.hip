@@ -7,8 +7,9 @@
 //                      coalesced loads (HBM-bound).
 //   scores_kernel      per group of 8 query blocks of one head: pooled
 //                      scores against every key block (each Kp row is read
-//                      once per group), softmax over J, a bitonic sort on
-//                      the key (mass desc, J asc) in LDS, then
+//                      once per group); then one wave per row: softmax over
+//                      J, a bitonic sort on the key (mass desc, J asc) held
+//                      in registers (shuffles across lanes), then
 //                        top-k: kept flags -> ascending CSR row, or
 //                        mass:  the row's cumulative mass array and order.
 //   radix select       mass budget with a global cap: the (N+1)-th smallest
@@ -86,16 +87,33 @@ struct ScoreParams {
     int32_t* ord;       // [rows][nkb] (mass)
 };
 
-template <int D>
+// 64-bit shuffle (two 32-bit halves)
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), m, 64);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), m, 64);
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_inclusive_scan_f(float x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// R: sort keys per lane (the row's 64 R >= nKB sort slots; element i = 64 k + lane)
+template <int D, int R>
 __global__ __launch_bounds__(kSelThreads) void scores_kernel(ScoreParams p) {
     constexpr int NT = kSelThreads;
+    constexpr int NS = 64 * R;  // sorted length (padding keys are 0, below every real key)
     __shared__ float qs[kRowsPerGroup][D];
     __shared__ float sc[kRowsPerGroup][kMaxKeyBlocks];
-    __shared__ uint64_t keys[kMaxKeyBlocks];
-    __shared__ int scan_tmp[NT / 64 + 1];
-    __shared__ float red[NT / 64];
 
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const int groups_per_head = (p.nqb + kRowsPerGroup - 1) / kRowsPerGroup;
     const int bh = blockIdx.x / groups_per_head;
     const int I0 = (blockIdx.x % groups_per_head) * kRowsPerGroup;
@@ -104,6 +122,7 @@ __global__ __launch_bounds__(kSelThreads) void scores_kernel(ScoreParams p) {
     const int g = h / p.group;
     const int nkb = p.nkb;
 
+    // pooled scores of the group's rows against every key block (each Kp row read once)
     for (int e = tid; e < nrows * D; e += NT) qs[e / D][e % D] = p.qp[(static_cast<size_t>(bh) * p.nqb + I0) * D + e];
     __syncthreads();
     const float* kp = p.kp + (static_cast<size_t>(b) * p.Hkv + g) * nkb * D;
@@ -128,105 +147,119 @@ __global__ __launch_bounds__(kSelThreads) void scores_kernel(ScoreParams p) {
     }
     __syncthreads();
 
-    for (int rr = 0; rr < nrows; ++rr) {
+    // one wave per row from here on: no workgroup barriers
+    for (int rr = tid >> 6; rr < nrows; rr += NT / 64) {
         const int row = bh * p.nqb + I0 + rr;
         // softmax over J
+        float v[R];
         float mx = -kInf;
-        for (int J = tid; J < nkb; J += NT) mx = fmaxf(mx, sc[rr][J]);
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int J = 64 * k + lane;
+            v[k] = J < nkb ? sc[rr][J] : -kInf;
+            mx = fmaxf(mx, v[k]);
+        }
         mx = wave_max(mx);
-        if ((tid & 63) == 0) red[tid >> 6] = mx;
-        __syncthreads();
-        mx = red[0];
-        for (int w = 1; w < NT / 64; ++w) mx = fmaxf(mx, red[w]);
-        __syncthreads();
         float sm = 0.f;
-        for (int J = tid; J < nkb; J += NT) {
-            const float e = expf(sc[rr][J] - mx);
-            sc[rr][J] = e;
-            sm += e;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int J = 64 * k + lane;
+            v[k] = J < nkb ? expf(v[k] - mx) : 0.f;
+            sm += v[k];
         }
         sm = wave_sum(sm);
-        if ((tid & 63) == 0) red[tid >> 6] = sm;
-        __syncthreads();
-        sm = 0.f;
-        for (int w = 0; w < NT / 64; ++w) sm += red[w];
         const float inv = 1.f / sm;
-        for (int J = tid; J < p.n2; J += NT) {
-            uint64_t key = 0;
+        // key = mass bits << 32 | ~J: descending order is mass desc, then J asc
+        uint64_t key[R];
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const int J = 64 * k + lane;
+            key[k] = 0;
             if (J < nkb) {
-                const float a = sc[rr][J] * inv;
+                const float a = v[k] * inv;
                 if (p.block_mass) p.block_mass[static_cast<size_t>(row) * nkb + J] = a;
-                key = (static_cast<uint64_t>(__float_as_uint(a)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(J));
+                key[k] = (static_cast<uint64_t>(__float_as_uint(a)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(J));
             }
-            keys[J] = key;
         }
-        __syncthreads();
-        // bitonic sort, descending
-        for (int size = 2; size <= p.n2; size <<= 1) {
+        // bitonic sort, descending: at each compare-exchange the lower index of
+        // a pair keeps the larger key in descending segments, the smaller in
+        // ascending ones
+#pragma unroll
+        for (int size = 2; size <= NS; size <<= 1) {
+#pragma unroll
             for (int stride = size >> 1; stride > 0; stride >>= 1) {
-                for (int i = tid; i < (p.n2 >> 1); i += NT) {
-                    const int lo = 2 * i - (i & (stride - 1));
-                    const int hi = lo + stride;
-                    const bool desc = (lo & size) == 0;
-                    const uint64_t a = keys[lo], c = keys[hi];
-                    if ((a < c) == desc) {
-                        keys[lo] = c;
-                        keys[hi] = a;
+                if (stride >= 64) {
+                    const int ks = stride >> 6;
+#pragma unroll
+                    for (int k = 0; k < R; ++k) {
+                        const int kq = k ^ ks;
+                        if (kq > k) {
+                            const bool desc = ((64 * k + lane) & size) == 0;
+                            const uint64_t lo = key[k], hi = key[kq];
+                            if ((lo < hi) == desc) {
+                                key[k] = hi;
+                                key[kq] = lo;
+                            }
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < R; ++k) {
+                        const uint64_t o = shfl_xor_u64(key[k], stride);
+                        const bool lower = (lane & stride) == 0;
+                        const bool desc = ((64 * k + lane) & size) == 0;
+                        const uint64_t mxk = key[k] > o ? key[k] : o, mnk = key[k] > o ? o : key[k];
+                        key[k] = (lower == desc) ? mxk : mnk;
                     }
                 }
-                __syncthreads();
             }
         }
         if (p.topk > 0) {
-            // kept flags in natural order, then ascending compaction
-            int* flag = reinterpret_cast<int*>(&sc[rr][0]);  // reuse the row's score storage
-            for (int J = tid; J < nkb; J += NT) flag[J] = 0;
-            __syncthreads();
-            for (int i = tid; i < p.topk; i += NT) flag[0xFFFFFFFFu - static_cast<uint32_t>(keys[i])] = 1;
-            __syncthreads();
-            int base = 0;
-            for (int J0 = 0; J0 < nkb; J0 += NT) {
-                const int J = J0 + tid;
-                const int f = J < nkb ? flag[J] : 0;
-                int tot;
-                const int pos = block_exclusive_scan<NT>(f, scan_tmp, &tot);
-                if (f) p.col_idx[static_cast<size_t>(row) * p.topk + base + pos] = J;
-                base += tot;
+            // kept flags in natural order (over the row's score storage), then an
+            // ascending compaction by wave scans
+            int* flag = reinterpret_cast<int*>(&sc[rr][0]);
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int J = 64 * k + lane;
+                if (J < nkb) flag[J] = 0;
             }
-            if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (64 * k + lane < p.topk) flag[0xFFFFFFFFu - static_cast<uint32_t>(key[k])] = 1;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            int base = 0;
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int J = 64 * k + lane;
+                const int f = J < nkb ? flag[J] : 0;
+                const int inc = wave_inclusive_scan(f);
+                if (f) p.col_idx[static_cast<size_t>(row) * p.topk + base + inc - 1] = J;
+                base += __shfl(inc, 63, 64);
+            }
+            if (lane == 0) {
                 p.row_ptr[row + 1] = (row + 1) * p.topk;
                 if (row == 0) p.row_ptr[0] = 0;
             }
         } else {
-            // cumulative mass of the sorted row (block scan over chunks)
+            // cumulative mass of the sorted row and its block order
             float carry = 0.f;
-            for (int m0 = 0; m0 < nkb; m0 += NT) {
-                const int m = m0 + tid;
-                const float a = m < nkb ? __uint_as_float(static_cast<uint32_t>(keys[m] >> 32)) : 0.f;
-                // inclusive scan of floats within the workgroup
-                float x = a;
-                const int lane = tid & 63;
 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const float y = __shfl_up(x, off, 64);
-                    if (lane >= off) x += y;
-                }
-                if (lane == 63) red[tid >> 6] = x;
-                __syncthreads();
-                float wpre = 0.f, tot = 0.f;
-                for (int w = 0; w < NT / 64; ++w) {
-                    if (w < (tid >> 6)) wpre += red[w];
-                    tot += red[w];
-                }
+            for (int k = 0; k < R; ++k) {
+                const int m = 64 * k + lane;
+                const float a = m < nkb ? __uint_as_float(static_cast<uint32_t>(key[k] >> 32)) : 0.f;
+                const float x = wave_inclusive_scan_f(a);
                 if (m < nkb) {
-                    p.cum[static_cast<size_t>(row) * nkb + m] = carry + wpre + x;
-                    p.ord[static_cast<size_t>(row) * nkb + m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(keys[m]));
+                    p.cum[static_cast<size_t>(row) * nkb + m] = carry + x;
+                    p.ord[static_cast<size_t>(row) * nkb + m] = static_cast<int32_t>(0xFFFFFFFFu - static_cast<uint32_t>(key[k]));
                 }
-                carry += tot;
-                __syncthreads();
+                carry += __shfl(x, 63, 64);
             }
         }
-        __syncthreads();
     }
 }
 
@@ -361,6 +394,12 @@ __global__ __launch_bounds__(256) void mass_write_kernel(const int32_t* __restri
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+template <int R>
+void launch_scores(int D, unsigned grid, const ScoreParams& sp, hipStream_t st) {
+    if (D == 128) hipLaunchKernelGGL((scores_kernel<128, R>), dim3(grid), dim3(kSelThreads), 0, st, sp);
+    else hipLaunchKernelGGL((scores_kernel<64, R>), dim3(grid), dim3(kSelThreads), 0, st, sp);
+}
+
 }  // namespace
 
 BlockSelectWs select_blocks_ws_layout(const AttnShape& s, int block_q, int block_k, bool mass) {
@@ -438,8 +477,14 @@ hipError_t launch_select_blocks(const AttnShape& s, bool bf16, const void* q, co
     }
     const int groups = (nqb + kRowsPerGroup - 1) / kRowsPerGroup;
     const unsigned gs = static_cast<unsigned>(s.B * s.Hq * groups);
-    if (s.D == 128) hipLaunchKernelGGL(scores_kernel<128>, dim3(gs), dim3(kSelThreads), 0, st, sp);
-    else hipLaunchKernelGGL(scores_kernel<64>, dim3(gs), dim3(kSelThreads), 0, st, sp);
+    const int R = n2 <= 64 ? 1 : n2 / 64;
+    switch (R) {
+        case 1: launch_scores<1>(s.D, gs, sp, st); break;
+        case 2: launch_scores<2>(s.D, gs, sp, st); break;
+        case 4: launch_scores<4>(s.D, gs, sp, st); break;
+        case 8: launch_scores<8>(s.D, gs, sp, st); break;
+        default: launch_scores<16>(s.D, gs, sp, st); break;
+    }
     e = hipGetLastError();
     if (e != hipSuccess || !mass) return e;
 
