@@ -105,6 +105,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // the end of the sequence (dense), the last kept block of a row (block:
     // rows are ascending) or the end of the column list can be partial.
     int n_tiles = 0, n_full = 0, e0 = 0, ne = 0, sub_shift = 0;
+    int j_first = 0;  // block form: the row's first kept block
     const int32_t* cb = nullptr;
     if constexpr (MODE == MODE_DENSE) {
         n_tiles = (L + KT - 1) / KT;
@@ -116,6 +117,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         // block_k / KT tiles per kept key block (block_k in {64, 128}, KT in {32, 64})
         sub_shift = (p.block_k == 128 ? 1 : 0) + (KT == 32 ? 1 : 0);
         if (ne > 0) {
+            // the first and the last kept block, loaded together
+            j_first = p.col_idx[e0];
             const int rem = L - p.col_idx[e0 + ne - 1] * p.block_k;  // keys of the last block in range
             const int per = 1 << sub_shift;
             n_tiles = ((ne - 1) << sub_shift) + min(per, (rem + KT - 1) / KT);
@@ -449,16 +452,27 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // t+1 spread over those four MFMA groups.  K and V each use two stages:
     // at unit t's barrier every wave is done with K(t) and V(t-1), so V(t+1)
     // and K(t+2) are fetched into their places.  Tile 0 is computed before
-    // the first unit and sets the reference to its maximum.
+    // the first unit and sets the reference to its maximum; the last tile
+    // gets a half unit (its PV and the softmax of its block 1) without the QK
+    // of a tile past the end.
     auto run_pass_piped = [&]() __attribute__((always_inline)) {
         const int n = n_tiles;
         Src sv, sk;  // sources of the next V and K fetches
         init_src(sv);
         init_src(sk);
-        load_src(sk, 0);
+        // block form: tile 0 is in the first kept block, and so is tile 1 with
+        // two tiles per block, so neither DMA waits for an index load
+        if constexpr (MODE == MODE_BLOCK)
+            sk.j = j_first;
+        else
+            load_src(sk, 0);
         dma_rows(smem, 0, sk, std::false_type{});
         dma_rows(smem, 0, sk, std::true_type{});
-        load_src(sk, 1);
+        if constexpr (MODE == MODE_BLOCK) {
+            if (sub_shift == 0) load_src(sk, 1);
+        } else {
+            load_src(sk, 1);
+        }
         dma_rows(smem + STAGEB, 1, sk, std::false_type{});
         load_src(sv, 1);
         load_src(sk, 2);
@@ -543,16 +557,56 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         };
+        // The last tile: PV of both blocks and the softmax of block 1; there is
+        // no next tile to score.
+        auto last = [&](auto par) __attribute__((always_inline)) {
+            wait_vmcnt<0>();
+            __syncthreads();
+            char* st_t = smem + par * STAGEB;
+            constexpr std::integral_constant<int, 0> lo{};
+            constexpr std::integral_constant<int, 1> hi{};
+            pv(st_t, 0, pk0);
+            const float ta = exps_half(s1, lo, mc, pk1);
+            const float tb = exps_half(s1, hi, mc, pk1);
+            __builtin_amdgcn_sched_group_barrier(SG_DSR, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (i < 6) __builtin_amdgcn_sched_group_barrier(SG_DSR, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            pv(st_t, 1, pk1);
+            l_acc += ta + tb;
+        };
+        constexpr std::integral_constant<int, 0> P0{};
+        constexpr std::integral_constant<int, 1> P1{};
+        constexpr std::integral_constant<int, 0> FULL{};
+        constexpr std::integral_constant<int, 1> ANY{};
         int t = 0;
         // units whose next tile is full, in pairs so the stage parity is a constant
         for (; t + 3 <= n_full; t += 2) {
-            unit(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
-            unit(t + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+            unit(t, P0, FULL);
+            unit(t + 1, P1, FULL);
         }
-        // the rest (at most four units), t even on entry
-        for (; t < n; t += 2) {
-            unit(t, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-            if (t + 1 < n) unit(t + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{});
+        if constexpr (MODE == MODE_DENSE) {
+            // the rest (at most four units, t even on entry); the last one scores
+            // a tile of zeros past the end, masked (one unit in a thousand)
+            for (; t < n; t += 2) {
+                unit(t, P0, ANY);
+                if (t + 1 < n) unit(t + 1, P1, ANY);
+            }
+        } else {
+            // the rest of units 0 .. n-2 (only the last tile can be partial), then
+            // the last tile's half unit: short sparse rows feel a wasted unit
+            for (; t < n - 1; t += 2) {
+                unit(t, P0, ANY);
+                if (t + 1 < n - 1) unit(t + 1, P1, ANY);
+            }
+            if ((n - 1) & 1)
+                last(P1);
+            else
+                last(P0);
         }
         __builtin_amdgcn_s_waitcnt(0);
     };
