@@ -36,10 +36,12 @@ struct ColParams {
 
 // bf16: 8 waves x 32 keys = 256 keys per workgroup, K in registers.  All L
 // queries of the head stream through LDS in 64-query tiles (buffer-to-LDS
-// DMA, CS_NST stages), shared by the 8 waves; each wave takes S^T = K Q^T for
+// DMA, CS_NST stages), shared by the 8 waves, together with the tile's 64
+// log-sum-exp values (each wave fetches 8 of them), so that every load of the
+// loop is a DMA under the loop's own wait; each wave takes S^T = K Q^T for
 // its 32 keys and both 32-query halves of a tile.  exp2(s c - lse log2 e) in
 // fp32, accumulated per lane in fp32 over 8 tiles (512 queries), then in
-// fp64.  Queries past L have lse = +inf and add zero.
+// fp64.  Queries past L are given lse = +inf and add zero.
 constexpr int CS_NW = 8;
 constexpr int CS_QT = 64;
 constexpr int CS_NST = 3;
@@ -51,10 +53,12 @@ __global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
     constexpr int ROWB = D * 2;
     constexpr int TILEB = CS_QT * ROWB;
     constexpr int UNITS = D / 8;
-    constexpr int NDMA = CS_QT * UNITS / T;      // 16-byte DMA chunks per thread per tile
+    constexpr int NDMA = CS_QT * UNITS / T;      // 16-byte DMA chunks per thread per tile (Q)
     constexpr int ROWS_PER_DMA = T / UNITS;
+    constexpr int STAGEB = TILEB + CS_QT * 4;     // Q tile, then its log-sum-exp values
     static_assert(NDMA * T == CS_QT * UNITS, "DMA tiling");
-    __shared__ __attribute__((aligned(16))) char smem[CS_NST * TILEB];
+    static_assert(CS_QT * 4 == CS_NW * 32, "each wave fetches 8 lse values (two 16-byte lanes)");
+    __shared__ __attribute__((aligned(16))) char smem[CS_NST * STAGEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -70,6 +74,8 @@ __global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
     const float* lh = p.lse + static_cast<size_t>(bh) * L;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qh), 0,
                                                                         static_cast<uint32_t>(L) * ROWB, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lh), 0,
+                                                                        static_cast<uint32_t>(L) * 4, kRsrcWord3);
 
     bf16x8 kreg[DK];
     {
@@ -94,7 +100,11 @@ __global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
         const uint32_t base = qt < n_qt ? static_cast<uint32_t>(qt) * TILEB : kOOB;
 #pragma unroll
         for (int i = 0; i < NDMA; ++i)
-            dma_load16(rq, smem_lds + stage * TILEB + (i * T + wave_u * 64) * 16, base + qslot[i]);
+            dma_load16(rq, smem_lds + stage * STAGEB + (i * T + wave_u * 64) * 16, base + qslot[i]);
+        // lse values 8 w .. 8 w + 7 of the tile (lanes 0 and 1 of wave w);
+        // past L they read as zero and are replaced by +inf when read
+        const uint32_t lbase = qt < n_qt ? static_cast<uint32_t>(qt) * (CS_QT * 4) : kOOB;
+        if (lane < 2) dma_load16(rl, smem_lds + stage * STAGEB + TILEB + wave_u * 32, lbase + wave_u * 32 + lane * 16);
     };
     // B operand (query row l32 of half qb, unit 2 st + hl)
     int qoff[DK];
@@ -108,7 +118,11 @@ __global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
         dacc[r] = 0.0;
         facc[r] = 0.f;
     }
-    auto lse_of = [&](int qi) __attribute__((always_inline)) -> float { return qi < L ? lh[qi] * kLog2e : kInf; };
+    // lse (times log2 e) of query row j of the tile in `stage`
+    auto lse_at = [&](int stage, int qt, int j) __attribute__((always_inline)) -> float {
+        const float x = *reinterpret_cast<const float*>(smem + stage * STAGEB + TILEB + 4 * j);
+        return qt * CS_QT + j < L ? x * kLog2e : kInf;
+    };
 #pragma unroll
     for (int s0 = 0; s0 < CS_NST - 1; ++s0) dma_tile(s0, s0);
     // Software pipeline: the exponentials of one 32-query half run beside
@@ -118,20 +132,17 @@ __global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) a1[r] = 0.f;
     float lb = kInf;  // lse of the pending half (none yet: adds exp2(-inf) = 0)
-    float ls0 = lse_of(l32), ls1 = lse_of(32 + l32);
     auto accumulate = [&](const f32x16& a, float l) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) facc[r] += exp2_fast(fmaf(a[r], p.c, -l));
     };
     auto tile = [&](int qt, int stage) __attribute__((always_inline)) {
-        wait_vmcnt<(CS_NST - 2) * NDMA>();
+        wait_vmcnt<(CS_NST - 2) * (NDMA + 1)>();
         __syncthreads();
         dma_tile(qt + CS_NST - 1, (stage + CS_NST - 1) % CS_NST);
-        const float la = ls0, lnext = ls1;
-        ls0 = lse_of((qt + 1) * CS_QT + l32);
-        ls1 = lse_of((qt + 1) * CS_QT + 32 + l32);
+        const float la = lse_at(stage, qt, l32), lnext = lse_at(stage, qt, 32 + l32);
         __builtin_amdgcn_sched_barrier(0);
-        const char* stg = smem + stage * TILEB;
+        const char* stg = smem + stage * STAGEB;
         f32x16 a0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) a0[r] = 0.f;
