@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     constexpr int SLOTS = KT * UNITS;       // 16-byte slots per tile
     constexpr int NDMA = SLOTS / T;         // DMA instructions per thread per tile (K; same for V)
     constexpr int ROWS_PER_DMA = T / UNITS;
-    constexpr int OPITCH = D * 2;           // epilogue staging row (one-time, conflicts tolerated)
+    constexpr int OPITCH = D * 2;           // epilogue staging row (units XOR-swizzled by row)
     constexpr int STAGEB = 2 * TILEB;       // K tile then V tile
     static_assert(NDMA * T == SLOTS && T % UNITS == 0 && ROWS_PER_DMA % 4 == 0, "DMA tiling");
     static_assert(NW * 32 * OPITCH <= NST * STAGEB, "epilogue staging fits in the stages");
@@ -633,17 +633,24 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
     const float lt = sum_with_half_swap(l_acc);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // Each wave stages its own 32 rows; 16-byte unit u of row r sits at unit
+    // u ^ (r mod UNITS), so the column-wise writes spread over the banks and
+    // the row-wise reads stay conflict-free.
     char* ob = smem + wave * 32 * OPITCH;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-            const int d0 = db * 32 + 8 * rq + 4 * hl;
+            // d = 32 db + 8 rq + 4 hl: unit 4 db + rq, half hl
+            const int pu = (4 * db + rq) ^ (l32 & (UNITS - 1));
             u32x2 w = {pack_bf16x2(oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv),
                        pack_bf16x2(oacc[db][4 * rq + 2] * inv, oacc[db][4 * rq + 3] * inv)};
-            *reinterpret_cast<u32x2*>(ob + l32 * OPITCH + d0 * 2) = w;
+            *reinterpret_cast<u32x2*>(ob + l32 * OPITCH + pu * 16 + hl * 8) = w;
         }
-    __syncthreads();
+    // only this wave reads these rows back
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const size_t obase = (static_cast<size_t>(b) * p.Hq + h) * L;
     constexpr int CHUNKS = 32 * D * 2 / 16;
 #pragma unroll
@@ -652,7 +659,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         const int row = cid / UNITS, u = cid % UNITS;
         const int qi = q0 + wave * 32 + row;
         if (qi < L) {
-            const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + u * 16);
+            const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + ((u ^ (row & (UNITS - 1))) << 4));
             *reinterpret_cast<u32x4*>(p.o + (obase + qi) * D + u * 8) = val;
         }
     }
