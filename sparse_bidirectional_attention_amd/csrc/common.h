@@ -146,12 +146,26 @@ __device__ __forceinline__ uint32_t lds_addr(LDS_AS char* ptr) {
     return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ptr)));
 }
 
+// Raw buffer descriptor for `bytes` bytes at `base` (gfx9 layout: base
+// address, stride 0, record count, kRsrcWord3).  The values are uniform; each
+// dword is passed through readfirstlane so that the descriptor is an SGPR
+// quad wherever the compiler keeps it, as the DMA below requires.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = kRsrcWord3;
+    return r;
+}
+
 // 16-byte buffer load of every lane into LDS at lds + 16 * lane (the
 // buffer-to-LDS DMA; offsets at or past the range read as zero).  Issued
 // through asm because the compiler, unable to tell which stage a DMA writes,
 // would otherwise wait for it before every later LDS read; the kernel orders
 // DMA and LDS reads itself (memory-count wait and barrier once per tile).
-__device__ __forceinline__ void dma_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds, uint32_t voffset) {
+__device__ __forceinline__ void dma_load16(u32x4 rsrc, uint32_t lds, uint32_t voffset) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"

@@ -96,8 +96,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int L = p.L;
     const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * L * D;
     const uint32_t head_bytes = static_cast<uint32_t>(L) * ROWB;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + kvoff), 0, head_bytes, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + kvoff), 0, head_bytes, kRsrcWord3);
+    const u32x4 rk = buffer_rsrc(p.k + kvoff, head_bytes);
+    const u32x4 rv = buffer_rsrc(p.v + kvoff, head_bytes);
     const int q0 = qt * (NW * 32);
 
     // ---- tile source ------------------------------------------------------
@@ -460,22 +460,36 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         Src sv, sk;  // sources of the next V and K fetches
         init_src(sv);
         init_src(sk);
-        // block form: tile 0 is in the first kept block, and so is tile 1 with
-        // two tiles per block, so neither DMA waits for an index load
-        if constexpr (MODE == MODE_BLOCK)
-            sk.j = j_first;
-        else
+        if constexpr (MODE == MODE_COLUMN) {
+            // the column lists of tiles 0 and 1 first, then all three gathers:
+            // no gather waits behind another's index load
+            Src s1c;
+            init_src(s1c);
             load_src(sk, 0);
-        dma_rows(smem, 0, sk, std::false_type{});
-        dma_rows(smem, 0, sk, std::true_type{});
-        if constexpr (MODE == MODE_BLOCK) {
-            if (sub_shift == 0) load_src(sk, 1);
+            load_src(s1c, 1);
+            dma_rows(smem, 0, sk, std::false_type{});
+            dma_rows(smem + STAGEB, 1, s1c, std::false_type{});
+            dma_rows(smem, 0, sk, std::true_type{});
+            sv = s1c;
+            load_src(sk, 2);
         } else {
-            load_src(sk, 1);
+            // block form: tile 0 is in the first kept block, and so is tile 1
+            // with two tiles per block, so neither DMA waits for an index load
+            if constexpr (MODE == MODE_BLOCK)
+                sk.j = j_first;
+            else
+                load_src(sk, 0);
+            dma_rows(smem, 0, sk, std::false_type{});
+            dma_rows(smem, 0, sk, std::true_type{});
+            if constexpr (MODE == MODE_BLOCK) {
+                if (sub_shift == 0) load_src(sk, 1);
+            } else {
+                load_src(sk, 1);
+            }
+            dma_rows(smem + STAGEB, 1, sk, std::false_type{});
+            load_src(sv, 1);
+            load_src(sk, 2);
         }
-        dma_rows(smem + STAGEB, 1, sk, std::false_type{});
-        load_src(sv, 1);
-        load_src(sk, 2);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         f32x16 s0, s1;

@@ -72,10 +72,8 @@ __global__ __launch_bounds__(CS_NW * 64) void colsum_bf16_kernel(ColParams p) {
     const uint16_t* kh = static_cast<const uint16_t*>(p.k) + (static_cast<size_t>(b) * p.Hkv + g) * L * D;
     const uint16_t* qh = static_cast<const uint16_t*>(p.q) + static_cast<size_t>(bh) * L * D;
     const float* lh = p.lse + static_cast<size_t>(bh) * L;
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qh), 0,
-                                                                        static_cast<uint32_t>(L) * ROWB, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(lh), 0,
-                                                                        static_cast<uint32_t>(L) * 4, kRsrcWord3);
+    const u32x4 rq = buffer_rsrc(qh, static_cast<uint32_t>(L) * ROWB);
+    const u32x4 rl = buffer_rsrc(lh, static_cast<uint32_t>(L) * 4);
 
     bf16x8 kreg[DK];
     {
