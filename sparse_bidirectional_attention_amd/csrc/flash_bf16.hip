@@ -632,7 +632,16 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     } else {
         run_pass(std::false_type{});
     }
-    if (__syncthreads_or(!(l_acc <= kBigRow))) {
+    // one flag per wave and one barrier; the barrier also ends every wave's
+    // reads of the stages, which the epilogue reuses
+    __shared__ int redo_flag[NW];
+    const bool wave_redo = __any(!(l_acc <= kBigRow));
+    if (lane == 0) redo_flag[wave] = wave_redo ? 1 : 0;
+    __syncthreads();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) redo |= redo_flag[w];
+    if (redo) {
         m_ref = -kInf;
         mc = -kInf;
         l_acc = 0.f;
@@ -641,8 +650,8 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
         run_pass(std::true_type{});
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
     const float lt = sum_with_half_swap(l_acc);
