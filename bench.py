@@ -36,6 +36,7 @@ METRIC = "ms/denoise step + effective TFLOP/s (MFMA %) of sparse attn at 8K–64
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+MAX_GFX_CLOCK_MHZ = 2400.0  # the clock the MFMA peak is quoted at
 
 
 def log(*a):
@@ -55,6 +56,71 @@ def rescaled(w, K):
     refresh = tuple(sorted({min(K - 1, int(round(t * f))) for t in w.refresh_steps} - {sel}))
     return scaled(w, total_steps=K, dense_steps=dense, select_step=sel, refresh_interval=interval,
                   refresh_steps=refresh)
+
+
+class GpuMonitor:
+    """Samples the GPU's socket power and graphics clocks with amd-smi from a
+    host thread while the timed region runs.  Under sustained MFMA load the
+    chip may run below its 2.4 GHz maximum (power management); the samples
+    show at which clock the timed steps actually ran.  Reports nothing when
+    amd-smi is absent or fails."""
+
+    def __init__(self, period_s=0.5):
+        import shutil
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self.exe = shutil.which("amd-smi")
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def read(self):
+        import subprocess
+        r = subprocess.run([self.exe, "metric", "-g", "0", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        if r.returncode != 0:
+            raise RuntimeError(f"amd-smi exited {r.returncode}: {r.stderr.strip()[:200]}")
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+        power = float(g["power"]["socket_power"]["value"])
+        clocks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                  if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        return power, (sum(clocks) / len(clocks) if clocks else None)
+
+    def _run(self):
+        while not self._stop.is_set():
+            t0 = time.perf_counter()
+            try:
+                self.samples.append(self.read())
+            except Exception as e:  # noqa: BLE001 - monitoring must never break the bench
+                self.error = str(e)
+                return
+            self._stop.wait(max(0.0, self.period - (time.perf_counter() - t0)))
+
+    def start(self):
+        if self.exe:
+            self._thread.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join(timeout=30)
+
+    def summary(self):
+        import numpy as np
+        if not self.samples:
+            return {"samples": 0, "error": self.error or ("amd-smi not found" if not self.exe else None)}
+        pw = np.array([s[0] for s in self.samples])
+        ck = np.array([s[1] for s in self.samples if s[1] is not None])
+        out = {"samples": len(self.samples), "tool": "amd-smi metric -p -c",
+               "socket_power_w": {"median": round(float(np.median(pw)), 1), "min": round(float(pw.min()), 1),
+                                  "max": round(float(pw.max()), 1)}}
+        if len(ck):
+            out["gfx_clock_mhz"] = {"median": round(float(np.median(ck)), 1), "min": round(float(ck.min()), 1),
+                                    "max": round(float(ck.max()), 1)}
+        return out
 
 
 def schedule_desc(sd, w):
@@ -236,6 +302,7 @@ def main():
     h = sd.sdattn_schedule_create(p, schedule_desc(sd, w))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
+    monitor = GpuMonitor().start()
     t_wall = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -248,6 +315,7 @@ def main():
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    monitor.stop()
     total_ms = start.elapsed_time(end)
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     stats, last_sel = sd.sdattn_schedule_stats(h)
@@ -337,6 +405,13 @@ def main():
     roof = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dom
 
+    # the MFMA peak scales with the graphics clock: the published peak is at 2.4 GHz
+    gpu_state = monitor.summary()
+    if "gfx_clock_mhz" in gpu_state:
+        clk = gpu_state["gfx_clock_mhz"]["median"]
+        gpu_state["peak_at_median_clock_tflops"] = round(peak * clk / MAX_GFX_CLOCK_MHZ, 1)
+        gpu_state["frac_of_peak_at_median_clock"] = {
+            k: round(v["achieved"] / (peak * clk / MAX_GFX_CLOCK_MHZ), 4) for k, v in kernels.items() if v["achieved"]}
     out = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),
@@ -369,6 +444,7 @@ def main():
                            "sparse_step_speedup": round(dense_base_ms / sparse_ms, 3) if sparse_ms else None},
         "kernels": kernels,
         "wall_s": round(wall, 2),
+        "gpu_state": gpu_state,
         "schedule_stats": stats,
     }
     if not args.no_cpu_baseline:
