@@ -127,7 +127,8 @@ def schedule_desc(sd, w):
     sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
-                            w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac)
+                            w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac,
+                            w.probe_interval, w.min_overlap)
 
 
 def to_dev(x):
@@ -205,6 +206,12 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
                                       qblocks=qb)
         t_sparse = (time.perf_counter() - t0) * (nqb / len(qb)) * H
         samples["sparse"] = f"{len(qb)} query blocks of 1 head, x{nqb / len(qb) * H:.0f}"
+        t_ov = 0.0
+        if "PROBE_SPARSE" in acts:
+            t0 = time.perf_counter()
+            oracle.mask_overlap(rp, ci, rp, ci)
+            t_ov = (time.perf_counter() - t0) * H
+            samples["overlap"] = f"pattern overlap of 1 head's rows, x{H}"
     else:
         kcol = oracle.count_from_fraction(w.column_keep_frac, L)
         qrows = np.arange(0, L, max(1, L // 16))[:16]
@@ -219,9 +226,10 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
         oracle.column_sparse_attention(xs["q"][:, :1], xs["k"][:, :1], xs["v"][:, :1], cols[:, :1], rows=qrows)
         t_sparse = (time.perf_counter() - t0) * (L / len(qrows)) * H
         samples["sparse"] = f"{len(qrows)} query rows of 1 head, x{L / len(qrows) * H:.0f}"
-    n = {a: acts.count(a) for a in ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE")}
+        t_ov = 0.0
+    n = {a: acts.count(a) for a in ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE", "PROBE_SPARSE")}
     total = (n["DENSE"] * t_dense + n["DENSE_SELECT"] * (t_dense + t_sel) + n["SELECT_SPARSE"] * (t_sel + t_sparse)
-             + n["SPARSE"] * t_sparse)
+             + n["SPARSE"] * t_sparse + n["PROBE_SPARSE"] * (t_sel + t_ov + t_sparse))
     ms = 1e3 * total / len(acts)
     return {"value": round(ms, 3), "unit": "ms/denoise step", "cores": threads, "host_cores": cores,
             "kind": "oracle",
@@ -238,6 +246,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="sparsed_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe-interval", type=int, default=None,
+                    help="adaptive anchors (block workloads): probe the pattern every N steps after the selection")
+    ap.add_argument("--min-overlap", type=float, default=0.9,
+                    help="with --probe-interval: adopt a probe whose overlap with the cached pattern is below this")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
                          "kernel that scales the profiler's HBM byte counters)")
@@ -255,10 +267,13 @@ def main():
     import oracle
 
     w0 = get_workload(args.workload)
+    if args.probe_interval is not None:
+        from workloads.configs import scaled
+        w0 = scaled(w0, probe_interval=args.probe_interval, min_overlap=args.min_overlap)
     K = args.steps if args.steps is not None else w0.total_steps
     w = rescaled(w0, K)
     acts = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
-                                   w.refresh_steps, w.refresh_dense)
+                                   w.refresh_steps, w.refresh_dense, w.probe_interval)
     torch.cuda.set_device(0)
     log(f"workload {w.name}: L={w.seq_len} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} {w.dtype} "
         f"block={w.block}; schedule of {K} steps: " + ", ".join(f"{a} x{acts.count(a)}" for a in sorted(set(acts))))
@@ -282,7 +297,7 @@ def main():
         ww = rescaled(w0, max(2, args.warmup))
         hw = sd.sdattn_schedule_create(p, schedule_desc(sd, ww))
         acts_w = oracle.schedule_actions(ww.total_steps, ww.dense_steps, ww.select_step, ww.refresh_interval,
-                                         ww.refresh_steps, ww.refresh_dense)
+                                         ww.refresh_steps, ww.refresh_dense, ww.probe_interval)
         for t in range(args.warmup):
             x = inputs_for(t, acts_w[t])
             sd.sdattn_schedule_step(hw, t, x["q"], x["k"], x["v"], o, lse)
@@ -319,6 +334,7 @@ def main():
     total_ms = start.elapsed_time(end)
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     stats, last_sel = sd.sdattn_schedule_stats(h)
+    n_probes, n_adopted, last_overlap = sd.sdattn_schedule_probe_stats(h)
 
     # pattern size for the kept-FLOP count
     L, H, Hkv, d = w.seq_len, w.q_heads, w.kv_heads, w.head_dim
@@ -372,6 +388,7 @@ def main():
     elif idx.get("DENSE_SELECT"):
         select_ms = med(step_ms[idx["DENSE_SELECT"]]) - dense_ms
 
+    probe_ms = med(step_ms[idx["PROBE_SPARSE"]]) if idx.get("PROBE_SPARSE") else None
     ms_per_step = total_ms / K
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # Roofline figures use each kernel's average launch inside the timed region:
@@ -385,7 +402,7 @@ def main():
     dense_tflops = dense_flops / (dense_launch_ms * 1e9)
     dense_base_tflops = dense_flops / (dense_base_ms * 1e9)
     # kernel with the largest share of the timed region
-    n_sparse = len(idx.get("SPARSE", [])) + len(idx.get("SELECT_SPARSE", []))
+    n_sparse = len(idx.get("SPARSE", [])) + len(idx.get("SELECT_SPARSE", [])) + len(idx.get("PROBE_SPARSE", []))
     n_dense = len(idx.get("DENSE", [])) + len(idx.get("DENSE_SELECT", []))
     share_sparse = n_sparse * (sparse_launch_ms or 0)
     share_dense = n_dense * dense_launch_ms
@@ -438,6 +455,10 @@ def main():
                    "sparse_effective_tflops": round(sparse_tflops, 1) if sparse_tflops else None,
                    "sparse_mfma_frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
                    "kept_density": round(density, 5), "kept_nnz": nnz},
+        "probes": ({"probe_step_ms": round(probe_ms, 4), "probe_overhead_ms": round(probe_ms - sparse_ms, 4)
+                    if sparse_ms else None, "n_probes": n_probes, "n_adopted": n_adopted,
+                    "last_overlap": round(last_overlap, 6), "min_overlap": w.min_overlap,
+                    "probe_interval": w.probe_interval} if probe_ms is not None else None),
         "dense_baseline": {"ms_per_step": round(dense_base_ms, 3), "tflops": round(dense_base_tflops, 1),
                            "mfma_frac": round(dense_base_tflops / peak, 4),
                            "schedule_speedup": round(dense_base_ms / ms_per_step, 3),

@@ -16,7 +16,9 @@
  *     column-summed attention at an early step, refreshed at a few
  *     intermediate steps (PulseCol, Abstract): sdattn_select_columns and
  *     sdattn_forward_column_sparse.
- *   - A host-side schedule handle runs warm-up, reuse and refresh.
+ *   - A host-side schedule handle runs warm-up, reuse and refresh, and can
+ *     probe the pattern between anchors and refresh it when it has moved
+ *     (sdattn_mask_overlap).
  *
  * Conventions for every call
  *   Tensors.   Caller-owned device buffers, contiguous.  q and o are
@@ -57,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SDATTN_ABI_VERSION 1
+#define SDATTN_ABI_VERSION 2
 
 /* Exported entry points (the library is built with hidden visibility). */
 #define SDATTN_API __attribute__((visibility("default")))
@@ -176,6 +178,22 @@ SDATTN_API sdattn_status sdattn_forward_block_sparse(const sdattn_problem* p, co
                                           const int32_t* row_ptr, const int32_t* col_idx,
                                           void* o, float* lse, void* stream);
 
+/*
+ * Overlap of two block patterns (the test of an adaptive anchor: Step-dLLM,
+ * Abstract, patterns hold only locally across steps).  A and B are CSR
+ * patterns over the same `rows` rows (row_ptr [rows + 1], rows ascending and
+ * duplicate-free, as sdattn_select_blocks writes them).  Writes, to the
+ * device array counts [3] (int64): |A n B| over (row, block) pairs, |A| =
+ * row_ptr_a[rows] - row_ptr_a[0] and |B| likewise.  Enqueued on `stream`;
+ * counts is overwritten (not accumulated).  rows >= 0 (rows == 0 gives
+ * {0, 0, 0}); SDATTN_ERR_NULL if a pointer is NULL while rows > 0, or if
+ * counts is NULL.  The patterns are trusted: a row_ptr that is not
+ * non-decreasing, or that points past its col_idx, reads out of bounds.
+ */
+SDATTN_API sdattn_status sdattn_mask_overlap(int32_t rows, const int32_t* row_ptr_a, const int32_t* col_idx_a,
+                                  const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,
+                                  void* stream);
+
 /* Workspace bytes for sdattn_select_columns.  Host only. */
 SDATTN_API sdattn_status sdattn_select_columns_workspace(const sdattn_problem* p, int32_t kcol,
                                               size_t* ws_bytes);
@@ -212,7 +230,9 @@ typedef enum {
     SDATTN_ACT_DENSE = 0,         /* dense attention                          */
     SDATTN_ACT_DENSE_SELECT = 1,  /* dense attention, then a new pattern      */
     SDATTN_ACT_SELECT_SPARSE = 2, /* new pattern from this step, then sparse  */
-    SDATTN_ACT_SPARSE = 3         /* sparse attention with the cached pattern */
+    SDATTN_ACT_SPARSE = 3,        /* sparse attention with the cached pattern */
+    SDATTN_ACT_PROBE_SPARSE = 4   /* probe selection, adopt it if the pattern
+                                     moved, then sparse attention            */
 } sdattn_action;
 
 /*
@@ -228,6 +248,20 @@ typedef enum {
  * column scores use the dense pass's lse; kcol = max(1, ceil(
  * column_keep_frac * L - 1e-9)).  A new pattern applies from the step that
  * builds it (SELECT_SPARSE) or from the next step (DENSE_SELECT).
+ *
+ * Adaptive anchors (blocks only; Step-dLLM, Abstract: attention patterns
+ * hold only locally across steps and change abruptly at some transitions,
+ * so the mask is refreshed at anchor steps).  With probe_interval = s > 0, a
+ * step t not in S with t >= dense_steps, t > select_step and
+ * (t - select_step) mod s == 0 is PROBE_SPARSE: the pooled selector runs on
+ * the step's Q/K into the idle pattern buffer, the overlap
+ * J = |A n B| / |A u B| of the cached pattern A and the probe B is taken
+ * over (row, block) pairs (J = 1 when both are empty), and if
+ * J < min_overlap the probe replaces the cached pattern before the sparse
+ * attention of that step; otherwise the cached pattern stays.  The decision
+ * is made on the GPU (no host synchronisation); see
+ * sdattn_schedule_probe_stats.  0 <= min_overlap <= 1 (0: never adopt,
+ * 1: adopt whenever the patterns differ).
  */
 typedef struct {
     int32_t total_steps;
@@ -241,6 +275,8 @@ typedef struct {
     int32_t block_q, block_k;       /* blocks only */
     sdattn_budget budget;           /* blocks only */
     double column_keep_frac;        /* columns only */
+    int32_t probe_interval;         /* 0 = no probes; blocks only (ABI 2) */
+    double min_overlap;             /* adoption threshold of a probe (ABI 2) */
 } sdattn_schedule_desc;
 
 typedef struct sdattn_schedule sdattn_schedule; /* opaque */
@@ -272,9 +308,19 @@ SDATTN_API sdattn_status sdattn_schedule_mask(const sdattn_schedule* s, const in
                                    const int32_t** col_idx, int64_t* nnz_capacity);
 
 /* Counters: number of steps run by action (4 entries, indexed by
- * sdattn_action) and the step of the last selection (-1 if none). */
+ * sdattn_action; PROBE_SPARSE steps are counted by
+ * sdattn_schedule_probe_stats) and the step of the last selection or
+ * adopted probe known to the host (-1 if none; adoption is decided on the
+ * GPU, so probes are not reflected here). */
 SDATTN_API sdattn_status sdattn_schedule_stats(const sdattn_schedule* s, int64_t counts[4],
                                     int32_t* last_select_step);
+
+/* Probe counters: probe steps run, probes adopted, and the overlap J of
+ * the last probe (1.0 if none).  Waits for `stream` (the stream the steps
+ * were enqueued on; NULL = default stream), then reads the counters from
+ * device memory: a synchronous call. */
+SDATTN_API sdattn_status sdattn_schedule_probe_stats(const sdattn_schedule* s, int64_t* n_probes,
+                                          int64_t* n_adopted, double* last_overlap, void* stream);
 
 /* Frees the handle and its device buffers (NULL is a no-op).  The caller
  * must make sure no enqueued step still uses them (synchronise first). */

@@ -15,8 +15,9 @@ Modules
   select    : block mean-pooling, pooled scores and their softmax mass,
               top-k and mass-with-global-cap block selection to CSR,
               exact column scores and column top-k.
-  schedule  : the per-step action table (warm-up, selection, reuse, refresh)
-              and a whole-schedule runner for small shapes.
+  schedule  : the per-step action table (warm-up, selection, reuse, refresh,
+              probes), the overlap of two block patterns and the probe's
+              adoption rule, and a whole-schedule runner for small shapes.
 
 Every function is pinned by the CPU tests (tests/test_oracle_*.py) to
 brute force, closed forms, library routines or invariants; no function is
@@ -45,4 +46,12 @@ from .select import (  # noqa: F401
     select_mass_cap,
     select_topk,
 )
-from .schedule import ACTIONS, run_schedule, schedule_actions, select_steps  # noqa: F401
+from .schedule import (  # noqa: F401
+    ACTIONS,
+    mask_overlap,
+    overlap_ratio,
+    probe_adopts,
+    run_schedule,
+    schedule_actions,
+    select_steps,
+)

@@ -24,7 +24,7 @@ STATUS_NAMES = ["SDATTN_OK", "SDATTN_ERR_NULL", "SDATTN_ERR_SHAPE", "SDATTN_ERR_
 SDATTN_F32, SDATTN_BF16 = 0, 1
 SDATTN_BUDGET_TOPK, SDATTN_BUDGET_MASS = 0, 1
 SDATTN_SEL_BLOCKS, SDATTN_SEL_COLUMNS = 0, 1
-ACTIONS = ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE")
+ACTIONS = ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE", "PROBE_SPARSE")
 
 
 class SdattnError(RuntimeError):
@@ -50,7 +50,8 @@ class ScheduleDesc(ctypes.Structure):
                 ("refresh_interval", ctypes.c_int32), ("refresh_steps", ctypes.POINTER(ctypes.c_int32)),
                 ("n_refresh_steps", ctypes.c_int32), ("refresh_dense", ctypes.c_int32), ("sel", ctypes.c_int),
                 ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("budget", Budget),
-                ("column_keep_frac", ctypes.c_double)]
+                ("column_keep_frac", ctypes.c_double), ("probe_interval", ctypes.c_int32),
+                ("min_overlap", ctypes.c_double)]
 
 
 _P = ctypes.c_void_p
@@ -73,6 +74,7 @@ _SIGS = {
                                              ctypes.c_size_t, _P]),
     "sdattn_forward_column_sparse": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.c_int32, _P,
                                                     _P, _P]),
+    "sdattn_mask_overlap": (ctypes.c_int, [ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "sdattn_schedule_create": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.POINTER(ScheduleDesc),
                                               ctypes.POINTER(_P)]),
     "sdattn_schedule_action": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int)]),
@@ -80,6 +82,8 @@ _SIGS = {
     "sdattn_schedule_mask": (ctypes.c_int, [_P, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                             ctypes.POINTER(ctypes.c_int64)]),
     "sdattn_schedule_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32)]),
+    "sdattn_schedule_probe_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                                   ctypes.POINTER(ctypes.c_double), _P]),
     "sdattn_schedule_destroy": (None, [_P]),
 }
 
@@ -226,13 +230,21 @@ def sdattn_forward_column_sparse(p, q, k, v, col_idx, kcol, o, lse=None, stream=
            "sdattn_forward_column_sparse")
 
 
+def sdattn_mask_overlap(rows, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, counts, stream=None):
+    """counts: int64 device tensor of 3 slots <- (|A n B|, |A|, |B|)."""
+    _check(lib().sdattn_mask_overlap(rows, _ptr(row_ptr_a), _ptr(col_idx_a), _ptr(row_ptr_b), _ptr(col_idx_b),
+                                     _ptr(counts), _stream(stream)), "sdattn_mask_overlap")
+
+
 def schedule_desc(total_steps, dense_steps, select_step, refresh_interval=0, refresh_steps=(), refresh_dense=False,
-                  sel=SDATTN_SEL_BLOCKS, block_q=128, block_k=128, budget=None, column_keep_frac=0.0):
+                  sel=SDATTN_SEL_BLOCKS, block_q=128, block_k=128, budget=None, column_keep_frac=0.0,
+                  probe_interval=0, min_overlap=0.0):
     arr = (ctypes.c_int32 * max(1, len(refresh_steps)))(*refresh_steps)
     d = ScheduleDesc(total_steps, dense_steps, select_step, refresh_interval,
                      ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)) if refresh_steps else None,
                      len(refresh_steps), int(bool(refresh_dense)), sel, block_q, block_k,
-                     budget if budget is not None else topk_budget(1.0), column_keep_frac)
+                     budget if budget is not None else topk_budget(1.0), column_keep_frac, probe_interval,
+                     min_overlap)
     d._keep = arr  # the C side copies the array at create; keep it alive until then
     return d
 
@@ -266,7 +278,15 @@ def sdattn_schedule_stats(h):
     counts = (ctypes.c_int64 * 4)()
     last = ctypes.c_int32(0)
     _check(lib().sdattn_schedule_stats(h, counts, ctypes.byref(last)), "sdattn_schedule_stats")
-    return {a: counts[i] for i, a in enumerate(ACTIONS)}, last.value
+    return {a: counts[i] for i, a in enumerate(ACTIONS[:4])}, last.value
+
+
+def sdattn_schedule_probe_stats(h, stream=None):
+    """(probe steps run, probes adopted, overlap of the last probe); waits for the stream."""
+    n, a, j = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_double(0.0)
+    _check(lib().sdattn_schedule_probe_stats(h, ctypes.byref(n), ctypes.byref(a), ctypes.byref(j), _stream(stream)),
+           "sdattn_schedule_probe_stats")
+    return n.value, a.value, j.value
 
 
 def sdattn_schedule_destroy(h):

@@ -8,6 +8,7 @@
 
 #include "host_common.h"
 #include "launch.h"
+#include "probe.h"
 #include "schedule.h"
 
 using namespace sdattn;
@@ -170,6 +171,19 @@ sdattn_status sdattn_forward_column_sparse(const sdattn_problem* p, const void* 
     return run_attention(MODE_COLUMN, pr, q, k, v, o, lse, ix, stream, "sdattn_forward_column_sparse");
 }
 
+sdattn_status sdattn_mask_overlap(int32_t rows, const int32_t* row_ptr_a, const int32_t* col_idx_a,
+                                  const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,
+                                  void* stream) {
+    if (rows < 0) return fail(SDATTN_ERR_SHAPE, "rows must be >= 0");
+    if (counts == nullptr) return fail(SDATTN_ERR_NULL, "counts must be non-NULL");
+    if (rows > 0 && (row_ptr_a == nullptr || col_idx_a == nullptr || row_ptr_b == nullptr || col_idx_b == nullptr))
+        return fail(SDATTN_ERR_NULL, "row_ptr and col_idx of both patterns must be non-NULL");
+    hipError_t e = launch_mask_overlap(rows, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, counts,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdattn_mask_overlap");
+    return SDATTN_OK;
+}
+
 }  // extern "C"
 
 // ---- HIP backend of the schedule driver ------------------------------------
@@ -213,9 +227,34 @@ sdattn_status be_alloc(void*, size_t bytes, void** out) {
     return SDATTN_OK;
 }
 void be_release(void*, void* ptr) { (void)hipFree(ptr); }
+sdattn_status be_overlap(void*, int32_t rows, const int32_t* rpa, const int32_t* cia, const int32_t* rpb,
+                         const int32_t* cib, int64_t* counts, void* st) {
+    return sdattn_mask_overlap(rows, rpa, cia, rpb, cib, counts, st);
+}
+sdattn_status be_probe_adopt(void*, int32_t rows, int32_t* rp_dst, int32_t* ci_dst, const int32_t* rp_src,
+                             const int32_t* ci_src, const int64_t* counts, void* state, double min_overlap,
+                             int64_t max_copy, void* st) {
+    hipError_t e = launch_probe_adopt(rows, rp_dst, ci_dst, rp_src, ci_src, counts, static_cast<ProbeState*>(state),
+                                      min_overlap, max_copy, static_cast<hipStream_t>(st));
+    if (e != hipSuccess) return hip_fail(e, "probe adoption");
+    return SDATTN_OK;
+}
+sdattn_status be_probe_init(void*, void* state) {
+    hipError_t e = launch_probe_init(static_cast<ProbeState*>(state), nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "probe record initialisation");
+    return SDATTN_OK;
+}
+sdattn_status be_probe_read(void*, const void* state, int64_t out[4], void* st) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(st));
+    if (e == hipSuccess) e = hipMemcpy(out, state, sizeof(ProbeState), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "sdattn_schedule_probe_stats");
+    return SDATTN_OK;
+}
 
-const Backend kHipBackend = {nullptr,          be_dense,        be_select_blocks, be_block_sparse, be_select_columns,
-                             be_column_sparse, be_ws_blocks,    be_ws_columns,    be_alloc,        be_release};
+const Backend kHipBackend = {nullptr,          be_dense,       be_select_blocks, be_block_sparse, be_select_columns,
+                             be_column_sparse, be_ws_blocks,   be_ws_columns,    be_alloc,        be_release,
+                             be_overlap,       be_probe_adopt, be_probe_init,    be_probe_read};
 
 }  // namespace
 

@@ -1,7 +1,10 @@
 // Host-side step-schedule driver (SparseD, abstract: full attention in the
 // early steps, then a pattern computed once and reused; Step-dLLM, Abstract:
 // refresh at anchor steps, reuse within each interval; PulseCol, Abstract:
-// column pattern refreshed at a few intermediate steps).
+// column pattern refreshed at a few intermediate steps).  Between anchors a
+// block schedule can probe: rerun the pooled selector and adopt its pattern
+// when it overlaps the cached one too little (Step-dLLM, Abstract: patterns
+// hold only locally and change abruptly at some transitions).
 //
 // The handle owns two pattern buffers: a selection always writes the buffer
 // not in use and the handle switches to it only when every call of the step
@@ -33,6 +36,10 @@ struct sdattn_schedule {
     float* lse = nullptr;  // own lse buffer (columns)
     int64_t counts[4] = {0, 0, 0, 0};
     int32_t last_select = -1;
+    // probes (blocks with probe_interval > 0): device counts [3] + ProbeState
+    int64_t rows = 0;
+    int64_t* probe_buf = nullptr;  // [0..2] overlap counts, [4..7] probe record
+    int64_t n_probes = 0;          // probe steps enqueued (host count)
 };
 
 namespace sdattn {
@@ -47,7 +54,10 @@ sdattn_action schedule_action_of(const sdattn_schedule_desc& d, int32_t t) {
         const bool dense = t < d.dense_steps || (d.refresh_dense && t > d.select_step);
         return dense ? SDATTN_ACT_DENSE_SELECT : SDATTN_ACT_SELECT_SPARSE;
     }
-    return t < d.dense_steps ? SDATTN_ACT_DENSE : SDATTN_ACT_SPARSE;
+    if (t < d.dense_steps) return SDATTN_ACT_DENSE;
+    if (d.probe_interval > 0 && t > d.select_step && (t - d.select_step) % d.probe_interval == 0)
+        return SDATTN_ACT_PROBE_SPARSE;
+    return SDATTN_ACT_SPARSE;
 }
 
 namespace {
@@ -74,7 +84,12 @@ sdattn_status check_desc(const Problem& pr, const sdattn_schedule_desc* d) {
         // the first column selection needs a dense pass for its lse
         if (d->select_step >= d->dense_steps)
             return fail(SDATTN_ERR_SHAPE, "column selection step must be a dense step (select_step < dense_steps)");
+        if (d->probe_interval != 0)
+            return fail(SDATTN_ERR_UNSUPPORTED, "probes are for block patterns (column selection needs a dense pass)");
     }
+    if (d->probe_interval < 0) return fail(SDATTN_ERR_SHAPE, "probe_interval must be >= 0");
+    if (d->probe_interval > 0 && !(d->min_overlap >= 0.0 && d->min_overlap <= 1.0))
+        return fail(SDATTN_ERR_BUDGET, "min_overlap must be in [0, 1]");
     (void)pr;
     return SDATTN_OK;
 }
@@ -118,6 +133,7 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         st = s->be.workspace_blocks(s->be.ctx, p, desc->block_q, desc->block_k, &desc->budget, &s->ws_bytes, &max_nnz);
         if (st != SDATTN_OK) return cleanup_fail(st);
         s->nnz_cap = std::max<int64_t>(max_nnz, 1);
+        s->rows = plan.rows;
         rp_bytes = static_cast<size_t>(plan.rows + 1) * sizeof(int32_t);
         ci_bytes = static_cast<size_t>(s->nnz_cap) * sizeof(int32_t);
     } else {
@@ -140,6 +156,12 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
     }
     if (s->ws_bytes) {
         st = s->be.alloc(s->be.ctx, s->ws_bytes, &s->ws);
+        if (st != SDATTN_OK) return cleanup_fail(st);
+    }
+    if (desc->probe_interval > 0) {
+        st = s->be.alloc(s->be.ctx, 8 * sizeof(int64_t), reinterpret_cast<void**>(&s->probe_buf));
+        if (st != SDATTN_OK) return cleanup_fail(st);
+        st = s->be.probe_init(s->be.ctx, s->probe_buf + 4);
         if (st != SDATTN_OK) return cleanup_fail(st);
     }
     *out = s;
@@ -196,6 +218,32 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
                 s->last_select = step;
             }
             break;
+        case SDATTN_ACT_PROBE_SPARSE: {
+            // blocks only (checked at create).  The probe goes into the idle
+            // buffer; the adoption kernel copies it over the cached pattern
+            // when the overlap is below min_overlap, so the cached buffer
+            // stays the active one either way.
+            if (s->active < 0) return fail(SDATTN_ERR_STATE, "probe step before any pattern was selected");
+            // the adoption changes the cached pattern before the attention
+            // launch, so every argument that launch checks is checked first
+            if (s->pr.L > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+                return fail(SDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+            const int a = s->active;
+            st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
+                                  s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
+            if (st == SDATTN_OK)
+                st = be.overlap(be.ctx, static_cast<int32_t>(s->rows), s->row_ptr[a], s->col_idx[a], s->row_ptr[next],
+                                s->col_idx[next], s->probe_buf, stream);
+            if (st == SDATTN_OK)
+                st = be.probe_adopt(be.ctx, static_cast<int32_t>(s->rows), s->row_ptr[a], s->col_idx[a],
+                                    s->row_ptr[next], s->col_idx[next], s->probe_buf, s->probe_buf + 4,
+                                    s->desc.min_overlap, s->nnz_cap, stream);
+            if (st == SDATTN_OK)
+                st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[a],
+                                     s->col_idx[a], o, lse, stream);
+            if (st == SDATTN_OK) s->n_probes += 1;
+            return st;
+        }
         case SDATTN_ACT_SPARSE:
             if (s->active < 0) return fail(SDATTN_ERR_STATE, "sparse step before any pattern was selected");
             if (blocks)
@@ -228,9 +276,27 @@ sdattn_status sdattn_schedule_stats(const sdattn_schedule* s, int64_t counts[4],
     return SDATTN_OK;
 }
 
+sdattn_status sdattn_schedule_probe_stats(const sdattn_schedule* s, int64_t* n_probes, int64_t* n_adopted,
+                                          double* last_overlap, void* stream) {
+    if (s == nullptr || n_probes == nullptr || n_adopted == nullptr || last_overlap == nullptr)
+        return fail(SDATTN_ERR_NULL, "schedule or an output pointer is NULL");
+    *n_probes = 0;
+    *n_adopted = 0;
+    *last_overlap = 1.0;
+    if (s->probe_buf == nullptr) return SDATTN_OK;
+    int64_t rec[4] = {0, 0, 0, 0};
+    const sdattn_status st = s->be.probe_read(s->be.ctx, s->probe_buf + 4, rec, stream);
+    if (st != SDATTN_OK) return st;
+    *n_probes = rec[0];
+    *n_adopted = rec[1];
+    if (rec[0] > 0) *last_overlap = rec[3] > 0 ? static_cast<double>(rec[2]) / static_cast<double>(rec[3]) : 1.0;
+    return SDATTN_OK;
+}
+
 void sdattn_schedule_destroy(sdattn_schedule* s) {
     if (s == nullptr) return;
     const Backend& be = s->be;
+    if (s->probe_buf) be.release(be.ctx, s->probe_buf);
     for (int i = 0; i < 2; ++i) {
         if (s->row_ptr[i]) be.release(be.ctx, s->row_ptr[i]);
         if (s->col_idx[i]) be.release(be.ctx, s->col_idx[i]);

@@ -27,6 +27,17 @@ struct Backend {
     sdattn_status (*workspace_columns)(void* ctx, const sdattn_problem*, int32_t kcol, size_t* ws);
     sdattn_status (*alloc)(void* ctx, size_t bytes, void** out);
     void (*release)(void* ctx, void* ptr);
+    // adaptive anchors: overlap counts of two CSR patterns (counts [3] on the
+    // device), the probe's adoption decided and applied on the device, and
+    // the device-resident probe record (4 int64: probes, adopted, last
+    // |A n B|, last |A u B|)
+    sdattn_status (*overlap)(void* ctx, int32_t rows, const int32_t* rpa, const int32_t* cia, const int32_t* rpb,
+                             const int32_t* cib, int64_t* counts, void* stream);
+    sdattn_status (*probe_adopt)(void* ctx, int32_t rows, int32_t* rp_dst, int32_t* ci_dst, const int32_t* rp_src,
+                                 const int32_t* ci_src, const int64_t* counts, void* state, double min_overlap,
+                                 int64_t max_copy, void* stream);
+    sdattn_status (*probe_init)(void* ctx, void* state);                            // synchronous
+    sdattn_status (*probe_read)(void* ctx, const void* state, int64_t out[4], void* stream);  // synchronous
 };
 
 // The backend used by sdattn_schedule_create (defined by the library build

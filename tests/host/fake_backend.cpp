@@ -85,8 +85,36 @@ void f_release(void*, void* p) {
     --g_live;
 }
 
-const sdattn::Backend kFake = {nullptr,         f_dense,      f_select_blocks, f_block_sparse, f_select_columns,
-                               f_column_sparse, f_ws_blocks,  f_ws_columns,    f_alloc,        f_release};
+sdattn_status f_overlap(void*, int32_t rows, const int32_t* rpa, const int32_t* cia, const int32_t* rpb,
+                        const int32_t* cib, int64_t* counts, void*) {
+    return record("overlap rows=" + std::to_string(rows) + " a=" + ptr(rpa) + "," + ptr(cia) + " b=" + ptr(rpb) +
+                  "," + ptr(cib) + " counts=" + ptr(counts));
+}
+sdattn_status f_probe_adopt(void*, int32_t rows, int32_t* rp_dst, int32_t* ci_dst, const int32_t* rp_src,
+                            const int32_t* ci_src, const int64_t* counts, void* state, double min_overlap,
+                            int64_t max_copy, void*) {
+    char th[32];
+    snprintf(th, sizeof th, "%g", min_overlap);
+    const sdattn_status st = record("probe_adopt rows=" + std::to_string(rows) + " dst=" + ptr(rp_dst) + "," +
+                                    ptr(ci_dst) + " src=" + ptr(rp_src) + "," + ptr(ci_src) + " counts=" +
+                                    ptr(counts) + " state=" + ptr(state) + " min_overlap=" + th +
+                                    " max_copy=" + std::to_string(max_copy));
+    if (st == SDATTN_OK) static_cast<int64_t*>(state)[0] += 1;  // probes; the fake never adopts
+    return st;
+}
+sdattn_status f_probe_init(void*, void* state) {
+    for (int i = 0; i < 4; ++i) static_cast<int64_t*>(state)[i] = 0;
+    g_log.push_back("probe_init state=" + ptr(state));
+    return SDATTN_OK;
+}
+sdattn_status f_probe_read(void*, const void* state, int64_t out[4], void*) {
+    for (int i = 0; i < 4; ++i) out[i] = static_cast<const int64_t*>(state)[i];
+    return SDATTN_OK;
+}
+
+const sdattn::Backend kFake = {nullptr,         f_dense,       f_select_blocks, f_block_sparse, f_select_columns,
+                               f_column_sparse, f_ws_blocks,   f_ws_columns,    f_alloc,        f_release,
+                               f_overlap,       f_probe_adopt, f_probe_init,    f_probe_read};
 
 }  // namespace
 

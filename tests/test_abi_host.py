@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 18
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
     assert set(names) == exported  # nothing missing, nothing extra
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.sdattn_abi_version() == 1
+    assert sd.sdattn_abi_version() == 2
     for i, name in enumerate(sd.STATUS_NAMES):
         assert sd.sdattn_status_string(i) == name
 
@@ -109,6 +109,15 @@ def test_sparse_and_column_validation():
     assert lib.sdattn_select_columns(ctypes.byref(p), BAD, BAD, BAD, 492, BAD, None, BAD, ws - 8, None) == 5
     with pytest.raises(sd.SdattnError, match="BUDGET"):
         sd.sdattn_select_columns_workspace(p, 0)
+
+
+def test_mask_overlap_validation():
+    lib = sd.lib()
+    assert lib.sdattn_mask_overlap(-1, BAD, BAD, BAD, BAD, BAD, None) == 2
+    assert lib.sdattn_mask_overlap(4, BAD, BAD, BAD, BAD, None, None) == 1
+    assert lib.sdattn_mask_overlap(4, BAD, None, BAD, BAD, BAD, None) == 1
+    assert lib.sdattn_mask_overlap(4, BAD, BAD, None, BAD, BAD, None) == 1
+    assert "non-NULL" in sd.sdattn_last_error()
 
 
 def test_schedule_descriptor_validation():

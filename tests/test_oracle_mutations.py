@@ -11,6 +11,7 @@ from scipy.special import logsumexp
 
 import oracle
 import oracle.attention as oatt
+import oracle.schedule as osch
 import oracle.select as osel
 from workloads import tiny_random
 
@@ -62,9 +63,30 @@ def pin_topk_count():
     assert np.all(np.diff(rp) == 26)
 
 
+def pin_overlap_rows_matter():
+    # block 3 kept in row 0 of A and in row 1 of B: no common (row, block) pair
+    assert oracle.mask_overlap(np.array([0, 1, 1]), np.array([3]), np.array([0, 0, 1]), np.array([3])) == (0, 1, 1)
+
+
+def pin_overlap_ratio_hand():
+    # A = {(0,1), (0,2)}, B = {(0,2), (0,3)}: J = 1/3
+    c = oracle.mask_overlap(np.array([0, 2]), np.array([1, 2]), np.array([0, 2]), np.array([2, 3]))
+    assert oracle.overlap_ratio(*c) == 1 / 3
+
+
+def pin_adoption_strict():
+    assert not oracle.probe_adopts(1, 2, 2, 1 / 3) and oracle.probe_adopts(1, 2, 2, 0.34)
+
+
+def pin_probe_steps_hand():
+    assert oracle.schedule_actions(10, 2, 2, 4, (), False, probe_interval=3)[5] == "PROBE_SPARSE"
+    assert oracle.schedule_actions(10, 2, 2, 4, (), False, probe_interval=3).count("PROBE_SPARSE") == 2
+
+
 def test_pins_pass_on_the_real_oracle():
     for pin in (pin_dense_vs_torch, pin_pooling_closed_form, pin_topk_ties_brute_force,
-                pin_mass_exact_hit, pin_column_sum_total, pin_topk_count):
+                pin_mass_exact_hit, pin_column_sum_total, pin_topk_count, pin_overlap_rows_matter,
+                pin_overlap_ratio_hand, pin_adoption_strict, pin_probe_steps_hand):
         pin()
 
 
@@ -146,3 +168,31 @@ def test_floor_instead_of_ceil_count_is_caught(monkeypatch):
     monkeypatch.setattr(osel, "count_from_fraction",
                         lambda f, n: max(1, int(Fraction(str(f)) * n)))
     _fails(pin_topk_count)
+
+
+def test_overlap_that_ignores_rows_is_caught(monkeypatch):
+    monkeypatch.setattr(osch, "_pairs", lambda rp, ci: {int(c) for c in np.asarray(ci)})
+    _fails(pin_overlap_rows_matter)
+
+
+def test_union_taken_as_the_larger_pattern_is_caught(monkeypatch):
+    monkeypatch.setattr(osch, "overlap_ratio", lambda i, a, b: 1.0 if max(a, b) == 0 else i / max(a, b))
+    monkeypatch.setattr(oracle, "overlap_ratio", osch.overlap_ratio)
+    _fails(pin_overlap_ratio_hand)
+
+
+def test_adoption_at_equality_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "probe_adopts", lambda i, a, b, th: osch.overlap_ratio(i, a, b) <= th)
+    _fails(pin_adoption_strict)
+
+
+def test_probes_counted_from_step_zero_are_caught(monkeypatch):
+    real = osch.schedule_actions
+
+    def bad(total_steps, dense_steps, select_step, refresh_interval=0, refresh_steps=(), refresh_dense=False,
+            probe_interval=0):
+        acts = real(total_steps, dense_steps, select_step, refresh_interval, refresh_steps, refresh_dense)
+        return ["PROBE_SPARSE" if a == "SPARSE" and probe_interval and t % probe_interval == 0 else a
+                for t, a in enumerate(acts)]
+    monkeypatch.setattr(oracle, "schedule_actions", bad)
+    _fails(pin_probe_steps_hand)

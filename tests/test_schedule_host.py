@@ -17,6 +17,7 @@ import oracle
 import sparse_bidirectional_attention_amd as sd
 from sparse_bidirectional_attention_amd import build as sdbuild
 from workloads import WORKLOADS
+from workloads.configs import scaled
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -36,7 +37,8 @@ def _desc_of(w):
     sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
-                            w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac)
+                            w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac,
+                            w.probe_interval, w.min_overlap)
 
 
 def _prob_of(w):
@@ -86,9 +88,11 @@ def test_random_schedules_match_oracle(fake):
         interval = rng.choice([0, 0, 1, 3, 7])
         refresh = tuple(sorted(rng.sample(range(T), rng.randint(0, min(4, T)))))
         rdense = rng.random() < 0.5
-        d = sd.schedule_desc(T, dense, sel, interval, list(refresh), rdense, budget=sd.topk_budget(0.5))
+        probe = rng.choice([0, 0, 1, 2, 5])
+        d = sd.schedule_desc(T, dense, sel, interval, list(refresh), rdense, budget=sd.topk_budget(0.5),
+                             probe_interval=probe, min_overlap=0.5)
         h = _create(fake, p, d)
-        ref = oracle.schedule_actions(T, dense, sel, interval, refresh, rdense)
+        ref = oracle.schedule_actions(T, dense, sel, interval, refresh, rdense, probe)
         assert _actions(fake, h, T) == ref
         fake.sdattn_schedule_destroy(h)
     assert fake.sdattn_fake_live_allocs() == 0
@@ -178,5 +182,98 @@ def test_column_schedule_uses_own_lse_buffer(fake):
     for d, s in zip(dense, sel):  # dense writes the lse that the selection reads
         assert re.search(r"lse=(\S+)", d).group(1) == re.search(r"lse=(\S+)", s).group(1) != "(nil)"
     assert sum(l.startswith("column_sparse") for l in log) == 189
+    fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def _probe_desc(**kw):
+    w = scaled(WORKLOADS["llada8b_8k"], total_steps=12, refresh_interval=8, probe_interval=3, min_overlap=0.7)
+    return w, _desc_of(scaled(w, **kw))
+
+
+def test_probe_step_selects_into_the_idle_buffer_and_adopts_over_the_cached_one(fake):
+    w, d = _probe_desc()
+    fake.sdattn_fake_reset(-1, 0)
+    h = _create(fake, _prob_of(w), d)
+    init = _log(fake)
+    assert len(init) == 1 and init[0].startswith("probe_init")
+    state = re.search(r"state=(\S+)", init[0]).group(1)
+    assert _actions(fake, h, 12) == oracle.schedule_actions(12, 1, 0, 8, (), False, 3)
+    fake.sdattn_fake_reset(-1, 0)
+    for t in range(12):
+        assert _step(fake, h, t) == 0
+    log = _log(fake)
+    cached = re.search(r"rp=(\S+) ci=(\S+)", [l for l in log if l.startswith("select_blocks")][0]).groups()
+    i = 0
+    probes = 0
+    while i < len(log):
+        l = log[i]
+        if l.startswith("select_blocks") and i + 1 < len(log) and log[i + 1].startswith("overlap"):
+            # a probe: selection into the idle buffer, overlap(cached, probe),
+            # adoption of the probe over the cached buffer, attention on the cached buffer
+            probe_buf = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
+            assert probe_buf != cached
+            ov, ad, bs = log[i + 1], log[i + 2], log[i + 3]
+            assert re.search(r"a=(\S+),(\S+) b=(\S+),(\S+)", ov).groups() == cached + probe_buf
+            assert f"rows={32 * 128}" in ov
+            assert re.search(r"dst=(\S+),(\S+) src=(\S+),(\S+)", ad).groups() == cached + probe_buf
+            assert re.search(r"counts=(\S+)", ad).group(1) == re.search(r"counts=(\S+)", ov).group(1)
+            assert f"state={state}" in ad and "min_overlap=0.7" in ad and "max_copy=52428" in ad
+            assert bs.startswith("block_sparse") and re.search(r"rp=(\S+) ci=(\S+)", bs).groups() == cached
+            probes += 1
+            i += 4
+            continue
+        if l.startswith("select_blocks"):  # a scheduled refresh switches buffers
+            cached = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
+        i += 1
+    assert probes == 3  # steps 3, 6 and 9; the refresh at step 8 switches buffers before the last one
+    n, a, j = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()
+    assert fake.sdattn_schedule_probe_stats(h, ctypes.byref(n), ctypes.byref(a), ctypes.byref(j), None) == 0
+    assert (n.value, a.value) == (probes, 0)
+    fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def test_probe_descriptor_checks(fake):
+    w = WORKLOADS["llada8b_8k"]
+    p = _prob_of(w)
+    cases = [
+        (_desc_of(scaled(w, probe_interval=-1)), 2),
+        (_desc_of(scaled(w, probe_interval=4, min_overlap=1.5)), 4),
+        (_desc_of(scaled(w, probe_interval=4, min_overlap=-0.1)), 4),
+        (_desc_of(scaled(WORKLOADS["pulsecol_dream7b_16k"], probe_interval=4, min_overlap=0.5)), 8),
+    ]
+    for d, want in cases:
+        h = ctypes.c_void_p(None)
+        assert fake.sdattn_schedule_create(ctypes.byref(p), ctypes.byref(d), ctypes.byref(h)) == want
+        assert h.value is None
+    # min_overlap is not checked when there are no probes; 0 and 1 are valid thresholds
+    for d in (_desc_of(scaled(w, min_overlap=7.0)), _desc_of(scaled(w, probe_interval=2, min_overlap=0.0)),
+              _desc_of(scaled(w, probe_interval=2, min_overlap=1.0))):
+        h = _create(fake, p, d)
+        fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def test_probe_step_errors_leave_the_pattern_alone(fake):
+    w, d = _probe_desc()
+    h = _create(fake, _prob_of(w), d)
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 3) == 9 and _log(fake) == []  # no pattern yet
+    assert _step(fake, h, 0) == 0
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 3, o=0) == 1 and _log(fake) == []  # NULL output: nothing enqueued
+    fake.sdattn_fake_reset(0, 7)  # the probe's selection fails: no overlap, no adoption
+    assert _step(fake, h, 3) == 7
+    assert len(_log(fake)) == 1 and _log(fake)[0].startswith("FAIL select_blocks")
+    fake.sdattn_fake_reset(1, 7)  # the overlap fails: no adoption, no attention
+    assert _step(fake, h, 3) == 7
+    assert [l.split()[0] for l in _log(fake)] == ["select_blocks", "FAIL"]
+    n, a, j = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_double()
+    assert fake.sdattn_schedule_probe_stats(h, ctypes.byref(n), ctypes.byref(a), ctypes.byref(j), None) == 0
+    assert (n.value, a.value, j.value) == (0, 0, 1.0)
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 3) == 0
+    assert [l.split()[0] for l in _log(fake)] == ["select_blocks", "overlap", "probe_adopt", "block_sparse"]
     fake.sdattn_schedule_destroy(h)
     assert fake.sdattn_fake_live_allocs() == 0

@@ -44,6 +44,10 @@ class Workload:
     mass: float = 0.0             # cumulative pooled-mass target
     max_mean_density: float = 1.0  # global cap on the mean kept fraction
     column_keep_frac: float = 0.0  # top fraction of key columns per kv head
+    # adaptive anchors (blocks): probe every probe_interval sparse steps and
+    # adopt the probe when its overlap with the cached pattern is below min_overlap
+    probe_interval: int = 0
+    min_overlap: float = 0.0
     # generator
     pattern: str = "mix"          # "mix" (round-robin head types) or "columns"
     extra_pair_frac: float = 0.0  # fraction of (I, J) block pairs given extra alignment
