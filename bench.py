@@ -52,6 +52,8 @@ def rescaled(w, K):
     dense = min(K, int(math.ceil(w.dense_steps * f)))
     sel = min(dense, int(math.ceil(w.select_step * f))) if w.select_step else 0
     sel = min(sel, K - 1)
+    if w.refresh_dense and w.selector != "blocks" and dense > 0:
+        sel = min(sel, dense - 1)  # these selectors read a dense pass's lse: the selection step is dense
     interval = max(1, int(round(w.refresh_interval * f))) if w.refresh_interval else 0
     refresh = tuple(sorted({min(K - 1, int(round(t * f))) for t in w.refresh_steps} - {sel}))
     return scaled(w, total_steps=K, dense_steps=dense, select_step=sel, refresh_interval=interval,
@@ -124,7 +126,7 @@ class GpuMonitor:
 
 
 def schedule_desc(sd, w):
-    sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
+    sel = sd.SEL_KINDS[w.selector]
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
                             w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac,
@@ -185,14 +187,27 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
     samples["dense"] = f"{len(rows)} query rows of 1 head, x{L / len(rows) * H:.0f}"
     # selection: pooling + pooled mass + budget for one kv group, scaled to all groups
     t0 = time.perf_counter()
-    if w.selector == "blocks":
-        A = oracle.pooled_mass(xs["q"][:, :G], xs["k"][:, :1], w.block, w.block)
-        if w.budget == "topk":
-            oracle.select_topk(A, w.keep_frac)
+    if w.selector != "columns":
+        if w.selector == "blocks_exact":
+            # exact block mass of 4 query blocks of one head (with their lse), scaled to every block and head
+            nqb = -(-L // w.block)
+            nb = min(4, nqb)
+            qs = xs["q"][:, :1, :nb * w.block]
+            _, lse_s = oracle.dense_attention(qs, xs["k"][:, :1], xs["v"][:, :1])
+            t0 = time.perf_counter()
+            A = oracle.exact_block_mass(qs, xs["k"][:, :1], lse_s, w.block, w.block)
+            if w.budget == "topk":
+                oracle.select_topk(A, w.keep_frac)
+            t_sel = (time.perf_counter() - t0) * (nqb / nb) * H
+            samples["select"] = f"exact mass of {nb} query blocks of 1 head, x{nqb / nb * H:.0f}"
         else:
-            oracle.select_mass_cap(A, w.mass, w.max_mean_density)
-        t_sel = (time.perf_counter() - t0) * w.kv_heads
-        samples["select"] = f"1 of {w.kv_heads} kv groups, x{w.kv_heads}"
+            A = oracle.pooled_mass(xs["q"][:, :G], xs["k"][:, :1], w.block, w.block)
+            if w.budget == "topk":
+                oracle.select_topk(A, w.keep_frac)
+            else:
+                oracle.select_mass_cap(A, w.mass, w.max_mean_density)
+            t_sel = (time.perf_counter() - t0) * w.kv_heads
+            samples["select"] = f"1 of {w.kv_heads} kv groups, x{w.kv_heads}"
         # sparse step: a few query blocks of one head, gather form
         nqb = -(-L // w.block)
         A1 = oracle.pooled_mass(xs["q"][:, :1], xs["k"][:, :1], w.block, w.block)
@@ -246,6 +261,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="sparsed_64k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--selector", choices=["pooled", "exact"], default="pooled",
+                    help="block workloads: pattern from pooled scores (default) or from the exact block mass of "
+                         "the last dense step")
     ap.add_argument("--probe-interval", type=int, default=None,
                     help="adaptive anchors (block workloads): probe the pattern every N steps after the selection")
     ap.add_argument("--min-overlap", type=float, default=0.9,
@@ -267,8 +285,14 @@ def main():
     import oracle
 
     w0 = get_workload(args.workload)
+    from workloads.configs import scaled
+    if args.selector == "exact":
+        if w0.selector != "blocks" or w0.dense_steps < 1:
+            print("--selector exact needs a block workload with at least one dense step", file=sys.stderr)
+            sys.exit(2)
+        # the exact mass reads the lse of a dense pass: select on the last dense step at the latest
+        w0 = scaled(w0, selector="blocks_exact", refresh_dense=True, select_step=min(w0.select_step, w0.dense_steps - 1))
     if args.probe_interval is not None:
-        from workloads.configs import scaled
         w0 = scaled(w0, probe_interval=args.probe_interval, min_overlap=args.min_overlap)
     K = args.steps if args.steps is not None else w0.total_steps
     w = rescaled(w0, K)
@@ -339,7 +363,7 @@ def main():
     # pattern size for the kept-FLOP count
     L, H, Hkv, d = w.seq_len, w.q_heads, w.kv_heads, w.head_dim
     kept_flops = None
-    if w.selector == "blocks":
+    if w.selector != "columns":
         rp_ptr, ci_ptr, cap = sd.sdattn_schedule_mask(h)
         rows = w.batch * H * (-(-L // w.block))
         last = torch.empty(1, dtype=torch.int32, device="cuda")
@@ -407,7 +431,7 @@ def main():
     share_sparse = n_sparse * (sparse_launch_ms or 0)
     share_dense = n_dense * dense_launch_ms
     kernels = {
-        "flash_fwd_bf16_sparse" if w.selector == "blocks" else "flash_fwd_bf16_column": {
+        "flash_fwd_bf16_sparse" if w.selector != "columns" else "flash_fwd_bf16_column": {
             "bound": "mfma", "achieved": round(sparse_tflops, 1) if sparse_tflops else None, "peak": peak,
             "unit": "TFLOP/s", "frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
             "launch_ms": round(sparse_launch_ms, 4) if sparse_launch_ms else None,
@@ -444,9 +468,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w0.name, "batch": w.batch, "q_heads": H, "kv_heads": Hkv, "seq_len": L,
                    "head_dim": d, "block": w.block,
-                   "selector": w.selector, "budget": (f"top-{w.keep_frac:g}" if w.budget == "topk" and w.selector == "blocks"
+                   "selector": w.selector, "budget": (f"top-{w.keep_frac:g}" if w.budget == "topk" and w.selector != "columns"
                                                       else f"mass {w.mass:g} cap {w.max_mean_density:g}"
-                                                      if w.selector == "blocks" else f"columns {w.column_keep_frac:g}"),
+                                                      if w.selector != "columns" else f"columns {w.column_keep_frac:g}"),
                    "schedule": {a: acts.count(a) for a in sorted(set(acts))}},
         "roofline": roof,
         "phases": {"dense_step_ms": round(dense_ms, 3) if dense_ms else None,

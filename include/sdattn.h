@@ -16,6 +16,8 @@
  *     column-summed attention at an early step, refreshed at a few
  *     intermediate steps (PulseCol, Abstract): sdattn_select_columns and
  *     sdattn_forward_column_sparse.
+ *   - The block pattern can also come from the exact attention mass of each
+ *     block pair after a dense step (sdattn_select_blocks_exact).
  *   - A host-side schedule handle runs warm-up, reuse and refresh, and can
  *     probe the pattern between anchors and refresh it when it has moved
  *     (sdattn_mask_overlap).
@@ -168,6 +170,31 @@ SDATTN_API sdattn_status sdattn_select_blocks(const sdattn_problem* p, const voi
                                    float* block_mass, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Exact block mass, the alternative to pooled scores (SparseD, abstract:
+ * head-specific patterns of where attention goes; Step-dLLM, Abstract: heads
+ * concentrate their attention mass to different extents).  The mass of key
+ * block J for query block I of head h is the attention that block's queries
+ * actually give to its keys:
+ *   A[b][h][I][J] = (1/|I|) sum_{i in I} sum_{j in J} exp(scale q_i.k_j - lse_i),
+ * with lse [B][Hq][L] the log-sum-exp of the full attention of the same q, k
+ * (sdattn_forward_dense), so every row of A sums to 1.  The budget and the
+ * output are those of sdattn_select_blocks, with A in place of the pooled
+ * mass.  Workspace bytes and max_nnz from
+ * sdattn_select_blocks_exact_workspace (host only); block_mass (optional)
+ * receives A.  The scores are exact softmax probabilities (bf16 inputs: MFMA
+ * with fp32 accumulation), summed in fp32; selection is made in fp32 as in
+ * sdattn_select_blocks.  Cost: one pass of Q K^T over all (i, j).
+ */
+SDATTN_API sdattn_status sdattn_select_blocks_exact_workspace(const sdattn_problem* p, int32_t block_q,
+                                                   int32_t block_k, const sdattn_budget* budget,
+                                                   size_t* ws_bytes, int64_t* max_nnz);
+SDATTN_API sdattn_status sdattn_select_blocks_exact(const sdattn_problem* p, const void* q, const void* k,
+                                         const float* lse, int32_t block_q, int32_t block_k,
+                                         const sdattn_budget* budget, int32_t* row_ptr,
+                                         int32_t* col_idx, int64_t col_capacity, float* block_mass,
+                                         void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Block-sparse attention (Step-dLLM, Abstract: block-sparse attention with a
  * reused mask).  Query block I of head h attends only the key tokens of the
  * key blocks listed in its CSR row; an empty row gives o = 0 and
@@ -224,7 +251,12 @@ SDATTN_API sdattn_status sdattn_forward_column_sparse(const sdattn_problem* p, c
 /* Host-side step-schedule driver.                                          */
 /* ------------------------------------------------------------------------ */
 
-typedef enum { SDATTN_SEL_BLOCKS = 0, SDATTN_SEL_COLUMNS = 1 } sdattn_sel_kind;
+typedef enum {
+    SDATTN_SEL_BLOCKS = 0,        /* block pattern from pooled scores           */
+    SDATTN_SEL_COLUMNS = 1,       /* column pattern from column sums (dense lse) */
+    SDATTN_SEL_BLOCKS_EXACT = 2   /* block pattern from the exact block mass
+                                     (dense lse; sdattn_select_blocks_exact)  */
+} sdattn_sel_kind;
 
 typedef enum {
     SDATTN_ACT_DENSE = 0,         /* dense attention                          */
@@ -244,9 +276,10 @@ typedef enum {
  * Step t in S is DENSE_SELECT if t < dense_steps or (refresh_dense and
  * t > select_step), else SELECT_SPARSE.  Step t not in S is DENSE if
  * t < dense_steps, else SPARSE.  Requires select_step <= dense_steps.
- * Columns (sel = SDATTN_SEL_COLUMNS) need refresh_dense = 1, because the
- * column scores use the dense pass's lse; kcol = max(1, ceil(
- * column_keep_frac * L - 1e-9)).  A new pattern applies from the step that
+ * Columns (sel = SDATTN_SEL_COLUMNS) and exact block mass
+ * (SDATTN_SEL_BLOCKS_EXACT) need refresh_dense = 1 and select_step <
+ * dense_steps, because their scores use the dense pass's lse; kcol = max(1,
+ * ceil(column_keep_frac * L - 1e-9)).  A new pattern applies from the step that
  * builds it (SELECT_SPARSE) or from the next step (DENSE_SELECT).
  *
  * Adaptive anchors (blocks only; Step-dLLM, Abstract: attention patterns
@@ -272,8 +305,8 @@ typedef struct {
     int32_t n_refresh_steps;
     int32_t refresh_dense;
     sdattn_sel_kind sel;
-    int32_t block_q, block_k;       /* blocks only */
-    sdattn_budget budget;           /* blocks only */
+    int32_t block_q, block_k;       /* blocks (pooled or exact) only */
+    sdattn_budget budget;           /* blocks (pooled or exact) only */
     double column_keep_frac;        /* columns only */
     int32_t probe_interval;         /* 0 = no probes; blocks only (ABI 2) */
     double min_overlap;             /* adoption threshold of a probe (ABI 2) */

@@ -13,8 +13,9 @@ Modules
   attention : dense, token-masked, block-sparse and column-sparse softmax
               attention (the definition, with its log-sum-exp).
   select    : block mean-pooling, pooled scores and their softmax mass,
-              top-k and mass-with-global-cap block selection to CSR,
-              exact column scores and column top-k.
+              the exact block mass from the full attention, top-k and
+              mass-with-global-cap block selection to CSR, exact column
+              scores and column top-k.
   schedule  : the per-step action table (warm-up, selection, reuse, refresh,
               probes), the overlap of two block patterns and the probe's
               adoption rule, and a whole-schedule runner for small shapes.
@@ -38,6 +39,7 @@ from .attention import (  # noqa: F401
 from .select import (  # noqa: F401
     column_scores,
     count_from_fraction,
+    exact_block_mass,
     pool_blocks,
     pooled_mass,
     pooled_scores,

@@ -32,6 +32,7 @@ from .attention import block_sparse_attention, column_sparse_attention, dense_at
 from .select import (
     column_scores,
     count_from_fraction,
+    exact_block_mass,
     pooled_mass,
     select_columns,
     select_mass_cap,
@@ -98,7 +99,8 @@ def run_schedule(w, step_inputs, steps=None):
 
     step_inputs(t) -> dict(q, k, v) for step t.  Returns a list, per step, of
     dict(action, o, lse, pattern) where pattern is (row_ptr, col_idx) for
-    blocks or col_idx for columns (the pattern in force after the step); a
+    blocks (pooled or exact) or col_idx for columns (the pattern in force
+    after the step; a DENSE_SELECT step's pattern applies from the next); a
     probe step also gives the probe's counts (|A n B|, |A|, |B|) and whether
     it was adopted.
     """
@@ -113,7 +115,21 @@ def run_schedule(w, step_inputs, steps=None):
         q, k, v = x["q"], x["k"], x["v"]
         o = lse = None
         probe = None
-        if w.selector == "blocks":
+        if w.selector == "blocks_exact":
+            # the exact block mass needs the dense pass's log-sum-exp: every
+            # selection step is dense; the pattern applies from the next step
+            if a in ("DENSE", "DENSE_SELECT"):
+                o, lse = dense_attention(q, k, v)
+                if a == "DENSE_SELECT":
+                    A = exact_block_mass(q, k, lse, w.block, w.block)
+                    if w.budget == "topk":
+                        pattern = select_topk(A, w.keep_frac)
+                    else:
+                        rp, ci, _ = select_mass_cap(A, w.mass, w.max_mean_density)
+                        pattern = (rp, ci)
+            else:
+                o, lse = block_sparse_attention(q, k, v, pattern[0], pattern[1], w.block, w.block)
+        elif w.selector == "blocks":
             if a in ("DENSE_SELECT", "SELECT_SPARSE", "PROBE_SPARSE"):
                 A = pooled_mass(q, k, w.block, w.block)
                 if w.budget == "topk":

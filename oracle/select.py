@@ -168,6 +168,31 @@ def column_scores(q, k, lse, scale=None) -> np.ndarray:
     return C
 
 
+def exact_block_mass(q, k, lse, block_q: int, block_k: int, scale=None) -> np.ndarray:
+    """Exact attention mass of each block pair: the mean over the queries of
+    query block I of the probability they give to the keys of key block J,
+    A[b, h, I, J] = (1/|I|) sum_{i in I} sum_{j in J} exp(scale <q_i, k_j> - lse_i),
+    with lse the log-sum-exp of the full attention rows.  [B, Hq, nQB, nKB].
+    (The other reading of a block's attention mass beside the pooled one:
+    SparseD, abstract; Step-dLLM, Abstract.)"""
+    q, k = as_f64(q), as_f64(k)
+    lse = np.asarray(lse, dtype=np.float64)
+    B, Hq, L, d = q.shape
+    Lk = k.shape[2]
+    grp = head_group(Hq, k.shape[1])
+    scale = default_scale(d) if scale is None else scale
+    nqb, nkb = -(-L // block_q), -(-Lk // block_k)
+    A = np.zeros((B, Hq, nqb, nkb))
+    for b in range(B):
+        for h in range(Hq):
+            for I in range(nqb):
+                rows = slice(I * block_q, min(L, (I + 1) * block_q))
+                P = np.exp(scale * (q[b, h, rows] @ k[b, grp[h]].T) - lse[b, h, rows, None])
+                for J in range(nkb):
+                    A[b, h, I, J] = P[:, J * block_k:(J + 1) * block_k].sum() / P.shape[0]
+    return A
+
+
 def select_columns(C: np.ndarray, kcol: int) -> np.ndarray:
     """Top-kcol columns per (b, g) by (C desc, j asc), listed ascending.  [B, Hkv, kcol]."""
     B, Hkv, L = C.shape

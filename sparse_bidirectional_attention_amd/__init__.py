@@ -23,7 +23,8 @@ STATUS_NAMES = ["SDATTN_OK", "SDATTN_ERR_NULL", "SDATTN_ERR_SHAPE", "SDATTN_ERR_
                 "SDATTN_ERR_STATE"]
 SDATTN_F32, SDATTN_BF16 = 0, 1
 SDATTN_BUDGET_TOPK, SDATTN_BUDGET_MASS = 0, 1
-SDATTN_SEL_BLOCKS, SDATTN_SEL_COLUMNS = 0, 1
+SDATTN_SEL_BLOCKS, SDATTN_SEL_COLUMNS, SDATTN_SEL_BLOCKS_EXACT = 0, 1, 2
+SEL_KINDS = {"blocks": SDATTN_SEL_BLOCKS, "columns": SDATTN_SEL_COLUMNS, "blocks_exact": SDATTN_SEL_BLOCKS_EXACT}
 ACTIONS = ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE", "PROBE_SPARSE")
 
 
@@ -66,6 +67,12 @@ _SIGS = {
     "sdattn_select_blocks": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(Budget), _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t,
                                             _P]),
+    "sdattn_select_blocks_exact_workspace": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32,
+                                                            ctypes.POINTER(Budget), ctypes.POINTER(ctypes.c_size_t),
+                                                            ctypes.POINTER(ctypes.c_int64)]),
+    "sdattn_select_blocks_exact": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.POINTER(Budget), _P, _P, ctypes.c_int64, _P, _P,
+                                                  ctypes.c_size_t, _P]),
     "sdattn_forward_block_sparse": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32,
                                                    ctypes.c_int32, _P, _P, _P, _P, _P]),
     "sdattn_select_columns_workspace": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32,
@@ -201,6 +208,27 @@ def sdattn_select_blocks(p, q, k, block_q, block_k, budget, row_ptr, col_idx, co
     _check(lib().sdattn_select_blocks(ctypes.byref(p), _ptr(q), _ptr(k), block_q, block_k, ctypes.byref(budget),
                                       _ptr(row_ptr), _ptr(col_idx), col_capacity, _ptr(block_mass), _ptr(ws),
                                       ws_bytes, _stream(stream)), "sdattn_select_blocks")
+
+
+def sdattn_select_blocks_exact_workspace(p, block_q, block_k, budget):
+    ws = ctypes.c_size_t(0)
+    nnz = ctypes.c_int64(0)
+    _check(lib().sdattn_select_blocks_exact_workspace(ctypes.byref(p), block_q, block_k, ctypes.byref(budget),
+                                                      ctypes.byref(ws), ctypes.byref(nnz)),
+           "sdattn_select_blocks_exact_workspace")
+    return ws.value, nnz.value
+
+
+def sdattn_select_blocks_exact(p, q, k, lse, block_q, block_k, budget, row_ptr, col_idx, col_capacity=None,
+                               block_mass=None, ws=None, ws_bytes=None, stream=None):
+    if col_capacity is None:
+        col_capacity = col_idx.numel()
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sdattn_select_blocks_exact(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(lse), block_q, block_k,
+                                            ctypes.byref(budget), _ptr(row_ptr), _ptr(col_idx), col_capacity,
+                                            _ptr(block_mass), _ptr(ws), ws_bytes, _stream(stream)),
+           "sdattn_select_blocks_exact")
 
 
 def sdattn_forward_block_sparse(p, q, k, v, block_q, block_k, row_ptr, col_idx, o, lse=None, stream=None):

@@ -7,6 +7,7 @@
 #include <string>
 
 #include "host_common.h"
+#include "exact.h"
 #include "launch.h"
 #include "probe.h"
 #include "schedule.h"
@@ -99,6 +100,69 @@ sdattn_status sdattn_select_blocks(const sdattn_problem* p, const void* q, const
                                         plan.cap_extra, row_ptr, col_idx, block_mass, ws,
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "sdattn_select_blocks");
+    return SDATTN_OK;
+}
+
+namespace {
+
+// workspace of the exact selector: the selection stages' layout, then the
+// mass matrix [rows][nKB] fp32
+size_t exact_mass_offset(const Problem& pr, int32_t block_q, int32_t block_k, bool mass) {
+    return (select_blocks_ws_layout(shape_of(pr), block_q, block_k, mass).total + 255) & ~static_cast<size_t>(255);
+}
+size_t exact_ws_bytes(const Problem& pr, int32_t block_q, int32_t block_k, const BlockPlan& plan) {
+    return exact_mass_offset(pr, block_q, block_k, plan.mass) + static_cast<size_t>(plan.rows) * plan.nkb * 4;
+}
+
+}  // namespace
+
+sdattn_status sdattn_select_blocks_exact_workspace(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                                   const sdattn_budget* budget, size_t* ws_bytes, int64_t* max_nnz) {
+    if (ws_bytes == nullptr || max_nnz == nullptr) return fail(SDATTN_ERR_NULL, "ws_bytes and max_nnz must be non-NULL");
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    BlockPlan plan;
+    s = check_blocks(pr, block_q, block_k, budget, &plan);
+    if (s != SDATTN_OK) return s;
+    *ws_bytes = pr.L == 0 ? 0 : exact_ws_bytes(pr, block_q, block_k, plan);
+    *max_nnz = plan.max_nnz;
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_select_blocks_exact(const sdattn_problem* p, const void* q, const void* k, const float* lse,
+                                         int32_t block_q, int32_t block_k, const sdattn_budget* budget,
+                                         int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity, float* block_mass,
+                                         void* ws, size_t ws_bytes, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    BlockPlan plan;
+    s = check_blocks(pr, block_q, block_k, budget, &plan);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (q == nullptr || k == nullptr || lse == nullptr || row_ptr == nullptr || col_idx == nullptr)
+        return fail(SDATTN_ERR_NULL, "q, k, lse, row_ptr and col_idx must be non-NULL");
+    if (col_capacity < plan.max_nnz) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "col_capacity %lld < worst-case kept blocks %lld", static_cast<long long>(col_capacity),
+                 static_cast<long long>(plan.max_nnz));
+        return fail(SDATTN_ERR_CAPACITY, buf);
+    }
+    const size_t need = exact_ws_bytes(pr, block_q, block_k, plan);
+    if (ws_bytes < need || ws == nullptr) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "workspace of %zu bytes < required %zu", ws_bytes, need);
+        return fail(SDATTN_ERR_WORKSPACE, buf);
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    float* mass = reinterpret_cast<float*>(static_cast<char*>(ws) + exact_mass_offset(pr, block_q, block_k, plan.mass));
+    hipError_t e = launch_exact_block_mass(shape_of(pr), pr.dtype == SDATTN_BF16, q, k, lse, block_q, block_k, mass, st);
+    if (e == hipSuccess)
+        e = launch_select_blocks_from_mass(shape_of(pr), mass, block_q, block_k, plan.mass, static_cast<int>(plan.topk),
+                                           static_cast<float>(budget->mass), plan.cap_extra, row_ptr, col_idx,
+                                           block_mass, ws, st);
+    if (e != hipSuccess) return hip_fail(e, "sdattn_select_blocks_exact");
     return SDATTN_OK;
 }
 
@@ -252,9 +316,20 @@ sdattn_status be_probe_read(void*, const void* state, int64_t out[4], void* st) 
     return SDATTN_OK;
 }
 
+sdattn_status be_select_blocks_exact(void*, const sdattn_problem* p, const void* q, const void* k, const float* lse,
+                                     int32_t bq, int32_t bk, const sdattn_budget* b, int32_t* rp, int32_t* ci,
+                                     int64_t cap, void* ws, size_t wsb, void* st) {
+    return sdattn_select_blocks_exact(p, q, k, lse, bq, bk, b, rp, ci, cap, nullptr, ws, wsb, st);
+}
+sdattn_status be_ws_blocks_exact(void*, const sdattn_problem* p, int32_t bq, int32_t bk, const sdattn_budget* b,
+                                 size_t* ws, int64_t* nnz) {
+    return sdattn_select_blocks_exact_workspace(p, bq, bk, b, ws, nnz);
+}
+
 const Backend kHipBackend = {nullptr,          be_dense,       be_select_blocks, be_block_sparse, be_select_columns,
                              be_column_sparse, be_ws_blocks,   be_ws_columns,    be_alloc,        be_release,
-                             be_overlap,       be_probe_adopt, be_probe_init,    be_probe_read};
+                             be_overlap,       be_probe_adopt, be_probe_init,    be_probe_read,   be_select_blocks_exact,
+                             be_ws_blocks_exact};
 
 }  // namespace
 

@@ -19,7 +19,7 @@ namespace sdattn {
 namespace {
 
 constexpr int kOvWaves = 4;        // waves per workgroup
-constexpr int kOvRowsPerWave = 4;  // rows per wave
+constexpr int kOvRowsPerWave = 1;  // rows per wave (each row is a chain of dependent loads)
 
 __global__ void overlap_zero_kernel(int64_t* counts) {
     if (threadIdx.x < 3) counts[threadIdx.x] = 0;

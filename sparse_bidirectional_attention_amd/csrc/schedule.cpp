@@ -74,8 +74,17 @@ sdattn_status check_desc(const Problem& pr, const sdattn_schedule_desc* d) {
     if (d->refresh_interval < 0) return fail(SDATTN_ERR_SHAPE, "refresh_interval must be >= 0");
     if (d->n_refresh_steps < 0 || (d->n_refresh_steps > 0 && d->refresh_steps == nullptr))
         return fail(SDATTN_ERR_NULL, "refresh_steps is NULL but n_refresh_steps > 0");
-    if (d->sel != SDATTN_SEL_BLOCKS && d->sel != SDATTN_SEL_COLUMNS)
+    if (d->sel != SDATTN_SEL_BLOCKS && d->sel != SDATTN_SEL_COLUMNS && d->sel != SDATTN_SEL_BLOCKS_EXACT)
         return fail(SDATTN_ERR_SHAPE, "unknown selector kind");
+    if (d->sel == SDATTN_SEL_BLOCKS_EXACT) {
+        // the exact block mass uses the lse of a dense pass of the same step
+        if (!d->refresh_dense)
+            return fail(SDATTN_ERR_SHAPE, "exact block selection needs refresh_dense = 1 (the mass uses the dense lse)");
+        if (d->select_step >= d->dense_steps)
+            return fail(SDATTN_ERR_SHAPE, "exact block selection step must be a dense step (select_step < dense_steps)");
+        if (d->probe_interval != 0)
+            return fail(SDATTN_ERR_UNSUPPORTED, "probes use the pooled selector (exact selection needs a dense pass)");
+    }
     if (d->sel == SDATTN_SEL_COLUMNS) {
         if (!d->refresh_dense)
             return fail(SDATTN_ERR_SHAPE, "column selection needs refresh_dense = 1 (scores use the dense lse)");
@@ -125,13 +134,20 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         return e;
     };
     size_t rp_bytes = 0, ci_bytes = 0;
-    if (desc->sel == SDATTN_SEL_BLOCKS) {
+    const size_t lse_bytes = static_cast<size_t>(pr.B) * pr.Hq * std::max(pr.L, 1) * sizeof(float);
+    if (desc->sel == SDATTN_SEL_BLOCKS || desc->sel == SDATTN_SEL_BLOCKS_EXACT) {
+        const bool exact = desc->sel == SDATTN_SEL_BLOCKS_EXACT;
         BlockPlan plan;
         st = check_blocks(pr, desc->block_q, desc->block_k, &desc->budget, &plan);
         if (st != SDATTN_OK) return cleanup_fail(st);
         int64_t max_nnz = 0;
-        st = s->be.workspace_blocks(s->be.ctx, p, desc->block_q, desc->block_k, &desc->budget, &s->ws_bytes, &max_nnz);
+        st = (exact ? s->be.workspace_blocks_exact : s->be.workspace_blocks)(s->be.ctx, p, desc->block_q, desc->block_k,
+                                                                              &desc->budget, &s->ws_bytes, &max_nnz);
         if (st != SDATTN_OK) return cleanup_fail(st);
+        if (exact) {  // own lse buffer for steps run with lse = NULL
+            st = s->be.alloc(s->be.ctx, lse_bytes, reinterpret_cast<void**>(&s->lse));
+            if (st != SDATTN_OK) return cleanup_fail(st);
+        }
         s->nnz_cap = std::max<int64_t>(max_nnz, 1);
         s->rows = plan.rows;
         rp_bytes = static_cast<size_t>(plan.rows + 1) * sizeof(int32_t);
@@ -142,7 +158,6 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         if (st != SDATTN_OK) return cleanup_fail(st);
         s->nnz_cap = static_cast<int64_t>(pr.B) * pr.Hkv * s->kcol;
         ci_bytes = static_cast<size_t>(std::max<int64_t>(s->nnz_cap, 1)) * sizeof(int32_t);
-        const size_t lse_bytes = static_cast<size_t>(pr.B) * pr.Hq * std::max(pr.L, 1) * sizeof(float);
         st = s->be.alloc(s->be.ctx, lse_bytes, reinterpret_cast<void**>(&s->lse));
         if (st != SDATTN_OK) return cleanup_fail(st);
     }
@@ -182,7 +197,7 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
     const sdattn_action act = schedule_action_of(s->desc, step);
     const Backend& be = s->be;
     const sdattn_problem* p = &s->prob;
-    const bool blocks = s->desc.sel == SDATTN_SEL_BLOCKS;
+    const bool blocks = s->desc.sel != SDATTN_SEL_COLUMNS;  // pooled or exact block pattern
     const int next = s->active < 0 ? 0 : 1 - s->active;
     sdattn_status st = SDATTN_OK;
     switch (act) {
@@ -190,7 +205,14 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
             st = be.dense(be.ctx, p, q, k, v, o, lse, stream);
             break;
         case SDATTN_ACT_DENSE_SELECT:
-            if (blocks) {
+            if (s->desc.sel == SDATTN_SEL_BLOCKS_EXACT) {
+                float* l = lse != nullptr ? lse : s->lse;
+                st = be.dense(be.ctx, p, q, k, v, o, l, stream);
+                if (st == SDATTN_OK)
+                    st = be.select_blocks_exact(be.ctx, p, q, k, l, s->desc.block_q, s->desc.block_k, &s->desc.budget,
+                                                s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes,
+                                                stream);
+            } else if (blocks) {
                 st = be.dense(be.ctx, p, q, k, v, o, lse, stream);
                 if (st == SDATTN_OK)
                     st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
@@ -207,7 +229,8 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
             }
             break;
         case SDATTN_ACT_SELECT_SPARSE:
-            if (!blocks) return fail(SDATTN_ERR_STATE, "column selection needs a dense step");
+            if (s->desc.sel != SDATTN_SEL_BLOCKS)
+                return fail(SDATTN_ERR_STATE, "this selection needs a dense step (it uses the dense lse)");
             st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
                                   s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
             if (st == SDATTN_OK)

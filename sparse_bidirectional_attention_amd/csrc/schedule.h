@@ -38,6 +38,13 @@ struct Backend {
                                  int64_t max_copy, void* stream);
     sdattn_status (*probe_init)(void* ctx, void* state);                            // synchronous
     sdattn_status (*probe_read)(void* ctx, const void* state, int64_t out[4], void* stream);  // synchronous
+    // exact block mass selection (uses the dense pass's lse)
+    sdattn_status (*select_blocks_exact)(void* ctx, const sdattn_problem*, const void* q, const void* k,
+                                         const float* lse, int32_t bq, int32_t bk, const sdattn_budget*,
+                                         int32_t* row_ptr, int32_t* col_idx, int64_t cap, void* ws, size_t ws_bytes,
+                                         void* stream);
+    sdattn_status (*workspace_blocks_exact)(void* ctx, const sdattn_problem*, int32_t bq, int32_t bk,
+                                            const sdattn_budget*, size_t* ws, int64_t* max_nnz);
 };
 
 // The backend used by sdattn_schedule_create (defined by the library build

@@ -23,6 +23,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "exact.h"
 #include "launch.h"
 
 namespace sdattn {
@@ -85,6 +86,7 @@ struct ScoreParams {
     float* block_mass;  // nullable
     float* cum;         // [rows][nkb] (mass)
     int32_t* ord;       // [rows][nkb] (mass)
+    const float* mass_in;  // nullable: the rows' mass, given (no pooled scores, no softmax)
 };
 
 // 64-bit shuffle (two 32-bit halves)
@@ -122,6 +124,12 @@ __global__ __launch_bounds__(kSelThreads) void scores_kernel(ScoreParams p) {
     const int g = h / p.group;
     const int nkb = p.nkb;
 
+    if (p.mass_in != nullptr) {
+        // the rows' mass is given
+        for (int e = tid; e < nrows * nkb; e += NT)
+            sc[e / nkb][e % nkb] = p.mass_in[(static_cast<size_t>(bh) * p.nqb + I0) * nkb + e];
+        __syncthreads();
+    } else {
     // pooled scores of the group's rows against every key block (each Kp row read once)
     for (int e = tid; e < nrows * D; e += NT) qs[e / D][e % D] = p.qp[(static_cast<size_t>(bh) * p.nqb + I0) * D + e];
     __syncthreads();
@@ -146,29 +154,39 @@ __global__ __launch_bounds__(kSelThreads) void scores_kernel(ScoreParams p) {
         for (int r = 0; r < kRowsPerGroup; ++r) sc[r][J] = acc[r] * p.scale;
     }
     __syncthreads();
+    }
 
     // one wave per row from here on: no workgroup barriers
     for (int rr = tid >> 6; rr < nrows; rr += NT / 64) {
         const int row = bh * p.nqb + I0 + rr;
-        // softmax over J
+        // softmax over J (pooled scores), or the given mass as it is
         float v[R];
-        float mx = -kInf;
+        float inv = 1.f;
+        if (p.mass_in != nullptr) {
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int J = 64 * k + lane;
-            v[k] = J < nkb ? sc[rr][J] : -kInf;
-            mx = fmaxf(mx, v[k]);
-        }
-        mx = wave_max(mx);
-        float sm = 0.f;
+            for (int k = 0; k < R; ++k) {
+                const int J = 64 * k + lane;
+                v[k] = J < nkb ? sc[rr][J] : 0.f;
+            }
+        } else {
+            float mx = -kInf;
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int J = 64 * k + lane;
-            v[k] = J < nkb ? expf(v[k] - mx) : 0.f;
-            sm += v[k];
+            for (int k = 0; k < R; ++k) {
+                const int J = 64 * k + lane;
+                v[k] = J < nkb ? sc[rr][J] : -kInf;
+                mx = fmaxf(mx, v[k]);
+            }
+            mx = wave_max(mx);
+            float sm = 0.f;
+#pragma unroll
+            for (int k = 0; k < R; ++k) {
+                const int J = 64 * k + lane;
+                v[k] = J < nkb ? expf(v[k] - mx) : 0.f;
+                sm += v[k];
+            }
+            sm = wave_sum(sm);
+            inv = 1.f / sm;
         }
-        sm = wave_sum(sm);
-        const float inv = 1.f / sm;
         // key = mass bits << 32 | ~J: descending order is mass desc, then J asc
         uint64_t key[R];
 #pragma unroll
@@ -420,44 +438,23 @@ BlockSelectWs select_blocks_ws_layout(const AttnShape& s, int block_q, int block
     return w;
 }
 
-hipError_t launch_select_blocks(const AttnShape& s, bool bf16, const void* q, const void* k,
-                                int block_q, int block_k, bool mass, int topk, float mass_target,
-                                long long cap_extra, int32_t* row_ptr, int32_t* col_idx,
-                                float* block_mass, void* ws, hipStream_t st) {
+namespace {
+
+// Per row: the pooled scores and their softmax, or the given mass; the sort;
+// the top-k CSR or the cumulative mass.  Then, for the capped mass budget, the
+// global threshold and the CSR.
+hipError_t select_stages(const AttnShape& s, const float* qp, const float* kp, const float* mass_in, int block_q,
+                         int block_k, bool mass, int topk, float mass_target, long long cap_extra, int32_t* row_ptr,
+                         int32_t* col_idx, float* block_mass, void* ws, hipStream_t st) {
     const int nqb = (s.L + block_q - 1) / block_q, nkb = (s.L + block_k - 1) / block_k;
     const long long rows = static_cast<long long>(s.B) * s.Hq * nqb;
-    if (rows == 0) return hipSuccess;
     const BlockSelectWs w = select_blocks_ws_layout(s, block_q, block_k, mass);
     char* wsb = static_cast<char*>(ws);
-    float* qp = reinterpret_cast<float*>(wsb + w.qp_off);
-    float* kp = reinterpret_cast<float*>(wsb + w.kp_off);
-
-    // 1. pooling
-    const unsigned gq = static_cast<unsigned>(rows), gk = static_cast<unsigned>(s.B * s.Hkv * nkb);
-    if (bf16) {
-        if (s.D == 128) {
-            hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), dim3(gq), dim3(256), 0, st, static_cast<const uint16_t*>(q), qp, s.L, block_q, nqb);
-            hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), dim3(gk), dim3(256), 0, st, static_cast<const uint16_t*>(k), kp, s.L, block_k, nkb);
-        } else {
-            hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), dim3(gq), dim3(256), 0, st, static_cast<const uint16_t*>(q), qp, s.L, block_q, nqb);
-            hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), dim3(gk), dim3(256), 0, st, static_cast<const uint16_t*>(k), kp, s.L, block_k, nkb);
-        }
-    } else {
-        if (s.D == 128) {
-            hipLaunchKernelGGL((pool_kernel<float, 128>), dim3(gq), dim3(256), 0, st, static_cast<const float*>(q), qp, s.L, block_q, nqb);
-            hipLaunchKernelGGL((pool_kernel<float, 128>), dim3(gk), dim3(256), 0, st, static_cast<const float*>(k), kp, s.L, block_k, nkb);
-        } else {
-            hipLaunchKernelGGL((pool_kernel<float, 64>), dim3(gq), dim3(256), 0, st, static_cast<const float*>(q), qp, s.L, block_q, nqb);
-            hipLaunchKernelGGL((pool_kernel<float, 64>), dim3(gk), dim3(256), 0, st, static_cast<const float*>(k), kp, s.L, block_k, nkb);
-        }
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    // 2. pooled scores, softmax, sort, top-k CSR or cumulative mass
+    hipError_t e;
     ScoreParams sp{};
     sp.qp = qp;
     sp.kp = kp;
+    sp.mass_in = mass_in;
     sp.Hq = s.Hq;
     sp.Hkv = s.Hkv;
     sp.group = s.Hq / s.Hkv;
@@ -510,6 +507,56 @@ hipError_t launch_select_blocks(const AttnShape& s, bool bf16, const void* q, co
     hipLaunchKernelGGL(rows_scan_kernel, dim3(1), dim3(1024), 0, st, cnt, static_cast<int>(rows), row_ptr);
     hipLaunchKernelGGL(mass_write_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, st, sp.ord, cnt, row_ptr, nkb, col_idx);
     return hipGetLastError();
+}
+
+
+}  // namespace
+
+hipError_t launch_select_blocks(const AttnShape& s, bool bf16, const void* q, const void* k,
+                                int block_q, int block_k, bool mass, int topk, float mass_target,
+                                long long cap_extra, int32_t* row_ptr, int32_t* col_idx,
+                                float* block_mass, void* ws, hipStream_t st) {
+    const int nqb = (s.L + block_q - 1) / block_q, nkb = (s.L + block_k - 1) / block_k;
+    const long long rows = static_cast<long long>(s.B) * s.Hq * nqb;
+    if (rows == 0) return hipSuccess;
+    const BlockSelectWs w = select_blocks_ws_layout(s, block_q, block_k, mass);
+    char* wsb = static_cast<char*>(ws);
+    float* qp = reinterpret_cast<float*>(wsb + w.qp_off);
+    float* kp = reinterpret_cast<float*>(wsb + w.kp_off);
+
+    // 1. pooling
+    const unsigned gq = static_cast<unsigned>(rows), gk = static_cast<unsigned>(s.B * s.Hkv * nkb);
+    if (bf16) {
+        if (s.D == 128) {
+            hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), dim3(gq), dim3(256), 0, st, static_cast<const uint16_t*>(q), qp, s.L, block_q, nqb);
+            hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), dim3(gk), dim3(256), 0, st, static_cast<const uint16_t*>(k), kp, s.L, block_k, nkb);
+        } else {
+            hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), dim3(gq), dim3(256), 0, st, static_cast<const uint16_t*>(q), qp, s.L, block_q, nqb);
+            hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), dim3(gk), dim3(256), 0, st, static_cast<const uint16_t*>(k), kp, s.L, block_k, nkb);
+        }
+    } else {
+        if (s.D == 128) {
+            hipLaunchKernelGGL((pool_kernel<float, 128>), dim3(gq), dim3(256), 0, st, static_cast<const float*>(q), qp, s.L, block_q, nqb);
+            hipLaunchKernelGGL((pool_kernel<float, 128>), dim3(gk), dim3(256), 0, st, static_cast<const float*>(k), kp, s.L, block_k, nkb);
+        } else {
+            hipLaunchKernelGGL((pool_kernel<float, 64>), dim3(gq), dim3(256), 0, st, static_cast<const float*>(q), qp, s.L, block_q, nqb);
+            hipLaunchKernelGGL((pool_kernel<float, 64>), dim3(gk), dim3(256), 0, st, static_cast<const float*>(k), kp, s.L, block_k, nkb);
+        }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return select_stages(s, qp, kp, nullptr, block_q, block_k, mass, topk, mass_target, cap_extra, row_ptr, col_idx,
+                         block_mass, ws, st);
+}
+
+hipError_t launch_select_blocks_from_mass(const AttnShape& s, const float* mass_in, int block_q, int block_k,
+                                          bool mass, int topk, float mass_target, long long cap_extra,
+                                          int32_t* row_ptr, int32_t* col_idx, float* block_mass, void* ws,
+                                          hipStream_t st) {
+    const int nqb = (s.L + block_q - 1) / block_q;
+    if (static_cast<long long>(s.B) * s.Hq * nqb == 0) return hipSuccess;
+    return select_stages(s, nullptr, nullptr, mass_in, block_q, block_k, mass, topk, mass_target, cap_extra, row_ptr,
+                         col_idx, block_mass, ws, st);
 }
 
 }  // namespace sdattn

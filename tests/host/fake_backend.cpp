@@ -112,9 +112,23 @@ sdattn_status f_probe_read(void*, const void* state, int64_t out[4], void*) {
     return SDATTN_OK;
 }
 
+sdattn_status f_select_blocks_exact(void*, const sdattn_problem*, const void*, const void*, const float* lse,
+                                    int32_t bq, int32_t bk, const sdattn_budget*, int32_t* rp, int32_t* ci,
+                                    int64_t cap, void*, size_t, void*) {
+    return record("select_blocks_exact lse=" + ptr(lse) + " rp=" + ptr(rp) + " ci=" + ptr(ci) +
+                  " cap=" + std::to_string(cap) + " bq=" + std::to_string(bq) + " bk=" + std::to_string(bk));
+}
+sdattn_status f_ws_blocks_exact(void* ctx, const sdattn_problem* p, int32_t bq, int32_t bk, const sdattn_budget* b,
+                                size_t* ws, int64_t* nnz) {
+    const sdattn_status st = f_ws_blocks(ctx, p, bq, bk, b, ws, nnz);
+    *ws += 8192;
+    return st;
+}
+
 const sdattn::Backend kFake = {nullptr,         f_dense,       f_select_blocks, f_block_sparse, f_select_columns,
                                f_column_sparse, f_ws_blocks,   f_ws_columns,    f_alloc,        f_release,
-                               f_overlap,       f_probe_adopt, f_probe_init,    f_probe_read};
+                               f_overlap,       f_probe_adopt, f_probe_init,    f_probe_read,   f_select_blocks_exact,
+                               f_ws_blocks_exact};
 
 }  // namespace
 

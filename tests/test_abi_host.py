@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 20
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
     assert set(names) == exported  # nothing missing, nothing extra
@@ -109,6 +109,22 @@ def test_sparse_and_column_validation():
     assert lib.sdattn_select_columns(ctypes.byref(p), BAD, BAD, BAD, 492, BAD, None, BAD, ws - 8, None) == 5
     with pytest.raises(sd.SdattnError, match="BUDGET"):
         sd.sdattn_select_columns_workspace(p, 0)
+
+
+def test_exact_selection_validation():
+    lib = sd.lib()
+    p = sd.problem(1, 4, 4, 4096, 128, "bf16")
+    b = sd.topk_budget(0.1)
+    ws, nnz = sd.sdattn_select_blocks_exact_workspace(p, 128, 128, b)
+    ws_pooled, nnz_pooled = sd.sdattn_select_blocks_workspace(p, 128, 128, b)
+    assert nnz == nnz_pooled == 4 * 32 * 4 and ws >= ws_pooled + 4 * 32 * 32 * 4
+    sel = lib.sdattn_select_blocks_exact
+    assert sel(ctypes.byref(p), BAD, BAD, None, 128, 128, ctypes.byref(b), BAD, BAD, nnz, None, BAD, ws, None) == 1
+    assert sel(ctypes.byref(p), BAD, BAD, BAD, 128, 128, ctypes.byref(b), BAD, BAD, nnz - 1, None, BAD, ws, None) == 6
+    assert sel(ctypes.byref(p), BAD, BAD, BAD, 128, 128, ctypes.byref(b), BAD, BAD, nnz, None, BAD, ws - 4, None) == 5
+    assert sel(ctypes.byref(p), BAD, BAD, BAD, 96, 128, ctypes.byref(b), BAD, BAD, nnz, None, BAD, ws, None) == 8
+    with pytest.raises(sd.SdattnError, match="BUDGET"):
+        sd.sdattn_select_blocks_exact_workspace(p, 128, 128, sd.topk_budget(0.0))
 
 
 def test_mask_overlap_validation():

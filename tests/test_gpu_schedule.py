@@ -38,7 +38,7 @@ def _d2h(ptr, n, dtype=np.int32):
 
 
 def _desc(w):
-    sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
+    sel = sd.SEL_KINDS[w.selector]
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
                             w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac,

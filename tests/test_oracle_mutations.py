@@ -86,7 +86,7 @@ def pin_probe_steps_hand():
 def test_pins_pass_on_the_real_oracle():
     for pin in (pin_dense_vs_torch, pin_pooling_closed_form, pin_topk_ties_brute_force,
                 pin_mass_exact_hit, pin_column_sum_total, pin_topk_count, pin_overlap_rows_matter,
-                pin_overlap_ratio_hand, pin_adoption_strict, pin_probe_steps_hand):
+                pin_overlap_ratio_hand, pin_adoption_strict, pin_probe_steps_hand, pin_exact_mass_rows):
         pin()
 
 
@@ -196,3 +196,29 @@ def test_probes_counted_from_step_zero_are_caught(monkeypatch):
                 for t, a in enumerate(acts)]
     monkeypatch.setattr(oracle, "schedule_actions", bad)
     _fails(pin_probe_steps_hand)
+
+
+def pin_exact_mass_rows():
+    x = _x(5, L=13)
+    _, lse = oracle.dense_attention(x["q"], x["k"], x["v"])
+    A = oracle.exact_block_mass(x["q"], x["k"], lse, 4, 3)  # partial last blocks on both sides
+    np.testing.assert_allclose(A.sum(-1), 1.0, atol=1e-12)
+
+
+def test_exact_mass_divided_by_the_nominal_block_size_is_caught(monkeypatch):
+    real = osel.exact_block_mass
+
+    def bad(q, k, lse, bq, bk, scale=None):
+        A = real(q, k, lse, bq, bk, scale)
+        L = np.asarray(q).shape[2]
+        n_last = L - (A.shape[2] - 1) * bq
+        A[:, :, -1] *= n_last / bq  # sum over the last block divided by bq, not by its size
+        return A
+    monkeypatch.setattr(oracle, "exact_block_mass", bad)
+    _fails(pin_exact_mass_rows)
+
+
+def test_exact_mass_without_the_lse_is_caught(monkeypatch):
+    monkeypatch.setattr(oracle, "exact_block_mass",
+                        lambda q, k, lse, bq, bk, scale=None: osel.exact_block_mass(q, k, np.zeros_like(lse), bq, bk))
+    _fails(pin_exact_mass_rows)

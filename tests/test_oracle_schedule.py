@@ -170,3 +170,24 @@ def test_probe_schedule_keeps_a_stable_pattern_and_adopts_a_moved_one():
     x5 = inputs(5)
     o, lse = oracle.block_sparse_attention(x5["q"], x5["k"], x5["v"], rp, ci, 64, 64)
     np.testing.assert_allclose(res[5]["o"], o, atol=0)
+
+
+def test_exact_selector_schedule_selects_after_the_dense_pass():
+    """Exact block mass: the selection step runs dense attention, its lse gives
+    the mass, and the pattern applies from the next step."""
+    w = scaled(WORKLOADS["tiny_fp32_h4_l512"], selector="blocks_exact", refresh_dense=True, total_steps=5,
+               dense_steps=2, select_step=1, refresh_interval=2)
+    base = make_base(w)
+    res = oracle.run_schedule(w, lambda t: make_step(w, t, base))
+    assert [r["action"] for r in res] == ["DENSE", "DENSE_SELECT", "SPARSE", "DENSE_SELECT", "SPARSE"]
+    x1 = make_step(w, 1, base)
+    o1, lse1 = oracle.dense_attention(x1["q"], x1["k"], x1["v"])
+    np.testing.assert_allclose(res[1]["o"], o1, atol=0)
+    rp, ci = oracle.select_topk(oracle.exact_block_mass(x1["q"], x1["k"], lse1, 64, 64), 0.25)
+    np.testing.assert_array_equal(res[1]["pattern"][0], rp)
+    np.testing.assert_array_equal(res[1]["pattern"][1], ci)
+    x2 = make_step(w, 2, base)
+    o2, _ = oracle.block_sparse_attention(x2["q"], x2["k"], x2["v"], rp, ci, 64, 64)
+    np.testing.assert_allclose(res[2]["o"], o2, atol=0)
+    # the planted sink is found by the exact mass too
+    assert np.all((ci.reshape(4, 8, 2)[0] == 0).any(-1))

@@ -193,3 +193,49 @@ def test_select_columns_brute_force(seed, ties):
     ci = oracle.select_columns(C, 3)
     for g in range(2):
         assert list(ci[0, g]) == _brute_topk(C[0, g], 3)
+
+
+# ---- exact block mass -----------------------------------------------------------
+
+@pytest.mark.parametrize("L,bq,bk", [(13, 4, 4), (13, 5, 3), (16, 8, 4), (9, 9, 2)])
+def test_exact_block_mass_is_the_block_sum_of_the_probability_matrix(L, bq, bk):
+    """Against torch's attention probabilities (SDPA with V = I), summed over
+    each block pair and divided by the query block's size (partial blocks
+    included); rows sum to 1."""
+    x = {n: v.astype(np.float64) for n, v in tiny_random(40 + L + bq, 1, 4, 2, L, 8).items()}
+    _, lse = oracle.dense_attention(x["q"], x["k"], x["v"])
+    A = oracle.exact_block_mass(x["q"], x["k"], lse, bq, bk)
+    P = _probs_sdpa(x["q"], x["k"])
+    nqb, nkb = -(-L // bq), -(-L // bk)
+    assert A.shape == (1, 4, nqb, nkb)
+    for I in range(nqb):
+        for J in range(nkb):
+            blk = P[0, :, I * bq:(I + 1) * bq, J * bk:(J + 1) * bk]
+            np.testing.assert_allclose(A[0, :, I, J], blk.sum(axis=(1, 2)) / blk.shape[1], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(A.sum(-1), 1.0, atol=1e-13)
+
+
+def test_exact_block_mass_with_one_token_blocks_is_the_probability_matrix():
+    x = {n: v.astype(np.float64) for n, v in tiny_random(50, 1, 4, 2, 11, 8).items()}
+    _, lse = oracle.dense_attention(x["q"], x["k"], x["v"])
+    np.testing.assert_allclose(oracle.exact_block_mass(x["q"], x["k"], lse, 1, 1), _probs_sdpa(x["q"], x["k"]),
+                               atol=1e-13)
+
+
+def test_exact_block_mass_of_one_query_block_is_the_mean_column_mass():
+    # one query block over all rows, one-token key blocks, one head per group:
+    # A[0, j] = C[j] / L with C the column sums
+    x = {n: v.astype(np.float64) for n, v in tiny_random(51, 1, 2, 2, 12, 8).items()}
+    _, lse = oracle.dense_attention(x["q"], x["k"], x["v"])
+    A = oracle.exact_block_mass(x["q"], x["k"], lse, 12, 1)
+    np.testing.assert_allclose(A[0, :, 0], oracle.column_scores(x["q"], x["k"], lse)[0] / 12, rtol=1e-12)
+
+
+def test_exact_block_mass_of_uniform_attention_is_the_key_share():
+    # q = 0: every query attends every key equally, so A[I, J] = |J| / L
+    L, bk = 10, 4
+    q = np.zeros((1, 2, L, 4))
+    k = np.random.default_rng(3).standard_normal((1, 2, L, 4))
+    _, lse = oracle.dense_attention(q, k, k)
+    A = oracle.exact_block_mass(q, k, lse, 3, bk)
+    np.testing.assert_allclose(A, np.broadcast_to(np.array([4, 4, 2]) / L, A.shape), atol=1e-15)

@@ -34,7 +34,7 @@ def fake():
 
 
 def _desc_of(w):
-    sel = sd.SDATTN_SEL_COLUMNS if w.selector == "columns" else sd.SDATTN_SEL_BLOCKS
+    sel = sd.SEL_KINDS[w.selector]
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
                             w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac,
@@ -276,4 +276,50 @@ def test_probe_step_errors_leave_the_pattern_alone(fake):
     assert _step(fake, h, 3) == 0
     assert [l.split()[0] for l in _log(fake)] == ["select_blocks", "overlap", "probe_adopt", "block_sparse"]
     fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def test_exact_selector_schedule_uses_the_dense_lse(fake):
+    w = scaled(WORKLOADS["sparsed_64k"], selector="blocks_exact", refresh_dense=True, total_steps=10, dense_steps=4,
+               select_step=3, refresh_interval=4)
+    d = _desc_of(w)
+    assert d.sel == sd.SDATTN_SEL_BLOCKS_EXACT
+    h = _create(fake, _prob_of(w), d)
+    assert _actions(fake, h, 10) == ["DENSE", "DENSE", "DENSE", "DENSE_SELECT", "SPARSE", "SPARSE", "SPARSE",
+                                     "DENSE_SELECT", "SPARSE", "SPARSE"]
+    fake.sdattn_fake_reset(-1, 0)
+    for t in range(10):
+        assert _step(fake, h, t) == 0  # lse = NULL: the handle's own buffer
+    log = _log(fake)
+    sel = [i for i, l in enumerate(log) if l.startswith("select_blocks_exact")]
+    assert len(sel) == 2 and not any(l.startswith("select_blocks ") for l in log)
+    for i in sel:  # the dense pass right before writes the lse the selection reads
+        assert log[i - 1].startswith("dense")
+        own = re.search(r"lse=(\S+)", log[i - 1]).group(1)
+        assert own != "(nil)" and re.search(r"lse=(\S+)", log[i]).group(1) == own
+        assert "cap=425984" in log[i]
+    # sparse steps use the pattern of the latest selection (applies from the next step)
+    cur = None
+    for l in log:
+        if l.startswith("select_blocks_exact"):
+            cur = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
+        elif l.startswith("block_sparse"):
+            assert re.search(r"rp=(\S+) ci=(\S+)", l).groups() == cur
+    # a caller lse is used when given
+    fake.sdattn_fake_reset(-1, 0)
+    assert _step(fake, h, 3, lse=ctypes.c_void_p(0x7000)) == 0
+    assert all("lse=0x7000" in l for l in _log(fake)[:2])
+    fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
+def test_exact_selector_descriptor_checks(fake):
+    w = scaled(WORKLOADS["sparsed_64k"], selector="blocks_exact", total_steps=10, dense_steps=4, select_step=3,
+               refresh_dense=True)
+    p = _prob_of(w)
+    for kw, want in [(dict(refresh_dense=False), 2), (dict(select_step=4), 2),
+                     (dict(probe_interval=2, min_overlap=0.5), 8)]:
+        d = _desc_of(scaled(w, **kw))
+        h = ctypes.c_void_p(None)
+        assert fake.sdattn_schedule_create(ctypes.byref(p), ctypes.byref(d), ctypes.byref(h)) == want
     assert fake.sdattn_fake_live_allocs() == 0

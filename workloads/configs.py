@@ -37,7 +37,7 @@ class Workload:
     refresh_interval: int = 0     # 0: no periodic refresh
     refresh_steps: Tuple[int, ...] = ()
     refresh_dense: bool = False
-    selector: str = "blocks"      # "blocks" or "columns"
+    selector: str = "blocks"      # "blocks" (pooled), "blocks_exact" (exact block mass) or "columns"
     # budget
     budget: str = "topk"          # "topk" or "mass"
     keep_frac: float = 0.0        # top-k fraction of key blocks per row
