@@ -254,6 +254,48 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
                             "sparse": round(1e3 * t_sparse, 1)}}
 
 
+def compare_masks(sd, p, w, x, o, lse):
+    """The exact and the pooled pattern of the selection step's tensors: their
+    overlap |A n B| / |A u B| (sdattn_mask_overlap) and the share of the exact
+    attention mass each keeps (mean over rows of the kept blocks' exact mass)."""
+    import numpy as np
+    import torch
+    L = w.seq_len
+    nqb, nkb = -(-L // w.block), -(-L // w.block)
+    rows = w.batch * w.q_heads * nqb
+    budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
+    sd.sdattn_forward_dense(p, x["q"], x["k"], x["v"], o, lse)
+    out = {}
+    masks = {}
+    A = torch.empty(rows * nkb, dtype=torch.float32, device="cuda")
+    for kind in ("exact", "pooled"):
+        if kind == "exact":
+            wsb, cap = sd.sdattn_select_blocks_exact_workspace(p, w.block, w.block, budget)
+        else:
+            wsb, cap = sd.sdattn_select_blocks_workspace(p, w.block, w.block, budget)
+        rp = torch.empty(rows + 1, dtype=torch.int32, device="cuda")
+        ci = torch.empty(max(cap, 1), dtype=torch.int32, device="cuda")
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        if kind == "exact":
+            sd.sdattn_select_blocks_exact(p, x["q"], x["k"], lse, w.block, w.block, budget, rp, ci, cap, A, ws, wsb)
+        else:
+            sd.sdattn_select_blocks(p, x["q"], x["k"], w.block, w.block, budget, rp, ci, cap, None, ws, wsb)
+        masks[kind] = (rp, ci)
+    counts = torch.empty(3, dtype=torch.int64, device="cuda")
+    sd.sdattn_mask_overlap(rows, masks["exact"][0], masks["exact"][1], masks["pooled"][0], masks["pooled"][1], counts)
+    torch.cuda.synchronize()
+    inter, na, nb = (int(v) for v in counts.cpu())
+    out["overlap_exact_vs_pooled"] = round(inter / max(1, na + nb - inter), 4)
+    Ah = A.cpu().numpy().reshape(rows, nkb).astype(np.float64)
+    for kind, (rp, ci) in masks.items():
+        rph = rp.cpu().numpy()
+        cih = ci.cpu().numpy()[:rph[-1]]
+        rid = np.repeat(np.arange(rows), np.diff(rph))
+        out[f"captured_mass_{kind}"] = round(float(Ah[rid, cih].sum() / rows), 4)
+        out[f"nnz_{kind}"] = int(rph[-1])
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +424,7 @@ def main():
         density = kcol / L
     sd.sdattn_schedule_destroy(h)
     dense_flops = 4.0 * w.batch * H * L * L * d
+    mask_cmp = compare_masks(sd, p, w, xs, o, lse) if w.selector == "blocks_exact" else None
 
     def med(a):
         return float(np.median(a)) if len(a) else None
@@ -479,6 +522,7 @@ def main():
                    "sparse_effective_tflops": round(sparse_tflops, 1) if sparse_tflops else None,
                    "sparse_mfma_frac": round(sparse_tflops / peak, 4) if sparse_tflops else None,
                    "kept_density": round(density, 5), "kept_nnz": nnz},
+        "mask_comparison": mask_cmp,
         "probes": ({"probe_step_ms": round(probe_ms, 4), "probe_overhead_ms": round(probe_ms - sparse_ms, 4)
                     if sparse_ms else None, "n_probes": n_probes, "n_adopted": n_adopted,
                     "last_overlap": round(last_overlap, 6), "min_overlap": w.min_overlap,

@@ -10,16 +10,18 @@
 //
 // Both kernels are tiny next to the attention step: the overlap reads the two
 // CSR patterns once (one wave per row, each lane looking its entries of A up
-// in B's ascending row by binary search), and the adoption copies B over A
-// only when the decision, taken on the GPU from the counts, says so.
+// in B's ascending row by binary search; at most 256 workgroups, because the
+// workgroups' 64-bit atomics on the one count serialise), and the adoption
+// copies B over A only when the decision, taken on the GPU from the counts,
+// says so.
 
 #include "probe.h"
 
 namespace sdattn {
 namespace {
 
-constexpr int kOvWaves = 4;        // waves per workgroup
-constexpr int kOvRowsPerWave = 1;  // rows per wave (each row is a chain of dependent loads)
+constexpr int kOvWaves = 16;     // waves per workgroup
+constexpr int kOvMaxGroups = 256;  // at most one 64-bit atomic per workgroup on the shared count
 
 __global__ void overlap_zero_kernel(int64_t* counts) {
     if (threadIdx.x < 3) counts[threadIdx.x] = 0;
@@ -34,11 +36,11 @@ __global__ __launch_bounds__(kOvWaves * 64) void overlap_kernel(int rows, const 
     __shared__ int part[kOvWaves];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * (kOvWaves * kOvRowsPerWave);
     int hits = 0;
-    for (int i = 0; i < kOvRowsPerWave; ++i) {
-        const int64_t r = r0 + i * kOvWaves + wave;
-        if (r >= rows) break;
+    // one row per wave at a time (each row is a chain of dependent loads),
+    // grid-stride over the rows
+    for (int64_t r = static_cast<int64_t>(blockIdx.x) * kOvWaves + wave; r < rows;
+         r += static_cast<int64_t>(gridDim.x) * kOvWaves) {
         const int a1 = rpa[r + 1], b0 = rpb[r], b1 = rpb[r + 1];
         for (int e = rpa[r] + lane; e < a1; e += 64) {
             const int32_t x = cia[e];
@@ -113,8 +115,8 @@ hipError_t launch_mask_overlap(int rows, const int32_t* rpa, const int32_t* cia,
     hipLaunchKernelGGL(overlap_zero_kernel, dim3(1), dim3(64), 0, st, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || rows == 0) return e;
-    const int64_t per = kOvWaves * kOvRowsPerWave;
-    const int64_t grid = (static_cast<int64_t>(rows) + per - 1) / per;
+    int64_t grid = (static_cast<int64_t>(rows) + kOvWaves - 1) / kOvWaves;
+    if (grid > kOvMaxGroups) grid = kOvMaxGroups;
     hipLaunchKernelGGL(overlap_kernel, dim3(static_cast<unsigned>(grid)), dim3(kOvWaves * 64), 0, st, rows, rpa,
                        cia, rpb, cib, counts);
     return hipGetLastError();
