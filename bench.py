@@ -174,6 +174,18 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
     except Exception:  # pragma: no cover
         threads = 1
     cores = len(os.sched_getaffinity(0))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()
+                                 if i.get("user_api") == "blas"}))
+    except Exception:  # pragma: no cover
+        blas = None
     L, H, d = w.seq_len, w.q_heads, w.head_dim
     G = w.q_heads // w.kv_heads
     x0 = base_step
@@ -247,11 +259,40 @@ def cpu_baseline(w, acts, base_step, sel_step_inputs):
              + n["SPARSE"] * t_sparse + n["PROBE_SPARSE"] * (t_sel + t_ov + t_sparse))
     ms = 1e3 * total / len(acts)
     return {"value": round(ms, 3), "unit": "ms/denoise step", "cores": threads, "host_cores": cores,
-            "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas, "kind": "oracle",
             "sample": ("fp64 numpy oracle, extrapolated from timed samples: " + "; ".join(
                 f"{k}: {v}" for k, v in samples.items()) + "; weighted by the schedule's action counts"),
             "per_step_ms": {"dense": round(1e3 * t_dense, 1), "select": round(1e3 * t_sel, 1),
                             "sparse": round(1e3 * t_sparse, 1)}}
+
+
+def sdpa_dense_baseline(x, w, dense_ms):
+    """PyTorch-ROCm's own fused attention (scaled_dot_product_attention with
+    only the flash backend enabled: it raises instead of falling back to the
+    unfused path) on the dense step's tensors, for context beside this
+    library's dense forward.  GQA heads are expanded to Hq first."""
+    import torch
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    G = w.q_heads // w.kv_heads
+    try:
+        k = x["k"].repeat_interleave(G, dim=1).contiguous() if G > 1 else x["k"]
+        v = x["v"].repeat_interleave(G, dim=1).contiguous() if G > 1 else x["v"]
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            torch.nn.functional.scaled_dot_product_attention(x["q"], k, v)
+            torch.cuda.synchronize()
+            n = 3 if w.seq_len >= 32768 else 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                torch.nn.functional.scaled_dot_product_attention(x["q"], k, v)
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+    except Exception as e:  # noqa: BLE001 - context only; never fails the bench
+        return {"kind": "torch SDPA (flash backend)", "error": str(e)[:200]}
+    flops = 4.0 * w.batch * w.q_heads * w.seq_len ** 2 * w.head_dim
+    return {"kind": "torch SDPA (flash backend), PyTorch-ROCm, same GPU and tensors", "ms_per_step": round(ms, 3),
+            "tflops": round(flops / (ms * 1e9), 1), "this_library_speedup": round(ms / dense_ms, 3)}
 
 
 def compare_masks(sd, p, w, x, o, lse):
@@ -306,6 +347,8 @@ def main():
     ap.add_argument("--selector", choices=["pooled", "exact"], default="pooled",
                     help="block workloads: pattern from pooled scores (default) or from the exact block mass of "
                          "the last dense step")
+    ap.add_argument("--no-sdpa-baseline", action="store_true",
+                    help="skip timing torch's own SDPA (flash backend) on the dense step for context")
     ap.add_argument("--probe-interval", type=int, default=None,
                     help="adaptive anchors (block workloads): probe the pattern every N steps after the selection")
     ap.add_argument("--min-overlap", type=float, default=0.9,
@@ -457,6 +500,12 @@ def main():
 
     probe_ms = med(step_ms[idx["PROBE_SPARSE"]]) if idx.get("PROBE_SPARSE") else None
     ms_per_step = total_ms / K
+    # per action: median and p10/p90 of the step times; the schedule modelled
+    # from the medians, beside the measured one
+    step_stats = {a: {"n": len(v), "median_ms": round(float(np.median(step_ms[v])), 4),
+                      "p10_ms": round(float(np.percentile(step_ms[v], 10)), 4),
+                      "p90_ms": round(float(np.percentile(step_ms[v], 90)), 4)} for a, v in sorted(idx.items())}
+    modelled_ms = sum(len(v) * float(np.median(step_ms[v])) for v in idx.values()) / K
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     # Roofline figures use each kernel's average launch inside the timed region:
     # a SPARSE step is one sparse forward, a DENSE step one dense forward.
@@ -532,10 +581,14 @@ def main():
                            "schedule_speedup": round(dense_base_ms / ms_per_step, 3),
                            "sparse_step_speedup": round(dense_base_ms / sparse_ms, 3) if sparse_ms else None},
         "kernels": kernels,
+        "step_times": step_stats,
+        "modelled_ms_per_step": round(modelled_ms, 4),
         "wall_s": round(wall, 2),
         "gpu_state": gpu_state,
         "schedule_stats": stats,
     }
+    if not args.no_sdpa_baseline and w.dtype == "bf16":
+        out["sdpa_dense_baseline"] = sdpa_dense_baseline(x0, w, dense_launch_ms)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(w0, acts, x0h, xsh)
