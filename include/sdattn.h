@@ -325,9 +325,13 @@ SDATTN_API sdattn_status sdattn_schedule_action(const sdattn_schedule* s, int32_
 /*
  * Runs denoising step `step`: enqueues the step's kernels on `stream`.
  * o required; lse optional (the handle keeps its own buffer when NULL).
- * Steps may be run in any order, but a SPARSE step fails with
- * SDATTN_ERR_STATE if no pattern has been built yet; a failed step leaves
- * the cached pattern and step counters unchanged.
+ * Steps may be run in any order, but a SPARSE or PROBE_SPARSE step fails
+ * with SDATTN_ERR_STATE if no pattern has been built yet; a failed step
+ * leaves the cached pattern and step counters unchanged (one exception: a
+ * PROBE_SPARSE step whose last launch, the attention, fails after the
+ * adoption kernel was enqueued may have replaced the pattern; all its
+ * arguments are checked before anything is enqueued, so only a HIP launch
+ * failure can do that).
  */
 SDATTN_API sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void* q,
                                    const void* k, const void* v, void* o, float* lse,
