@@ -127,6 +127,17 @@ def test_exact_selection_validation():
         sd.sdattn_select_blocks_exact_workspace(p, 128, 128, sd.topk_budget(0.0))
 
 
+def test_exact_selection_of_an_empty_sequence_is_a_no_op():
+    lib = sd.lib()
+    p = sd.problem(1, 4, 4, 0, 128, "bf16")
+    b = sd.topk_budget(0.1)
+    ws, nnz = sd.sdattn_select_blocks_exact_workspace(p, 128, 128, b)
+    assert ws == 0 and nnz == 0
+    # nothing is enqueued for L = 0, so NULL buffers are accepted
+    assert lib.sdattn_select_blocks_exact(ctypes.byref(p), None, None, None, 128, 128, ctypes.byref(b), None, None,
+                                          0, None, None, 0, None) == 0
+
+
 def test_mask_overlap_validation():
     lib = sd.lib()
     assert lib.sdattn_mask_overlap(-1, BAD, BAD, BAD, BAD, BAD, None) == 2

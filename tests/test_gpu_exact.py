@@ -122,6 +122,30 @@ def test_exact_mass_sampled_at_the_64k_shape():
         check_topk_rows([ci[rp[r]:rp[r + 1]]], a[None], k, f"64K exact row h={h} I={I}")
 
 
+def test_exact_mass_at_the_largest_key_block_count():
+    """L = 65,536 with 64-token blocks: 1,024 key blocks per row, the selector's
+    largest row (two heads; sampled rows checked against the oracle)."""
+    L, H, bq = 65536, 2, 64
+    say("select_blocks_exact nKB=1024")
+    g = torch.Generator(device="cuda").manual_seed(1024)
+    x = {n: torch.randn(1, H, L, 128, device="cuda", dtype=torch.float32, generator=g).to(torch.bfloat16)
+         for n in "qkv"}
+    lse = _dense_lse(x)
+    rp, ci, mass = _select_exact(x, lse, bq, bq, sd.topk_budget(0.05))
+    nqb = L // bq
+    k = oracle.count_from_fraction(0.05, nqb)
+    assert k == 52 and np.all(np.diff(rp) == k)
+    for h, I in [(0, 0), (1, nqb - 1), (0, 517), (1, 3)]:
+        rows = slice(I * bq, (I + 1) * bq)
+        hq = host_inputs(x["q"][:, h:h + 1, rows].contiguous())
+        hk = host_inputs(x["k"][:, h:h + 1].contiguous())
+        _, rl = oracle.dense_attention(hq, hk, host_inputs(x["v"][:, h:h + 1].contiguous()))
+        a = oracle.exact_block_mass(hq, hk, rl, bq, bq)[0, 0, 0]
+        r = h * nqb + I
+        np.testing.assert_allclose(mass[r], a, rtol=SCORE_REL, atol=MASS_ABS)
+        check_topk_rows([ci[rp[r]:rp[r + 1]]], a[None], k, f"nKB=1024 exact row h={h} I={I}")
+
+
 def test_exact_selector_schedule_bf16():
     """Through the driver: warm-up, the exact selection on the last dense
     step (pattern from the next step on), a dense refresh, sparse steps."""
