@@ -113,7 +113,8 @@ class GpuMonitor:
     def summary(self):
         import numpy as np
         if not self.samples:
-            return {"samples": 0, "error": self.error or ("amd-smi not found" if not self.exe else None)}
+            why = self.error or ("amd-smi not found" if not self.exe else None)
+            return {"samples": 0, "error": why if why or self._thread.ident else "not sampled (--no-gpu-monitor)"}
         pw = np.array([s[0] for s in self.samples])
         ck = np.array([s[1] for s in self.samples if s[1] is not None])
         out = {"samples": len(self.samples), "tool": "amd-smi metric -p -c",
@@ -347,6 +348,8 @@ def main():
     ap.add_argument("--selector", choices=["pooled", "exact"], default="pooled",
                     help="block workloads: pattern from pooled scores (default) or from the exact block mass of "
                          "the last dense step")
+    ap.add_argument("--no-gpu-monitor", action="store_true",
+                    help="do not sample power and clocks with amd-smi (e.g. under a profiler)")
     ap.add_argument("--no-sdpa-baseline", action="store_true",
                     help="skip timing torch's own SDPA (flash backend) on the dense step for context")
     ap.add_argument("--probe-interval", type=int, default=None,
@@ -426,7 +429,9 @@ def main():
     h = sd.sdattn_schedule_create(p, schedule_desc(sd, w))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
-    monitor = GpuMonitor().start()
+    monitor = GpuMonitor()
+    if not args.no_gpu_monitor:
+        monitor.start()
     t_wall = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
