@@ -183,7 +183,9 @@ SDATTN_API sdattn_status sdattn_select_blocks(const sdattn_problem* p, const voi
  * sdattn_select_blocks_exact_workspace (host only); block_mass (optional)
  * receives A.  The scores are exact softmax probabilities (bf16 inputs: MFMA
  * with fp32 accumulation), summed in fp32; selection is made in fp32 as in
- * sdattn_select_blocks.  Cost: one pass of Q K^T over all (i, j).
+ * sdattn_select_blocks.  Cost: one pass of Q K^T over all (i, j).  Errors
+ * as sdattn_select_blocks, and SDATTN_ERR_NULL when lse is NULL (L > 0);
+ * the workspace must be non-NULL and at least the queried size.
  */
 SDATTN_API sdattn_status sdattn_select_blocks_exact_workspace(const sdattn_problem* p, int32_t block_q,
                                                    int32_t block_k, const sdattn_budget* budget,
