@@ -16,6 +16,9 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdattn.so")
 
+# ABI of include/sdattn.h that this binding marshals for (SDATTN_ABI_VERSION)
+SDATTN_ABI_VERSION = 2
+
 # ---- enums ------------------------------------------------------------------
 SDATTN_OK = 0
 STATUS_NAMES = ["SDATTN_OK", "SDATTN_ERR_NULL", "SDATTN_ERR_SHAPE", "SDATTN_ERR_DTYPE", "SDATTN_ERR_BUDGET",

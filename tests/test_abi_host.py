@@ -34,7 +34,9 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.sdattn_abi_version() == 2
+    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 2
+    hdr = open(os.path.join(ROOT, "include", "sdattn.h")).read()
+    assert f"#define SDATTN_ABI_VERSION {sd.SDATTN_ABI_VERSION}" in hdr
     for i, name in enumerate(sd.STATUS_NAMES):
         assert sd.sdattn_status_string(i) == name
 
