@@ -339,6 +339,13 @@ SDATTN_API sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, 
                                    const void* k, const void* v, void* o, float* lse,
                                    void* stream);
 
+/* Graph capture.  A step enqueues kernels only (no memset, copy, allocation
+ * or host wait), so steps may be captured into a HIP graph and replayed with
+ * new contents in the same buffers.  A captured step binds the pattern
+ * buffer in use at capture time: capture again after a selection or refresh
+ * step, which switches buffers.  A probe's adoption copies into the buffer in
+ * use, so captured steps stay valid across probes. */
+
 /* Borrowed device pointers of the cached pattern (valid until destroy):
  * blocks -> CSR row_ptr and col_idx; columns -> row_ptr = NULL and col_idx
  * [B][Hkv][kcol].  *nnz_capacity = int32 slots of col_idx.  Fails with
