@@ -161,3 +161,22 @@ def test_schedule_descriptor_validation():
     for d in bad:
         with pytest.raises(sd.SdattnError):
             sd.sdattn_schedule_create(p, d)
+
+
+def test_header_and_library_from_plain_c(tmp_path):
+    """The public header compiles as C99 and as C++17 with warnings as errors,
+    and a C program linked against the library gets the same host-side
+    answers as the binding."""
+    inc = os.path.join(ROOT, "include")
+    src = os.path.join(ROOT, "tests", "host", "abi_c_client.c")
+    libdir = os.path.dirname(sd.LIB_PATH)
+    exe = str(tmp_path / "abi_c_client")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", inc, src, "-o", exe, "-L", libdir,
+                    "-lsdattn", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True, text=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "C client OK (ABI 2)" in r.stdout
+    cpp = tmp_path / "hdr.cpp"
+    cpp.write_text('#include "sdattn.h"\nint main() { return sdattn_abi_version() == SDATTN_ABI_VERSION ? 0 : 1; }\n')
+    subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc, str(cpp)],
+                   check=True, capture_output=True, text=True)
