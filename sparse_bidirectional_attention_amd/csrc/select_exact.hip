@@ -17,8 +17,9 @@
 // DMA, three stages) with their 64 lse values; S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, exp2(s c - lse log2 e) in fp32 accumulated per
 // lane over the query block's tiles.  At each query block's end a wave sums
-// its lanes (its 32 keys x the block's queries); after the next barrier
-// wave 0 adds the waves of each key block in a fixed order and writes A.
+// its lanes in registers (its 32 keys x the block's queries); after the next
+// barrier wave 0 adds the waves of each key block in a fixed order and
+// writes A.
 // fp32: one workgroup per query block, one key per thread, exact fp32 FMAs
 // and expf.
 
@@ -41,6 +42,29 @@ struct MassParams {
 constexpr int BM_NW = 8;
 constexpr int BM_QT = 64;
 constexpr int BM_NST = 3;
+
+// Sum over the 64 lanes of a wave, in every lane, in registers: DPP
+// quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror and row_mirror pair each
+// lane with one in the other half of its 4, 8 and 16 lanes; v_permlane16_swap
+// and v_permlane32_swap then add the other row and the other half-wave.  All
+// VALU (no LDS crossbar round trips), and the same value in every lane
+// (each step adds the same two values in every pair).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_regs(float x) {
+    x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_move<0x141>(x);  // row_half_mirror
+    x += dpp_move<0x140>(x);  // row_mirror
+    uint32_t u = __float_as_uint(x);
+    const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    u = __float_as_uint(x);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
 
 template <int D>
 __global__ __launch_bounds__(BM_NW * 64) void block_mass_bf16_kernel(MassParams p) {
@@ -112,16 +136,27 @@ __global__ __launch_bounds__(BM_NW * 64) void block_mass_bf16_kernel(MassParams 
     for (int r = 0; r < 16; ++r) facc[r] = 0.f;
     const int tpb = p.bq / BM_QT;  // Q tiles per query block (1 or 2)
     const int wpb = p.bk / 32;     // waves per key block (2 or 4)
-    // this wave's sum over its (real) keys and the finished block's queries
+    // this wave's sum over its (real) keys and the finished block's queries;
+    // only a wave of the last key tile can hold keys past L
+    const bool partial_keys = key0 + 32 > L;
     auto finalize = [&](int I) __attribute__((always_inline)) {
         float x = 0.f;
+        if (partial_keys) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            x += key < L ? facc[r] : 0.f;
-            facc[r] = 0.f;
+            for (int r = 0; r < 16; ++r) {
+                const int key = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                x += key < L ? facc[r] : 0.f;
+                facc[r] = 0.f;
+            }
+        } else {
+            float y[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = (facc[4 * j] + facc[4 * j + 1]) + (facc[4 * j + 2] + facc[4 * j + 3]);
+            x = (y[0] + y[1]) + (y[2] + y[3]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) facc[r] = 0.f;
         }
-        x = wave_sum(x);
+        x = wave_sum_regs(x);
         if (lane == 0) red[I & 1][wave] = x;
     };
     // after a barrier that follows finalize(I) in every wave
@@ -143,6 +178,19 @@ __global__ __launch_bounds__(BM_NW * 64) void block_mass_bf16_kernel(MassParams 
     // The exponentials of one 32-query half run beside the MFMAs of the next
     // half; the second half of tile qt is accumulated during tile qt+1, so a
     // query block is finished there.
+    // Q operand reads two ahead of the MFMAs, and five VALU instructions of the
+    // other half's exponentials between consecutive MFMAs
+    auto interleave = [&]() __attribute__((always_inline)) {
+        if constexpr (DK == 8) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+            }
+        }
+    };
     f32x16 a1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) a1[r] = 0.f;
@@ -168,6 +216,8 @@ __global__ __launch_bounds__(BM_NW * 64) void block_mass_bf16_kernel(MassParams 
             a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kreg[st], q0, a0, 0, 0, 0);
         }
         accumulate(a1, lb);  // the previous tile's second half
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
         if (qt > 0 && (qt & (tpb - 1)) == 0) {
             finalize(qt / tpb - 1);
             pending = qt / tpb - 1;
@@ -182,6 +232,7 @@ __global__ __launch_bounds__(BM_NW * 64) void block_mass_bf16_kernel(MassParams 
         }
         accumulate(a0, la);
         lb = lnext;
+        interleave();
         __builtin_amdgcn_sched_barrier(0);
     };
     int qt = 0;
