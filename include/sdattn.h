@@ -249,6 +249,26 @@ SDATTN_API sdattn_status sdattn_forward_column_sparse(const sdattn_problem* p, c
                                            const void* v, const int32_t* col_idx, int32_t kcol,
                                            void* o, float* lse, void* stream);
 
+/*
+ * The column-sparse forward in two calls, for steps that reuse one column
+ * pattern (PulseCol, Abstract: the selected columns are shared by the query
+ * heads of a group and reused across steps).  sdattn_gather_columns copies the
+ * listed rows once: kc[b][g][j] = k[b][g][col_idx[b][g][j]] and likewise vc,
+ * j < kcol (kc, vc caller-owned, [B][Hkv][kcol][d] in the problem's dtype;
+ * indices outside [0, L) are clamped).  sdattn_forward_column_packed then
+ * gives exactly the result of sdattn_forward_column_sparse with that col_idx,
+ * reading the gathered rows as contiguous tiles instead of gathering in
+ * every query tile.  Errors: SDATTN_ERR_NULL for a NULL q, kc, vc, o (or k,
+ * v, col_idx, kc, vc for the gather); SDATTN_ERR_BUDGET unless
+ * 1 <= kcol <= L; L == 0 is a no-op.
+ */
+SDATTN_API sdattn_status sdattn_gather_columns(const sdattn_problem* p, const void* k, const void* v,
+                                    const int32_t* col_idx, int32_t kcol, void* kc, void* vc,
+                                    void* stream);
+SDATTN_API sdattn_status sdattn_forward_column_packed(const sdattn_problem* p, const void* q, const void* kc,
+                                           const void* vc, int32_t kcol, void* o, float* lse,
+                                           void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-side step-schedule driver.                                          */
 /* ------------------------------------------------------------------------ */

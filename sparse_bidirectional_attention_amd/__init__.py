@@ -84,6 +84,9 @@ _SIGS = {
                                              ctypes.c_size_t, _P]),
     "sdattn_forward_column_sparse": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, _P, ctypes.c_int32, _P,
                                                     _P, _P]),
+    "sdattn_gather_columns": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
+    "sdattn_forward_column_packed": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32, _P, _P,
+                                                    _P]),
     "sdattn_mask_overlap": (ctypes.c_int, [ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "sdattn_schedule_create": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.POINTER(ScheduleDesc),
                                               ctypes.POINTER(_P)]),
@@ -259,6 +262,16 @@ def sdattn_forward_column_sparse(p, q, k, v, col_idx, kcol, o, lse=None, stream=
     _check(lib().sdattn_forward_column_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(col_idx), kcol,
                                               _ptr(o), _ptr(lse), _stream(stream)),
            "sdattn_forward_column_sparse")
+
+
+def sdattn_gather_columns(p, k, v, col_idx, kcol, kc, vc, stream=None):
+    _check(lib().sdattn_gather_columns(ctypes.byref(p), _ptr(k), _ptr(v), _ptr(col_idx), kcol, _ptr(kc), _ptr(vc),
+                                       _stream(stream)), "sdattn_gather_columns")
+
+
+def sdattn_forward_column_packed(p, q, kc, vc, kcol, o, lse=None, stream=None):
+    _check(lib().sdattn_forward_column_packed(ctypes.byref(p), _ptr(q), _ptr(kc), _ptr(vc), kcol, _ptr(o), _ptr(lse),
+                                              _stream(stream)), "sdattn_forward_column_packed")
 
 
 def sdattn_mask_overlap(rows, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, counts, stream=None):

@@ -235,6 +235,35 @@ sdattn_status sdattn_forward_column_sparse(const sdattn_problem* p, const void* 
     return run_attention(MODE_COLUMN, pr, q, k, v, o, lse, ix, stream, "sdattn_forward_column_sparse");
 }
 
+sdattn_status sdattn_gather_columns(const sdattn_problem* p, const void* k, const void* v, const int32_t* col_idx,
+                                    int32_t kcol, void* kc, void* vc, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (kcol < 1 || kcol > pr.L) return fail(SDATTN_ERR_BUDGET, "kcol must be in [1, seq_len]");
+    if (k == nullptr || v == nullptr || col_idx == nullptr || kc == nullptr || vc == nullptr)
+        return fail(SDATTN_ERR_NULL, "k, v, col_idx, kc and vc must be non-NULL");
+    hipError_t e = launch_gather_columns(shape_of(pr), pr.dtype == SDATTN_BF16 ? 2 : 4, k, v, col_idx, kcol, kc, vc,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdattn_gather_columns");
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_forward_column_packed(const sdattn_problem* p, const void* q, const void* kc, const void* vc,
+                                           int32_t kcol, void* o, float* lse, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (kcol < 1 || kcol > pr.L) return fail(SDATTN_ERR_BUDGET, "kcol must be in [1, seq_len]");
+    s = check_tensors(pr, q, kc, vc, o);
+    if (s != SDATTN_OK) return s;
+    SparseIndex ix;
+    ix.kcol = kcol;
+    return run_attention(MODE_COLUMN_PACKED, pr, q, kc, vc, o, lse, ix, stream, "sdattn_forward_column_packed");
+}
+
 sdattn_status sdattn_mask_overlap(int32_t rows, const int32_t* row_ptr_a, const int32_t* col_idx_a,
                                   const int32_t* row_ptr_b, const int32_t* col_idx_b, int64_t* counts,
                                   void* stream) {
@@ -325,11 +354,19 @@ sdattn_status be_ws_blocks_exact(void*, const sdattn_problem* p, int32_t bq, int
                                  size_t* ws, int64_t* nnz) {
     return sdattn_select_blocks_exact_workspace(p, bq, bk, b, ws, nnz);
 }
+sdattn_status be_gather_columns(void*, const sdattn_problem* p, const void* k, const void* v, const int32_t* ci,
+                                int32_t kcol, void* kc, void* vc, void* st) {
+    return sdattn_gather_columns(p, k, v, ci, kcol, kc, vc, st);
+}
+sdattn_status be_column_packed(void*, const sdattn_problem* p, const void* q, const void* kc, const void* vc,
+                               int32_t kcol, void* o, float* lse, void* st) {
+    return sdattn_forward_column_packed(p, q, kc, vc, kcol, o, lse, st);
+}
 
 const Backend kHipBackend = {nullptr,          be_dense,       be_select_blocks, be_block_sparse, be_select_columns,
                              be_column_sparse, be_ws_blocks,   be_ws_columns,    be_alloc,        be_release,
                              be_overlap,       be_probe_adopt, be_probe_init,    be_probe_read,   be_select_blocks_exact,
-                             be_ws_blocks_exact};
+                             be_ws_blocks_exact, be_gather_columns, be_column_packed};
 
 }  // namespace
 

@@ -6,7 +6,9 @@
 //   block-sparse  query block I of head h attends the key tokens of the key
 //                 blocks in its CSR row (Step-dLLM, Abstract);
 //   column-sparse every query of group g attends a shared list of key
-//                 tokens (PulseCol, Abstract).
+//                 tokens (PulseCol, Abstract), either gathered by index in
+//                 every workgroup or read from rows gathered once per step
+//                 (packed, [B][Hkv][kcol][d], streamed like dense tiles).
 // Each form streams key tiles; only where the tile's rows come from differs.
 //
 // Work decomposition: one workgroup per (batch, head, tile of 32 NW queries),
@@ -94,8 +96,9 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int b = bh / p.Hq;
     const int g = h / p.group;
     const int L = p.L;
-    const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * L * D;
-    const uint32_t head_bytes = static_cast<uint32_t>(L) * ROWB;
+    const int kv_len = MODE == MODE_COLUMN_PACKED ? p.kcol : L;  // K/V rows per kv head
+    const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * kv_len * D;
+    const uint32_t head_bytes = static_cast<uint32_t>(kv_len) * ROWB;
     const u32x4 rk = buffer_rsrc(p.k + kvoff, head_bytes);
     const u32x4 rv = buffer_rsrc(p.v + kvoff, head_bytes);
     const int q0 = qt * (NW * 32);
@@ -125,12 +128,13 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             n_full = ((ne - 1) << sub_shift) + min(per, rem / KT);
         }
     } else {
-        cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
+        if constexpr (MODE == MODE_COLUMN) cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
         n_tiles = (p.kcol + KT - 1) / KT;
         n_full = p.kcol / KT;
     }
     // first key of tile u (dense / block: a token index; column: an entry of
-    // the column list); J is the tile's kept block (block form)
+    // the column list; packed: a row of the gathered rows); J is the tile's
+    // kept block (block form)
     auto tile_key0 = [&](int u, int J) __attribute__((always_inline)) -> int {
         if constexpr (MODE == MODE_BLOCK)
             return J * p.block_k + (u & ((1 << sub_shift) - 1)) * KT;
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     };
     // number of real keys in the tile that starts at key0
     auto tile_valid = [&](int key0) __attribute__((always_inline)) -> int {
-        if constexpr (MODE == MODE_COLUMN)
+        if constexpr (MODE == MODE_COLUMN || MODE == MODE_COLUMN_PACKED)
             return min(KT, p.kcol - key0);
         else
             return max(0, min(KT, L - key0));
@@ -712,6 +716,7 @@ hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st
     switch (mode) {
         case MODE_DENSE: return launch_one<D, 8, 64, 2, MODE_DENSE>(fp, st);
         case MODE_COLUMN: return launch_one<D, 8, 64, 2, MODE_COLUMN>(fp, st);
+        case MODE_COLUMN_PACKED: return launch_one<D, 8, 64, 2, MODE_COLUMN_PACKED>(fp, st);
         case MODE_BLOCK:
             if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK>(fp, st);
             return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st);

@@ -1,6 +1,7 @@
 // Bidirectional attention forward for fp32 inputs (VALU, fp32 throughout).
 //
-// Same three forms as the bf16 kernel (dense / block-sparse / column-sparse);
+// Same forms as the bf16 kernel (dense / block-sparse / column-sparse, the
+// latter also from gathered column rows);
 // this path exists for fp32 problems, whose results must agree with fp64 to
 // ~1e-5, so it uses exact fp32 FMAs and the accurate expf instead of MFMA.
 // One query row per thread, BQ queries per workgroup; 32-key K/V tiles are
@@ -38,7 +39,7 @@ __global__ __launch_bounds__(BQ) void flash_fwd_f32(F32Params p) {
     const int b = bh / p.Hq;
     const int g = h / p.group;
     const int L = p.L;
-    const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * L * D;
+    const size_t kvoff = (static_cast<size_t>(b) * p.Hkv + g) * (MODE == MODE_COLUMN_PACKED ? p.kcol : L) * D;
     const float* kh = p.k + kvoff;
     const float* vh = p.v + kvoff;
     const int qi = qt * BQ + tid;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(BQ) void flash_fwd_f32(F32Params p) {
         sub = p.block_k / KT;
         n_tiles = (p.row_ptr[r + 1] - e0) * sub;
     } else {
-        cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
+        if constexpr (MODE == MODE_COLUMN) cb = p.col_idx + (static_cast<size_t>(b) * p.Hkv + g) * p.kcol;
         n_tiles = (p.kcol + KT - 1) / KT;
     }
 
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(BQ) void flash_fwd_f32(F32Params p) {
 
     for (int t = 0; t < n_tiles; ++t) {
         int base, nvalid;
-        if constexpr (MODE == MODE_COLUMN) {
+        if constexpr (MODE == MODE_COLUMN || MODE == MODE_COLUMN_PACKED) {
             base = t * KT;
             nvalid = min(KT, p.kcol - base);
         } else {
@@ -87,6 +88,7 @@ __global__ __launch_bounds__(BQ) void flash_fwd_f32(F32Params p) {
             const int r = e / D, d = e % D;
             int row;
             if constexpr (MODE == MODE_COLUMN) row = min(max(cb[base + min(r, nvalid - 1)], 0), L - 1);
+            else if constexpr (MODE == MODE_COLUMN_PACKED) row = base + min(r, nvalid - 1);
             else row = min(max(base + r, 0), L - 1);
             Ks[r][d] = kh[static_cast<size_t>(row) * D + d];
             Vs[r][d] = vh[static_cast<size_t>(row) * D + d];
@@ -133,6 +135,9 @@ hipError_t launch_mode(AttnMode mode, const F32Params& fp, hipStream_t st) {
         case MODE_DENSE: hipLaunchKernelGGL((flash_fwd_f32<D, BQ, MODE_DENSE>), grid, block, 0, st, fp); break;
         case MODE_BLOCK: hipLaunchKernelGGL((flash_fwd_f32<D, BQ, MODE_BLOCK>), grid, block, 0, st, fp); break;
         case MODE_COLUMN: hipLaunchKernelGGL((flash_fwd_f32<D, BQ, MODE_COLUMN>), grid, block, 0, st, fp); break;
+        case MODE_COLUMN_PACKED:
+            hipLaunchKernelGGL((flash_fwd_f32<D, BQ, MODE_COLUMN_PACKED>), grid, block, 0, st, fp);
+            break;
     }
     return hipGetLastError();
 }

@@ -8,7 +8,9 @@
 
 namespace sdattn {
 
-enum AttnMode { MODE_DENSE = 0, MODE_BLOCK = 1, MODE_COLUMN = 2 };
+// MODE_COLUMN_PACKED: the kept columns' K/V rows are given gathered,
+// [B][Hkv][kcol][d], and streamed like contiguous tiles.
+enum AttnMode { MODE_DENSE = 0, MODE_BLOCK = 1, MODE_COLUMN = 2, MODE_COLUMN_PACKED = 3 };
 
 struct AttnShape {
     int B, Hq, Hkv, L, D;
@@ -19,7 +21,7 @@ struct SparseIndex {
     int block_q = 128, block_k = 128;     // MODE_BLOCK
     const int32_t* row_ptr = nullptr;     // MODE_BLOCK
     const int32_t* col_idx = nullptr;     // MODE_BLOCK (CSR) / MODE_COLUMN ([B][Hkv][kcol])
-    int kcol = 0;                         // MODE_COLUMN
+    int kcol = 0;                         // MODE_COLUMN, MODE_COLUMN_PACKED
 };
 
 // Flash-style forward; bf16 inputs (MFMA) or f32 inputs (VALU).
@@ -46,5 +48,10 @@ size_t select_columns_ws_bytes(const AttnShape& s);
 hipError_t launch_select_columns(const AttnShape& s, bool bf16, const void* q, const void* k,
                                  const float* lse, int kcol, int32_t* col_idx, double* col_scores,
                                  void* ws, hipStream_t st);
+
+// kc/vc [B][Hkv][kcol][d] = the rows of k/v listed in col_idx [B][Hkv][kcol]
+// (indices clamped to [0, L)); elem_bytes is 2 (bf16) or 4 (fp32).
+hipError_t launch_gather_columns(const AttnShape& s, int elem_bytes, const void* k, const void* v,
+                                 const int32_t* col_idx, int kcol, void* kc, void* vc, hipStream_t st);
 
 }  // namespace sdattn

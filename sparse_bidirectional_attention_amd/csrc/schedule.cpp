@@ -33,7 +33,9 @@ struct sdattn_schedule {
     int active = -1;  // -1: no pattern yet
     void* ws = nullptr;
     size_t ws_bytes = 0;
-    float* lse = nullptr;  // own lse buffer (columns)
+    float* lse = nullptr;  // own lse buffer (columns, exact blocks)
+    void* kc = nullptr;    // columns: the kept K / V rows of the step, [B][Hkv][kcol][d]
+    void* vc = nullptr;
     int64_t counts[4] = {0, 0, 0, 0};
     int32_t last_select = -1;
     // probes (blocks with probe_interval > 0): device counts [3] + ProbeState
@@ -160,6 +162,12 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         ci_bytes = static_cast<size_t>(std::max<int64_t>(s->nnz_cap, 1)) * sizeof(int32_t);
         st = s->be.alloc(s->be.ctx, lse_bytes, reinterpret_cast<void**>(&s->lse));
         if (st != SDATTN_OK) return cleanup_fail(st);
+        const size_t packed = static_cast<size_t>(std::max<int64_t>(s->nnz_cap, 1)) * pr.D *
+                              (pr.dtype == SDATTN_BF16 ? 2 : 4);
+        st = s->be.alloc(s->be.ctx, packed, &s->kc);
+        if (st != SDATTN_OK) return cleanup_fail(st);
+        st = s->be.alloc(s->be.ctx, packed, &s->vc);
+        if (st != SDATTN_OK) return cleanup_fail(st);
     }
     for (int i = 0; i < 2; ++i) {
         if (rp_bytes) {
@@ -272,8 +280,14 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
             if (blocks)
                 st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[s->active],
                                      s->col_idx[s->active], o, lse, stream);
-            else
-                st = be.column_sparse(be.ctx, p, q, k, v, s->col_idx[s->active], s->kcol, o, lse, stream);
+            else {
+                // the kept columns' K/V rows are gathered once, then streamed
+                // by every query tile of the group
+                if (s->pr.L > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+                    return fail(SDATTN_ERR_NULL, "q, k, v and o must be non-NULL");
+                st = be.gather_columns(be.ctx, p, k, v, s->col_idx[s->active], s->kcol, s->kc, s->vc, stream);
+                if (st == SDATTN_OK) st = be.column_packed(be.ctx, p, q, s->kc, s->vc, s->kcol, o, lse, stream);
+            }
             break;
     }
     if (st == SDATTN_OK) s->counts[act] += 1;
@@ -326,6 +340,8 @@ void sdattn_schedule_destroy(sdattn_schedule* s) {
     }
     if (s->ws) be.release(be.ctx, s->ws);
     if (s->lse) be.release(be.ctx, s->lse);
+    if (s->kc) be.release(be.ctx, s->kc);
+    if (s->vc) be.release(be.ctx, s->vc);
     delete s;
 }
 

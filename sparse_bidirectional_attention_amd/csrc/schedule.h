@@ -45,6 +45,11 @@ struct Backend {
                                          void* stream);
     sdattn_status (*workspace_blocks_exact)(void* ctx, const sdattn_problem*, int32_t bq, int32_t bk,
                                             const sdattn_budget*, size_t* ws, int64_t* max_nnz);
+    // column steps from rows gathered once per step
+    sdattn_status (*gather_columns)(void* ctx, const sdattn_problem*, const void* k, const void* v,
+                                    const int32_t* col_idx, int32_t kcol, void* kc, void* vc, void* stream);
+    sdattn_status (*column_packed)(void* ctx, const sdattn_problem*, const void* q, const void* kc, const void* vc,
+                                   int32_t kcol, void* o, float* lse, void* stream);
 };
 
 // The backend used by sdattn_schedule_create (defined by the library build

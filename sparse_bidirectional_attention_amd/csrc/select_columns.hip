@@ -323,7 +323,41 @@ __global__ __launch_bounds__(1024) void col_topk_kernel(const double* __restrict
     }
 }
 
+// Rows of k and v at the listed columns, packed [B][Hkv][kcol][d]: one
+// 16-byte unit per thread and pass (grid-stride), K and V together.  The
+// packed rows serve every query tile of the group, so the gather by index
+// happens once per step instead of in every workgroup.
+__global__ __launch_bounds__(256) void gather_columns_kernel(const char* __restrict__ k, const char* __restrict__ v,
+                                                             const int32_t* __restrict__ col_idx, int L, int kcol,
+                                                             int units, long long n_units, int row_bytes,
+                                                             char* __restrict__ kc, char* __restrict__ vc) {
+    for (long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x; i < n_units;
+         i += static_cast<long long>(gridDim.x) * 256) {
+        const long long row = i / units;  // (b Hkv + g) kcol + j
+        const int u = static_cast<int>(i - row * units);
+        const long long bg = row / kcol;
+        const int col = min(max(col_idx[row], 0), L - 1);
+        const size_t src = static_cast<size_t>(bg * L + col) * row_bytes + u * 16;
+        const size_t dst = static_cast<size_t>(row) * row_bytes + u * 16;
+        *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(k + src);
+        *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(v + src);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_gather_columns(const AttnShape& s, int elem_bytes, const void* k, const void* v,
+                                 const int32_t* col_idx, int kcol, void* kc, void* vc, hipStream_t st) {
+    const int row_bytes = s.D * elem_bytes;
+    const int units = row_bytes / 16;
+    const long long n_units = static_cast<long long>(s.B) * s.Hkv * kcol * units;
+    if (n_units == 0 || s.L == 0) return hipSuccess;
+    const unsigned grid = static_cast<unsigned>(std::min<long long>(4096, (n_units + 255) / 256));
+    hipLaunchKernelGGL(gather_columns_kernel, dim3(grid), dim3(256), 0, st, static_cast<const char*>(k),
+                       static_cast<const char*>(v), col_idx, s.L, kcol, units, n_units, row_bytes,
+                       static_cast<char*>(kc), static_cast<char*>(vc));
+    return hipGetLastError();
+}
 
 size_t select_columns_ws_bytes(const AttnShape& s) {
     const size_t a = static_cast<size_t>(s.B) * s.Hq * s.L * 8;

@@ -125,10 +125,20 @@ sdattn_status f_ws_blocks_exact(void* ctx, const sdattn_problem* p, int32_t bq, 
     return st;
 }
 
-const sdattn::Backend kFake = {nullptr,         f_dense,       f_select_blocks, f_block_sparse, f_select_columns,
-                               f_column_sparse, f_ws_blocks,   f_ws_columns,    f_alloc,        f_release,
-                               f_overlap,       f_probe_adopt, f_probe_init,    f_probe_read,   f_select_blocks_exact,
-                               f_ws_blocks_exact};
+sdattn_status f_gather_columns(void*, const sdattn_problem*, const void*, const void*, const int32_t* ci, int32_t kcol,
+                               void* kc, void* vc, void*) {
+    return record("gather_columns ci=" + ptr(ci) + " kcol=" + std::to_string(kcol) + " kc=" + ptr(kc) +
+                  " vc=" + ptr(vc));
+}
+sdattn_status f_column_packed(void*, const sdattn_problem*, const void*, const void* kc, const void* vc, int32_t kcol,
+                              void* o, float*, void*) {
+    return record("column_packed kc=" + ptr(kc) + " vc=" + ptr(vc) + " kcol=" + std::to_string(kcol) + " o=" + ptr(o));
+}
+
+const sdattn::Backend kFake = {nullptr,          f_dense,          f_select_blocks, f_block_sparse, f_select_columns,
+                               f_column_sparse,  f_ws_blocks,      f_ws_columns,    f_alloc,        f_release,
+                               f_overlap,        f_probe_adopt,    f_probe_init,    f_probe_read,   f_select_blocks_exact,
+                               f_ws_blocks_exact, f_gather_columns, f_column_packed};
 
 }  // namespace
 

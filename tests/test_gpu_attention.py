@@ -118,6 +118,38 @@ def test_column_sparse_matches_oracle(dtype, Hq, Hkv, L, kcol, d):
     check_out(to_np(o), ro, to_np(lse), rl, dtype, "column_sparse")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Hq,Hkv,L,kcol,d", [(6, 2, 700, 21, 128), (4, 4, 512, 64, 64), (7, 1, 1000, 130, 128),
+                                             (2, 2, 97, 97, 128), (28, 4, 2048, 61, 128), (2, 1, 300, 1, 64)])
+def test_gathered_columns_and_packed_forward(dtype, Hq, Hkv, L, kcol, d):
+    """sdattn_gather_columns copies exactly the listed rows; the packed forward
+    over them is bit-identical to the column-sparse forward with the same list
+    and matches the oracle."""
+    say(f"column gather + packed {dtype} Hq={Hq} Hkv={Hkv} L={L} kcol={kcol} d={d}")
+    rng = np.random.default_rng(kcol + L)
+    x = _inputs(kcol + 23, 1, Hq, Hkv, L, d, dtype)
+    cols = np.stack([np.sort(rng.choice(L, kcol, replace=False)) for _ in range(Hkv)])[None].astype(np.int32)
+    dcols = torch.from_numpy(cols).cuda()
+    p = sd.problem_of(x["q"], x["k"])
+    kc = torch.full((1, Hkv, kcol, d), 7, dtype=x["k"].dtype, device="cuda")
+    vc = torch.full_like(kc, 7)
+    sd.sdattn_gather_columns(p, x["k"], x["v"], dcols, kcol, kc, vc)
+    torch.cuda.synchronize()
+    hk, hv = host_inputs(x["k"]), host_inputs(x["v"])
+    for g in range(Hkv):  # the rows, byte for byte
+        np.testing.assert_array_equal(host_inputs(kc)[0, g], hk[0, g, cols[0, g]])
+        np.testing.assert_array_equal(host_inputs(vc)[0, g], hv[0, g, cols[0, g]])
+    o1, l1 = _out(x["q"], dtype)
+    o2, l2 = _out(x["q"], dtype)
+    sd.sdattn_forward_column_packed(p, x["q"], kc, vc, kcol, o1, l1)
+    sd.sdattn_forward_column_sparse(p, x["q"], x["k"], x["v"], dcols, kcol, o2, l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16) if dtype == "bf16" else o1, o2.view(torch.int16) if dtype == "bf16" else o2)
+    assert torch.equal(l1, l2)
+    ro, rl = oracle.column_sparse_attention(host_inputs(x["q"]), hk, hv, cols)
+    check_out(to_np(o1), ro, to_np(l1), rl, dtype, "column_packed")
+
+
 @pytest.mark.parametrize("bq,bk", [(64, 64), (128, 128), (128, 64)])
 def test_full_csr_equals_dense_and_ones_v(bq, bk):
     say(f"full CSR == dense, V=1 -> O=1, bq={bq} bk={bk}")

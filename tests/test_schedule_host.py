@@ -181,7 +181,18 @@ def test_column_schedule_uses_own_lse_buffer(fake):
     assert len(dense) == 3 and len(sel) == 3 and all("kcol=492" in l for l in sel)
     for d, s in zip(dense, sel):  # dense writes the lse that the selection reads
         assert re.search(r"lse=(\S+)", d).group(1) == re.search(r"lse=(\S+)", s).group(1) != "(nil)"
-    assert sum(l.startswith("column_sparse") for l in log) == 189
+    # sparse steps: the kept rows gathered into the handle's buffers, then the packed forward
+    gathers = [l for l in log if l.startswith("gather_columns")]
+    packed = [l for l in log if l.startswith("column_packed")]
+    assert len(gathers) == len(packed) == 189 and not any(l.startswith("column_sparse") for l in log)
+    kc, vc = re.search(r"kc=(\S+) vc=(\S+)", gathers[0]).groups()
+    assert all(f"kc={kc} vc={vc}" in l for l in gathers + packed) and "kcol=492" in packed[0]
+    cur = None
+    for l in log:  # every gather reads the most recent selection's columns
+        if l.startswith("select_columns"):
+            cur = re.search(r"ci=(\S+)", l).group(1)
+        elif l.startswith("gather_columns"):
+            assert re.search(r"ci=(\S+)", l).group(1) == cur
     fake.sdattn_schedule_destroy(h)
     assert fake.sdattn_fake_live_allocs() == 0
 
