@@ -94,30 +94,38 @@ class GpuMonitor:
         while not self._stop.is_set():
             t0 = time.perf_counter()
             try:
-                self.samples.append(self.read())
+                power, clock = self.read()
             except Exception as e:  # noqa: BLE001 - monitoring must never break the bench
                 self.error = str(e)
                 return
+            self.samples.append((t0, time.perf_counter(), power, clock))
             self._stop.wait(max(0.0, self.period - (time.perf_counter() - t0)))
 
     def start(self):
+        self.t_begin = time.perf_counter()
         if self.exe:
             self._thread.start()
         return self
 
     def stop(self):
+        self.t_end = time.perf_counter()
         self._stop.set()
         if self._thread.is_alive():
             self._thread.join(timeout=30)
 
     def summary(self):
+        """Statistics of the samples taken wholly inside the timed region."""
         import numpy as np
-        if not self.samples:
-            why = self.error or ("amd-smi not found" if not self.exe else None)
-            return {"samples": 0, "error": why if why or self._thread.ident else "not sampled (--no-gpu-monitor)"}
-        pw = np.array([s[0] for s in self.samples])
-        ck = np.array([s[1] for s in self.samples if s[1] is not None])
-        out = {"samples": len(self.samples), "tool": "amd-smi metric -p -c",
+        if not self._thread.ident:
+            return {"samples": 0, "error": self.error or ("amd-smi not found" if not self.exe
+                                                          else "not sampled (--no-gpu-monitor)")}
+        inside = [s for s in self.samples if s[0] >= self.t_begin and s[1] <= self.t_end]
+        if not inside:
+            return {"samples": 0, "error": self.error or (
+                f"no amd-smi reading fell inside the {self.t_end - self.t_begin:.2f} s timed region")}
+        pw = np.array([s[2] for s in inside])
+        ck = np.array([s[3] for s in inside if s[3] is not None])
+        out = {"samples": len(inside), "tool": "amd-smi metric -p -c",
                "socket_power_w": {"median": round(float(np.median(pw)), 1), "min": round(float(pw.min()), 1),
                                   "max": round(float(pw.max()), 1)}}
         if len(ck):
