@@ -547,6 +547,13 @@ def main():
             "frac": round(dense_tflops / peak, 4), "launch_ms": round(dense_launch_ms, 3),
             "flops_per_launch": dense_flops, "traffic": load_traffic("flash_dense", w0.name)},
     }
+    # the calibrated L2-to-fabric bytes per launch (FETCH_SIZE also counts
+    # Infinity Cache hits, so this bounds HBM traffic from above) as a rate
+    for kv in kernels.values():
+        if kv["traffic"] and kv["launch_ms"]:
+            gbs = kv["traffic"] / (kv["launch_ms"] * 1e6)
+            kv["traffic_gbs"] = round(gbs, 1)
+            kv["traffic_frac_of_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
     dom = max(kernels, key=lambda k: share_sparse if "dense" not in k else share_dense)
     roof = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
     roof["kernel"] = dom
