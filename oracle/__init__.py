@@ -16,6 +16,10 @@ Modules
               the exact block mass from the full attention, top-k and
               mass-with-global-cap block selection to CSR, exact column
               scores and column top-k.
+  losa      : LoSA-style partial attention for block-wise diffusion: the
+              query-change locality score, the Active set, per-query page
+              selection, the per-kv-head page union and the attention of
+              Active rows over (union pages + block) with Stable rows kept.
   schedule  : the per-step action table (warm-up, selection, reuse, refresh,
               probes), the overlap of two block patterns and the probe's
               adoption rule, and a whole-schedule runner for small shapes.
@@ -56,4 +60,17 @@ from .schedule import (  # noqa: F401
     run_schedule,
     schedule_actions,
     select_steps,
+)
+from .losa import (  # noqa: F401
+    block_attention,
+    locality_scores,
+    losa_attention,
+    losa_dense,
+    losa_step,
+    page_scores,
+    pool_pages,
+    select_active,
+    select_pages,
+    union_pages,
+    union_token_mask,
 )

@@ -13,6 +13,10 @@ Sources of the shapes and schedules:
     256 steps, 90% sparsity.
   * PulseCol (arXiv 2605.20813), abstract: column-sparse pattern found at an
     early step and refreshed at a few intermediate steps.
+  * LoSA (Locality Aware Sparse Attention for block-wise diffusion LMs),
+    sections 3 and 5: a block denoised on top of a cached prefix, a few Active
+    tokens per iteration, a per-query budget of 128 prefix tokens; Trado-8B /
+    SDAR-8B shaped heads (32 query heads, 8 kv heads, d = 128).
 """
 
 from dataclasses import dataclass
@@ -109,6 +113,47 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class LosaWorkload:
+    """A block of block_len tokens denoised on top of a cached prefix of
+    prefix_len tokens: iteration 0 dense, iterations 1..steps_per_block-1
+    LoSA-style (n_active Active tokens, pages_per_query pages of `page`
+    tokens kept per Active query)."""
+    name: str
+    wid: int
+    batch: int
+    q_heads: int
+    kv_heads: int
+    prefix_len: int
+    block_len: int
+    head_dim: int
+    dtype: str
+    page: int
+    pages_per_query: int
+    n_active: int
+    steps_per_block: int
+    # generator: per iteration, n_moving tokens of the block change by
+    # sigma_move * N(0, 1), the others by sigma_still * N(0, 1)
+    n_moving: int = 6
+    sigma_move: float = 0.5
+    sigma_still: float = 0.01
+    pages_per_token: int = 2      # prefix pages aligned with each block token
+    notes: str = ""
+
+
+LOSA_WORKLOADS = {
+    w.name: w
+    for w in [
+        LosaWorkload(
+            name="losa_sdar8b_32k", wid=6, batch=1, q_heads=32, kv_heads=8, prefix_len=32768,
+            block_len=32, head_dim=128, dtype="bf16", page=16, pages_per_query=8, n_active=8,
+            steps_per_block=8,
+            notes="32-token block over a 32K cached prefix; 8 Active tokens, 8 pages of 16 (128 tokens) per query",
+        ),
+    ]
+}
+
+
 def get_workload(name: str) -> Workload:
     try:
         return WORKLOADS[name]
@@ -116,8 +161,8 @@ def get_workload(name: str) -> Workload:
         raise KeyError(f"unknown workload {name!r}; known: {sorted(WORKLOADS)}") from e
 
 
-def scaled(w: Workload, **overrides) -> Workload:
+def scaled(w, **overrides):
     """A copy of a workload with some fields replaced (smaller parity shapes)."""
     d = dict(w.__dict__)
     d.update(overrides)
-    return Workload(**d)
+    return type(w)(**d)

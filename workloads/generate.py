@@ -22,6 +22,17 @@ Recipe (all draws from numpy PCG64 seeded by SeedSequence):
                     (the marginal of a random walk with step s, so any step
                     can be produced without replaying the earlier ones).
   * bf16          : the fp32 step tensor rounded to nearest-even.
+  * block-wise (LoSA workloads): prefix K/V caches N(0, 1) and a block's Q/K/V
+    N(0, 1) from SeedSequence([wid, 0, tensor]); kv head types by g mod 4:
+      sink    : K of prefix tokens 0..63 += 3u, the group's block Q += 3u;
+      recent  : K of the last 256 prefix tokens += 3u, the group's block Q += 3u;
+      stripes : K of 4 random 64-token prefix units += 3u, block Q += 3u;
+    and per kv head, each block token i gets its own unit w_i: its group's
+    queries += 2 w_i and the keys of pages_per_token random prefix pages
+    += 2 w_i, so Active tokens select different pages.  Iteration t >= 1 adds
+    sigma_move N to q, k, v of n_moving random block tokens and sigma_still N
+    to the others (SeedSequence([wid, 1 + t, 10 + tensor])), accumulated from
+    iteration 0.
 
 Tensors are returned as numpy arrays of shape [B, H, L, d]: float32 for the
 fp32 workloads, uint16 bf16 bit patterns for the bf16 workloads.
@@ -29,7 +40,7 @@ fp32 workloads, uint16 bf16 bit patterns for the bf16 workloads.
 
 import numpy as np
 
-from .configs import Workload
+from .configs import LosaWorkload, Workload
 
 _T_Q, _T_K, _T_V = 0, 1, 2
 UNIT = 64  # token unit of the planted sink/local/stripe patterns
@@ -204,3 +215,66 @@ def score_jump(seed: int, B, Hq, Hkv, L, d, jump, n_low=64, dtype="bf16"):
     if dtype == "bf16":
         out = {n: f32_to_bf16_bits(x) for n, x in out.items()}
     return out
+
+
+_T_KC, _T_VC = 3, 4
+
+
+def make_losa_base(w: LosaWorkload):
+    """Prefix caches and iteration-0 block tensors in fp32: dict k_cache,
+    v_cache, q, k_blk, v_blk."""
+    B, Hq, Hkv, Lp, Bs, d = w.batch, w.q_heads, w.kv_heads, w.prefix_len, w.block_len, w.head_dim
+    G = Hq // Hkv
+    kc = _rng(w.wid, 0, _T_KC).standard_normal((B, Hkv, Lp, d), dtype=np.float32)
+    vc = _rng(w.wid, 0, _T_VC).standard_normal((B, Hkv, Lp, d), dtype=np.float32)
+    q = _rng(w.wid, 0, _T_Q).standard_normal((B, Hq, Bs, d), dtype=np.float32)
+    kb = _rng(w.wid, 0, _T_K).standard_normal((B, Hkv, Bs, d), dtype=np.float32)
+    vb = _rng(w.wid, 0, _T_V).standard_normal((B, Hkv, Bs, d), dtype=np.float32)
+    n_units = -(-Lp // UNIT)
+    n_pages = Lp // w.page
+    for g in range(Hkv):
+        r = _rng(w.wid, 400, g)
+        qs = slice(g * G, (g + 1) * G)
+        kind = g % 4
+        u = _unit(r, d)
+        if kind == 0:
+            kc[:, g, :min(UNIT, Lp)] += 3.0 * u
+            q[:, qs] += 3.0 * u
+        elif kind == 1:
+            kc[:, g, max(0, Lp - 4 * UNIT):] += 3.0 * u
+            q[:, qs] += 3.0 * u
+        elif kind == 2:
+            for c in r.choice(n_units, size=min(4, n_units), replace=False):
+                kc[:, g, c * UNIT:min(Lp, (c + 1) * UNIT)] += 3.0 * u
+            q[:, qs] += 3.0 * u
+        for i in range(Bs):
+            wi = _unit(r, d)
+            q[:, qs, i] += 2.0 * wi
+            for P in r.choice(n_pages, size=min(w.pages_per_token, n_pages), replace=False):
+                kc[:, g, P * w.page:(P + 1) * w.page] += 2.0 * wi
+    return {"k_cache": kc, "v_cache": vc, "q": q, "k_blk": kb, "v_blk": vb}
+
+
+def _losa_rounded(w: LosaWorkload, x):
+    return f32_to_bf16_bits(x) if w.dtype == "bf16" else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def make_losa_cache(w: LosaWorkload, base=None):
+    """The prefix caches as stored: dict k_cache, v_cache."""
+    base = make_losa_base(w) if base is None else base
+    return {n: _losa_rounded(w, base[n]) for n in ("k_cache", "v_cache")}
+
+
+def make_losa_iteration(w: LosaWorkload, t: int, base=None):
+    """The block's q, k_blk, v_blk at iteration t, as stored."""
+    base = make_losa_base(w) if base is None else base
+    x = {n: base[n].copy() for n in ("q", "k_blk", "v_blk")}
+    Bs = w.block_len
+    for s in range(1, t + 1):
+        pick = _rng(w.wid, 1 + s, 9).choice(Bs, size=min(w.n_moving, Bs), replace=False)
+        sig = np.full(Bs, w.sigma_still, dtype=np.float32)
+        sig[pick] = w.sigma_move
+        for ti, n in enumerate(("q", "k_blk", "v_blk")):
+            noise = _rng(w.wid, 1 + s, 10 + ti).standard_normal(x[n].shape, dtype=np.float32)
+            x[n] += noise * sig[None, None, :, None]
+    return {n: _losa_rounded(w, a) for n, a in x.items()}
