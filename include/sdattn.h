@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SDATTN_ABI_VERSION 2
+#define SDATTN_ABI_VERSION 3
 
 /* Exported entry points (the library is built with hidden visibility). */
 #define SDATTN_API __attribute__((visibility("default")))
@@ -391,6 +391,84 @@ SDATTN_API sdattn_status sdattn_schedule_probe_stats(const sdattn_schedule* s, i
 /* Frees the handle and its device buffers (NULL is a no-op).  The caller
  * must make sure no enqueued step still uses them (synchronise first). */
 SDATTN_API void sdattn_schedule_destroy(sdattn_schedule* s);
+
+/* ===================================================================== */
+/* Block-wise diffusion over a cached prefix: LoSA-style partial          */
+/* attention (LoSA: Locality Aware Sparse Attention for block-wise        */
+/* diffusion language models, section 3, core principles and workflow).   */
+/* ===================================================================== */
+
+/* A block of block_len tokens is denoised on top of a prefix of
+ * prefix_len tokens whose keys and values are cached.  Layouts (contiguous,
+ * bf16 unless stated):
+ *   q, q_prev, o      [B][Hq][block_len][d]   (the block's queries, outputs)
+ *   k_cache, v_cache  [B][Hkv][prefix_len][d] (the prefix cache)
+ *   k_blk, v_blk      [B][Hkv][block_len][d]  (the block's own keys, values)
+ *   lse               [B][Hq][block_len] fp32, natural log
+ *   kp                [B][Hkv][prefix_len/page][d] fp32 page means of k_cache
+ * Every query attends, without a causal mask, to the prefix and to all keys
+ * of its block; query head h reads kv head h / (Hq/Hkv).
+ * Constraints: dtype SDATTN_BF16 (SDATTN_F32 -> SDATTN_ERR_UNSUPPORTED),
+ * head_dim 64 or 128, block_len <= 64, page divides prefix_len,
+ * prefix_len/page <= 4096, 1 <= n_active <= block_len (else
+ * SDATTN_ERR_BUDGET), 1 <= pages_per_query <= prefix_len/page (else
+ * SDATTN_ERR_BUDGET).  softmax_scale <= 0 means 1/sqrt(head_dim). */
+typedef struct {
+    int32_t batch, q_heads, kv_heads, prefix_len, block_len, head_dim;
+    sdattn_dtype dtype;
+    float softmax_scale;
+    int32_t page;            /* prefix tokens per page (the selection unit) */
+    int32_t n_active;        /* Active tokens per later iteration */
+    int32_t pages_per_query; /* pages kept per Active query and head */
+} sdattn_losa_problem;
+
+/* Workspace bytes for sdattn_losa_dense and sdattn_losa_step (the larger of
+ * the two) and the capacity of one kv head's page union,
+ * min(prefix_len/page, (Hq/Hkv) * n_active * pages_per_query). */
+SDATTN_API sdattn_status sdattn_losa_workspace(const sdattn_losa_problem* p, size_t* ws_bytes,
+                                               int32_t* max_union_pages);
+
+/* kp[b][g][P] = mean of k_cache[b][g][P*page .. P*page+page-1] (fp32).  The
+ * selector's page keys (section 3, the sparse selector run for the Active
+ * tokens; a per-page mean key stands in for the unnamed selector's page
+ * summary).  Run once per prefix: it does not change while a block is
+ * denoised. */
+SDATTN_API sdattn_status sdattn_losa_pool_pages(const sdattn_losa_problem* p, const void* k_cache, float* kp,
+                                                void* stream);
+
+/* The first iteration of a block (section 3, workflow: initialisation):
+ * every block query attends to the whole prefix and the whole block; writes
+ * all of o and lse, which later iterations keep for Stable tokens. */
+SDATTN_API sdattn_status sdattn_losa_dense(const sdattn_losa_problem* p, const void* q, const void* k_cache,
+                                           const void* v_cache, const void* k_blk, const void* v_blk, void* o,
+                                           float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* A later iteration (section 2, locality of representation changes;
+ * section 3, workflow steps 1-5):
+ *   1. locality[b][i] = mean over heads and channels of (q - q_prev)^2 (fp64);
+ *   2. active_idx[b][0..n_active) = the n_active largest, ties to the lower
+ *      index, listed ascending;
+ *   3. page_scores[b][h][a][P] = scale * <q[b][h][active_idx[b][a]], kp[b][g][P]>
+ *      (fp32), and each (b, h, a) row keeps its pages_per_query best pages
+ *      (score descending, page ascending);
+ *   4. union_pages[b][g][0..union_count[b][g]) = the ascending union of the
+ *      pages kept by the query heads of kv head g over all Active tokens
+ *      (capacity max_union_pages per kv head);
+ *   5. each Active query row attends to the prefix tokens of its kv head's
+ *      union and to the block's keys; o and lse rows of Active tokens are
+ *      overwritten, the rows of Stable tokens are left as they are
+ *      (section 3, reuse for Stable tokens).
+ * q_prev is the previous iteration's q.  locality and page_scores are
+ * optional outputs (NULL: not written; page_scores otherwise lives in the
+ * workspace).  All enqueued on `stream`; no host synchronisation.  Errors:
+ * SDATTN_ERR_NULL for a missing required pointer, SDATTN_ERR_WORKSPACE for
+ * a workspace below sdattn_losa_workspace, the problem errors above. */
+SDATTN_API sdattn_status sdattn_losa_step(const sdattn_losa_problem* p, const void* q, const void* q_prev,
+                                          const void* k_cache, const void* v_cache, const float* kp,
+                                          const void* k_blk, const void* v_blk, void* o, float* lse,
+                                          int32_t* active_idx, int32_t* union_pages, int32_t* union_count,
+                                          double* locality, float* page_scores, void* ws, size_t ws_bytes,
+                                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdattn.so")
 
 # ABI of include/sdattn.h that this binding marshals for (SDATTN_ABI_VERSION)
-SDATTN_ABI_VERSION = 2
+SDATTN_ABI_VERSION = 3
 
 # ---- enums ------------------------------------------------------------------
 SDATTN_OK = 0
@@ -56,6 +56,13 @@ class ScheduleDesc(ctypes.Structure):
                 ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("budget", Budget),
                 ("column_keep_frac", ctypes.c_double), ("probe_interval", ctypes.c_int32),
                 ("min_overlap", ctypes.c_double)]
+
+
+class LosaProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32),
+                ("prefix_len", ctypes.c_int32), ("block_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("softmax_scale", ctypes.c_float), ("page", ctypes.c_int32),
+                ("n_active", ctypes.c_int32), ("pages_per_query", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -98,6 +105,13 @@ _SIGS = {
     "sdattn_schedule_probe_stats": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
                                                    ctypes.POINTER(ctypes.c_double), _P]),
     "sdattn_schedule_destroy": (None, [_P]),
+    "sdattn_losa_workspace": (ctypes.c_int, [ctypes.POINTER(LosaProblem), ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(ctypes.c_int32)]),
+    "sdattn_losa_pool_pages": (ctypes.c_int, [ctypes.POINTER(LosaProblem), _P, _P, _P]),
+    "sdattn_losa_dense": (ctypes.c_int, [ctypes.POINTER(LosaProblem), _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "sdattn_losa_step": (ctypes.c_int, [ctypes.POINTER(LosaProblem), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib_handle = None
@@ -335,3 +349,40 @@ def sdattn_schedule_probe_stats(h, stream=None):
 
 def sdattn_schedule_destroy(h):
     lib().sdattn_schedule_destroy(h)
+
+
+# ---- block-wise diffusion over a cached prefix (LoSA-style) ----------------
+
+def losa_problem(batch, q_heads, kv_heads, prefix_len, block_len, head_dim, page, n_active, pages_per_query,
+                 dtype="bf16", softmax_scale=0.0):
+    dt = {"f32": SDATTN_F32, "bf16": SDATTN_BF16}[dtype] if isinstance(dtype, str) else int(dtype)
+    return LosaProblem(batch, q_heads, kv_heads, prefix_len, block_len, head_dim, dt, softmax_scale, page, n_active,
+                       pages_per_query)
+
+
+def sdattn_losa_workspace(p):
+    """Returns (ws_bytes, max_union_pages)."""
+    ws = ctypes.c_size_t(0)
+    cap = ctypes.c_int32(0)
+    _check(lib().sdattn_losa_workspace(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(cap)), "sdattn_losa_workspace")
+    return ws.value, cap.value
+
+
+def sdattn_losa_pool_pages(p, k_cache, kp, stream=None):
+    _check(lib().sdattn_losa_pool_pages(ctypes.byref(p), _ptr(k_cache), _ptr(kp), _stream(stream)),
+           "sdattn_losa_pool_pages")
+
+
+def sdattn_losa_dense(p, q, k_cache, v_cache, k_blk, v_blk, o, lse, ws, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sdattn_losa_dense(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_blk), _ptr(v_blk),
+                                   _ptr(o), _ptr(lse), _ptr(ws), ws_bytes, _stream(stream)), "sdattn_losa_dense")
+
+
+def sdattn_losa_step(p, q, q_prev, k_cache, v_cache, kp, k_blk, v_blk, o, lse, active_idx, union_pages, union_count,
+                     ws, locality=None, page_scores=None, stream=None):
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sdattn_losa_step(ctypes.byref(p), _ptr(q), _ptr(q_prev), _ptr(k_cache), _ptr(v_cache), _ptr(kp),
+                                  _ptr(k_blk), _ptr(v_blk), _ptr(o), _ptr(lse), _ptr(active_idx), _ptr(union_pages),
+                                  _ptr(union_count), _ptr(locality), _ptr(page_scores), _ptr(ws), ws_bytes,
+                                  _stream(stream)), "sdattn_losa_step")

@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 22
+    assert len(names) == 26
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
     assert set(names) == exported  # nothing missing, nothing extra
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 2
+    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 3
     hdr = open(os.path.join(ROOT, "include", "sdattn.h")).read()
     assert f"#define SDATTN_ABI_VERSION {sd.SDATTN_ABI_VERSION}" in hdr
     for i, name in enumerate(sd.STATUS_NAMES):
@@ -175,8 +175,50 @@ def test_header_and_library_from_plain_c(tmp_path):
                     "-lsdattn", f"-Wl,-rpath,{libdir}"], check=True, capture_output=True, text=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
-    assert "C client OK (ABI 2)" in r.stdout
+    assert f"C client OK (ABI {sd.SDATTN_ABI_VERSION})" in r.stdout
     cpp = tmp_path / "hdr.cpp"
     cpp.write_text('#include "sdattn.h"\nint main() { return sdattn_abi_version() == SDATTN_ABI_VERSION ? 0 : 1; }\n')
     subprocess.run(["g++", "-std=c++17", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", inc, str(cpp)],
                    check=True, capture_output=True, text=True)
+
+
+def test_losa_validation():
+    """The block-wise (LoSA-style) entry points reject bad problems and
+    missing pointers on the host, and size their workspace."""
+    lib = sd.lib()
+    ws, cap = ctypes.c_size_t(0), ctypes.c_int32(0)
+    good = sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 8)
+    assert lib.sdattn_losa_workspace(ctypes.byref(good), ctypes.byref(ws), ctypes.byref(cap)) == 0
+    assert cap.value == min(2048, 4 * 8 * 8) and ws.value > 0
+    assert lib.sdattn_losa_workspace(None, ctypes.byref(ws), ctypes.byref(cap)) == 1
+    assert lib.sdattn_losa_workspace(ctypes.byref(good), None, ctypes.byref(cap)) == 1
+    cases = [
+        (sd.losa_problem(1, 32, 5, 32768, 32, 128, 16, 8, 8), 2),      # Hq % Hkv
+        (sd.losa_problem(0, 32, 8, 32768, 32, 128, 16, 8, 8), 2),      # batch
+        (sd.losa_problem(1, 32, 8, 32768, 65, 128, 16, 8, 8), 2),      # block_len > 64
+        (sd.losa_problem(1, 32, 8, 32760, 32, 128, 16, 8, 8), 2),      # page does not divide prefix_len
+        (sd.losa_problem(1, 32, 8, 131072, 32, 128, 16, 8, 8), 2),     # more than 4096 pages
+        (sd.losa_problem(1, 32, 8, 32768, 32, 96, 16, 8, 8), 8),       # head_dim
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 8, "f32"), 8),
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 8, 7), 3),   # dtype
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 0, 8), 4),      # n_active
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 33, 8), 4),
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 0), 4),      # pages_per_query
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 2049), 4),
+        (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 8, "bf16", float("inf")), 2),
+    ]
+    for p, code in cases:
+        assert lib.sdattn_losa_workspace(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(cap)) == code, \
+            sd.sdattn_last_error()
+        assert lib.sdattn_losa_pool_pages(ctypes.byref(p), BAD, BAD, None) == code
+    # missing pointers and a short workspace fail before any launch
+    assert lib.sdattn_losa_pool_pages(ctypes.byref(good), None, BAD, None) == 1
+    assert lib.sdattn_losa_dense(ctypes.byref(good), BAD, BAD, BAD, BAD, BAD, BAD, None, BAD, 1 << 40, None) == 1
+    assert lib.sdattn_losa_dense(ctypes.byref(good), BAD, BAD, BAD, BAD, BAD, BAD, BAD, BAD, 16, None) == 5
+    step = [BAD] * 12
+    assert lib.sdattn_losa_step(ctypes.byref(good), *step, None, None, BAD, ctypes.c_size_t(16), None) == 5
+    step_missing = list(step)
+    step_missing[10] = None  # union_pages
+    assert lib.sdattn_losa_step(ctypes.byref(good), *step_missing, None, None, BAD, ctypes.c_size_t(1 << 40),
+                                None) == 1
+    assert "union_pages" in sd.sdattn_last_error()
