@@ -346,6 +346,183 @@ def compare_masks(sd, p, w, x, o, lse):
     return out
 
 
+def run_losa(args, w):
+    """Block-wise workload: a block of block_len tokens over a cached prefix.
+    A step is one denoising iteration of a block; the schedule repeats blocks
+    of steps_per_block iterations: iteration 0 computes the page means of the
+    prefix and runs the dense form, iterations 1.. run the LoSA-style step
+    (locality, Active set, page selection, union, partial attention)."""
+    import numpy as np
+    import torch
+
+    import sparse_bidirectional_attention_amd as sd
+    from workloads.generate import make_losa_base, make_losa_cache, make_losa_iteration
+
+    T = w.steps_per_block
+    K = args.steps if args.steps is not None else 64 * T
+    B, Hq, Hkv, Lp, Bs, d = w.batch, w.q_heads, w.kv_heads, w.prefix_len, w.block_len, w.head_dim
+    n_pages = Lp // w.page
+    torch.cuda.set_device(0)
+    log(f"workload {w.name}: prefix {Lp}, block {Bs}, Hq={Hq} Hkv={Hkv} d={d} {w.dtype}, page {w.page}, "
+        f"{w.n_active} Active tokens, {w.pages_per_query} pages per query; {K} steps in blocks of {T}")
+    t0 = time.time()
+    base = make_losa_base(w)
+    cache = make_losa_cache(w, base)
+    iters_h = [make_losa_iteration(w, t, base) for t in range(T)]
+    del base
+    log(f"inputs generated in {time.time() - t0:.1f} s")
+    kc, vc = to_dev(cache["k_cache"]), to_dev(cache["v_cache"])
+    its = [{n: to_dev(a) for n, a in x.items()} for x in iters_h]
+    p = sd.losa_problem(B, Hq, Hkv, Lp, Bs, d, w.page, w.n_active, w.pages_per_query)
+    ws_bytes, cap = sd.sdattn_losa_workspace(p)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    kp = torch.empty(B, Hkv, n_pages, d, dtype=torch.float32, device="cuda")
+    o = torch.empty(B, Hq, Bs, d, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, Hq, Bs, dtype=torch.float32, device="cuda")
+    active = torch.empty(B, w.n_active, dtype=torch.int32, device="cuda")
+    upages = torch.empty(B, Hkv, cap, dtype=torch.int32, device="cuda")
+    ucount = torch.empty(B, Hkv, dtype=torch.int32, device="cuda")
+
+    pool_ev = {}
+
+    def step(t, evs=None):
+        it = t % T
+        if it == 0:
+            sd.sdattn_losa_pool_pages(p, kc, kp)
+            if evs is not None:  # the dense call alone, for the roofline
+                pool_ev[t] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                pool_ev[t][0].record()
+            x = its[0]
+            sd.sdattn_losa_dense(p, x["q"], kc, vc, x["k_blk"], x["v_blk"], o, lse, ws)
+            if evs is not None:
+                pool_ev[t][1].record()
+        else:
+            x, xp = its[it], its[it - 1]
+            sd.sdattn_losa_step(p, x["q"], xp["q"], kc, vc, kp, x["k_blk"], x["v_blk"], o, lse, active, upages,
+                                ucount, ws)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    monitor = GpuMonitor()
+    if not args.no_gpu_monitor:
+        monitor.start()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for t in range(K):
+        ev[t][0].record()
+        step(t, ev)
+        ev[t][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    monitor.stop()
+    total_ms = start.elapsed_time(end)
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dense_call_ms = float(np.mean([a.elapsed_time(b) for a, b in pool_ev.values()])) if pool_ev else None
+    dense_idx = [t for t in range(K) if t % T == 0]
+    losa_idx = [t for t in range(K) if t % T != 0]
+    dense_ms = float(np.mean(step_ms[dense_idx])) if dense_idx else None
+    losa_ms = float(np.mean(step_ms[losa_idx])) if losa_idx else None
+
+    # union sizes of every iteration of one block (they repeat block after block)
+    unions = []
+    for it in range(1, T):
+        step(it)
+        torch.cuda.synchronize()
+        unions.append(ucount.cpu().numpy().astype(np.int64))
+    u_mean = float(np.mean([u.sum() for u in unions])) if unions else 0.0
+    # algorithmic work
+    G = Hq // Hkv
+    dense_flops = 4.0 * B * Hq * Bs * (Lp + Bs) * d
+    dense_bytes = 2.0 * B * Hkv * (Lp + Bs) * d * 2 + B * Hq * Bs * (d * 2 * 2 + 4)
+    losa_bytes = (u_mean * w.page * d * 2 * 2 + 2.0 * B * Hkv * Bs * d * 2 + 2.0 * B * Hq * Bs * d * 2
+                  + B * Hkv * n_pages * d * 4 + B * Hq * w.n_active * (d * 2 + 4))
+    losa_flops = 4.0 * G * w.n_active * d * (u_mean * w.page + B * Hkv * Bs) + 2.0 * B * Hq * w.n_active * n_pages * d
+    kernels = {}
+    if dense_call_ms:
+        a = dense_flops / (dense_call_ms * 1e9)
+        kernels["losa_dense_iteration"] = {
+            "bound": "alu", "achieved": round(a, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(a / PEAK_F32_TFLOPS, 4), "launch_ms": round(dense_call_ms, 4), "flops_per_launch": dense_flops,
+            "kernels": "losa_attend_kernel (dense) + losa_merge_kernel; the page means (losa_pool_kernel) run "
+                       "once per block before it", "traffic": None}
+    if losa_ms:
+        a = losa_bytes / (losa_ms * 1e6)
+        kernels["losa_step"] = {
+            "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4), "launch_ms": round(losa_ms, 4), "bytes_per_launch": losa_bytes,
+            "flops_per_launch": losa_flops,
+            "kernels": "delta, active, scores, topk, union, attend, merge (seven launches)", "traffic": None}
+    # The roofline names the heaviest single kernel: the dense iteration's
+    # attention (one C call = that kernel plus its merge, ~3% of the call).  A
+    # LoSA iteration is seven short launches and stays under "kernels".
+    dom = "losa_dense_iteration" if "losa_dense_iteration" in kernels else "losa_step"
+    roof = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
+    roof["kernel"] = dom
+    ms_per_step = total_ms / K
+    out = {
+        "metric": METRIC, "value": round(ms_per_step, 4), "unit": "ms/denoise step", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": False, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": Hkv, "prefix_len": Lp,
+                   "block_len": Bs, "head_dim": d, "page": w.page, "n_active": w.n_active,
+                   "pages_per_query": w.pages_per_query, "steps_per_block": T},
+        "roofline": roof,
+        "phases": {"dense_iteration_ms": round(dense_ms, 4) if dense_ms else None,
+                   "dense_call_ms": round(dense_call_ms, 4) if dense_call_ms else None,
+                   "losa_step_ms": round(losa_ms, 4) if losa_ms else None,
+                   "losa_step_speedup_vs_dense_iteration": round(dense_ms / losa_ms, 2) if dense_ms and losa_ms
+                   else None,
+                   "union_pages_per_step": round(u_mean, 1),
+                   "union_density": round(u_mean / (B * Hkv * n_pages), 5),
+                   "union_pages_by_iteration": [u.ravel().tolist() for u in unions]},
+        "dense_baseline": {"ms_per_step": round(dense_ms, 4) if dense_ms else None,
+                           "schedule_speedup": round(dense_ms / ms_per_step, 3) if dense_ms else None},
+        "kernels": kernels,
+        "step_times": {a: {"n": len(v), "median_ms": round(float(np.median(step_ms[v])), 4),
+                           "p10_ms": round(float(np.percentile(step_ms[v], 10)), 4),
+                           "p90_ms": round(float(np.percentile(step_ms[v], 90)), 4)}
+                       for a, v in (("DENSE", dense_idx), ("LOSA", losa_idx)) if v},
+        "wall_s": round(wall, 2),
+        "gpu_state": monitor.summary(),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host ...")
+        out["cpu_baseline"] = cpu_baseline_losa(w, cache, iters_h)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_losa(w, cache, iters):
+    """The oracle on one block's dense iteration and two later iterations,
+    weighted by the block schedule."""
+    import oracle.losa as ol
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    T = w.steps_per_block
+    t0 = time.perf_counter()
+    o, lse = ol.losa_dense(iters[0]["q"], cache["k_cache"], cache["v_cache"], iters[0]["k_blk"], iters[0]["v_blk"])
+    t_dense = time.perf_counter() - t0
+    n = min(2, T - 1)
+    t0 = time.perf_counter()
+    for it in range(1, n + 1):
+        r = ol.losa_step(iters[it]["q"], iters[it - 1]["q"], cache["k_cache"], cache["v_cache"], iters[it]["k_blk"],
+                         iters[it]["v_blk"], o, lse, w.page, w.n_active, w.pages_per_query)
+        o, lse = r["o"], r["lse"]
+    t_step = (time.perf_counter() - t0) / max(1, n)
+    ms = 1e3 * (t_dense + (T - 1) * t_step) / T
+    return {"value": round(ms, 3), "unit": "ms/denoise step", "cores": threads,
+            "host_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"fp64 numpy oracle: the dense iteration and {n} later iterations of one block, "
+                      f"weighted 1:{T - 1}",
+            "per_step_ms": {"dense": round(1e3 * t_dense, 1), "losa": round(1e3 * t_step, 1)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -372,6 +549,10 @@ def main():
         print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(sharding the heads across GPUs is not implemented); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    from workloads.configs import LOSA_WORKLOADS
+    if args.workload in LOSA_WORKLOADS:
+        run_losa(args, LOSA_WORKLOADS[args.workload])
+        return
 
     import numpy as np
     import torch

@@ -14,16 +14,17 @@
 //   6. leaves the outputs of Stable tokens as they are.
 //
 // Kernels, in stream order for one later iteration:
-//   losa_locality_kernel     one workgroup per batch row: fp64 locality score
-//                            of each block token, the Active list (ascending),
-//                            and zeroes that row's page bitmaps;
+//   losa_delta_kernel        one workgroup per block token: its fp64
+//                            locality score;
+//   losa_active_kernel       one wave per batch row: the Active list
+//                            (ascending), and zeroes that row's page bitmaps;
 //   losa_scores_kernel       page scores of every Active query row (fp32 FMA);
 //   losa_topk_kernel         one wave per Active query row: top-k pages by
 //                            (score desc, page asc), OR-ed into the bitmap;
 //   losa_union_kernel        one workgroup per (b, kv head): the ascending page
 //                            list of the bitmap and its length;
-//   losa_attend_kernel       one workgroup per (key chunk, kv head, 64-row
-//                            tile): partial softmax over the chunk's keys;
+//   losa_attend_kernel       one workgroup per (key chunk, kv head, 32- or
+//                            64-row tile): partial softmax over the chunk's keys;
 //                            the last chunk index is the block's own keys;
 //   losa_merge_kernel        one wave per query row: log-sum-exp merge of the
 //                            partials, bf16 output and fp32 LSE.
@@ -46,9 +47,8 @@ namespace {
 
 constexpr int kMaxBlockLen = 64;     // block tokens (one per lane of the locality wave)
 constexpr int kMaxPages = 4096;      // prefix pages (rows of scores held in registers)
-constexpr int kRowTile = 64;         // query rows per attention workgroup
 constexpr int kKeyTile = 64;         // keys per LDS tile
-constexpr int kChunkSparse = 128;    // keys per attention workgroup, later iterations
+constexpr int kChunkSparse = 64;     // keys per attention workgroup, later iterations
 constexpr int kChunkDense = 512;     // keys per attention workgroup, first iteration
 
 struct Dims {
@@ -58,76 +58,114 @@ struct Dims {
 
 // ---- 0. page means of the cached keys --------------------------------------
 
+// Thread = (page, 8-channel unit): a 16-byte load per page row; a workgroup
+// covers 256 / (D/8) pages.
 template <int D>
-__global__ __launch_bounds__(D) void losa_pool_kernel(const uint16_t* __restrict__ kc, float* __restrict__ kp,
-                                                      int Lp, int page, int n_pages) {
-    const int P = blockIdx.x, g = blockIdx.y, b = blockIdx.z, c = threadIdx.x;
+__global__ __launch_bounds__(256) void losa_pool_kernel(const uint16_t* __restrict__ kc, float* __restrict__ kp,
+                                                        int Lp, int page, int n_pages) {
+    constexpr int U = D / 8;
+    const int P = blockIdx.x * (256 / U) + threadIdx.x / U, u = threadIdx.x % U;
+    const int g = blockIdx.y, b = blockIdx.z;
+    if (P >= n_pages) return;
     const int64_t head = static_cast<int64_t>(b) * gridDim.y + g;
-    const uint16_t* src = kc + (head * Lp + static_cast<int64_t>(P) * page) * D + c;
-    float acc = 0.f;
-    for (int r = 0; r < page; ++r) acc += bf16_to_f32(src[static_cast<int64_t>(r) * D]);
-    kp[(head * n_pages + P) * D + c] = acc / static_cast<float>(page);
+    const uint16_t* src = kc + (head * Lp + static_cast<int64_t>(P) * page) * D + u * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < page; ++r) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r) * D);
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += __uint_as_float(w[e] << 16);
+            acc[2 * e + 1] += __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+    }
+    float* dst = kp + (head * n_pages + P) * D + u * 8;
+    const float inv = static_cast<float>(page);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = acc[e] / inv;
 }
 
 // ---- 1. locality scores and the Active list --------------------------------
 
-__global__ __launch_bounds__(256) void losa_locality_kernel(Dims dm, const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ qp,
-                                                            int32_t* __restrict__ active, double* locality,
-                                                            uint32_t* __restrict__ bitmap, int n_words) {
-    __shared__ double delta[kMaxBlockLen];
-    const int b = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t* bm = bitmap + static_cast<int64_t>(b) * dm.Hkv * n_words;
-    for (int w = threadIdx.x; w < dm.Hkv * n_words; w += 256) bm[w] = 0u;
-    const int n = dm.Hq * dm.D;
-    for (int i = wave; i < dm.Bs; i += 4) {
-        double acc = 0.0;
-        for (int e = lane; e < n; e += 64) {
-            const int h = e / dm.D, c = e - h * dm.D;
-            const int64_t off = ((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * dm.D + c;
-            const double d = static_cast<double>(bf16_to_f32(q[off])) - static_cast<double>(bf16_to_f32(qp[off]));
-            acc = fma(d, d, acc);
+// Workgroup (token i, b): delta over the Hq * D channels of the token, 16-byte
+// loads, fp64 squares and sums.
+__global__ __launch_bounds__(256) void losa_delta_kernel(Dims dm, const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ qp, double* __restrict__ delta,
+                                                         double* locality) {
+    __shared__ double part[4];
+    const int i = blockIdx.x, b = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int U = dm.D / 8, n_units = dm.Hq * U;
+    double acc = 0.0;
+    for (int k = threadIdx.x; k < n_units; k += 256) {
+        const int h = k / U, u = k - h * U;
+        const int64_t off = ((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * dm.D + u * 8;
+        const uint4 x = *reinterpret_cast<const uint4*>(q + off);
+        const uint4 y = *reinterpret_cast<const uint4*>(qp + off);
+        const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, ya[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double dl = static_cast<double>(__uint_as_float(xa[e] << 16)) -
+                              static_cast<double>(__uint_as_float(ya[e] << 16));
+            const double dh = static_cast<double>(__uint_as_float(xa[e] & 0xFFFF0000u)) -
+                              static_cast<double>(__uint_as_float(ya[e] & 0xFFFF0000u));
+            acc = fma(dl, dl, acc);
+            acc = fma(dh, dh, acc);
         }
-        acc = wave_sum(acc);
-        if (lane == 0) delta[i] = acc / static_cast<double>(n);
     }
+    acc = wave_sum(acc);
+    if (lane == 0) part[wave] = acc;
     __syncthreads();
-    if (wave != 0) return;
+    if (threadIdx.x == 0) {
+        const double dv = (part[0] + part[1] + part[2] + part[3]) / static_cast<double>(dm.Hq * dm.D);
+        delta[static_cast<int64_t>(b) * dm.Bs + i] = dv;
+        if (locality != nullptr) locality[static_cast<int64_t>(b) * dm.Bs + i] = dv;
+    }
+}
+
+// One wave per batch row: rank of every token by (delta desc, index asc);
+// the n_active first are Active, listed ascending.  Also clears the row's
+// page bitmaps for the top-k kernel.
+__global__ __launch_bounds__(64) void losa_active_kernel(Dims dm, const double* __restrict__ delta,
+                                                         int32_t* __restrict__ active, uint32_t* __restrict__ bitmap,
+                                                         int n_words) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    uint32_t* bm = bitmap + static_cast<int64_t>(b) * dm.Hkv * n_words;
+    for (int w = lane; w < dm.Hkv * n_words; w += 64) bm[w] = 0u;
+    const double* dl = delta + static_cast<int64_t>(b) * dm.Bs;
     const bool valid = lane < dm.Bs;
-    const double di = valid ? delta[lane] : 0.0;
+    const double di = valid ? dl[lane] : 0.0;
     int rank = 0;
     for (int j = 0; j < dm.Bs; ++j) {
-        const double dj = delta[j];
+        const double dj = dl[j];
         rank += (dj > di || (dj == di && j < lane)) ? 1 : 0;
     }
     const bool act = valid && rank < dm.n_a;
     const unsigned long long mask = __ballot(act);
     if (act) active[static_cast<int64_t>(b) * dm.n_a + __popcll(mask & ((1ull << lane) - 1ull))] = lane;
-    if (valid && locality != nullptr) locality[static_cast<int64_t>(b) * dm.Bs + lane] = di;
 }
 
 // ---- 2. page scores of the Active query rows --------------------------------
-// Workgroup (64-page chunk, kv head g, b).  Group row r = (query head
-// g*G + r / n_a, Active slot r % n_a).  Each wave scores 4 rows at a time,
-// one page per lane.
+// Workgroup (32-page chunk, kv head g, b).  Group row r = (query head
+// g*G + r / n_a, Active slot r % n_a).  Thread = (page t % 32, row slot
+// t / 32); 32 rows per pass, 4 per thread.
 
 template <int D>
 __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_t* __restrict__ q,
                                                           const int32_t* __restrict__ active,
                                                           const float* __restrict__ kp, float* __restrict__ scores) {
-    __shared__ float ks[64][D + 1];
-    __shared__ float qs[16][D];
-    const int P0 = blockIdx.x * 64, g = blockIdx.y, b = blockIdx.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ float ks[32][D + 1];
+    __shared__ float qs[32][D];
+    const int P0 = blockIdx.x * 32, g = blockIdx.y, b = blockIdx.z;
+    const int pg = threadIdx.x & 31, slot = threadIdx.x >> 5;
     const int64_t kvh = static_cast<int64_t>(b) * dm.Hkv + g;
-    for (int idx = threadIdx.x; idx < 64 * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < 32 * D; idx += 256) {
         const int p = idx / D, c = idx - p * D;
         ks[p][c] = P0 + p < dm.n_pages ? kp[(kvh * dm.n_pages + P0 + p) * D + c] : 0.f;
     }
     const int R = dm.G * dm.n_a;
-    for (int r0 = 0; r0 < R; r0 += 16) {
+    for (int r0 = 0; r0 < R; r0 += 32) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
+        for (int idx = threadIdx.x; idx < 32 * D; idx += 256) {
             const int rr = idx / D, c = idx - rr * D, r = r0 + rr;
             float v = 0.f;
             if (r < R) {
@@ -140,14 +178,14 @@ __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
         for (int c = 0; c < D; ++c) {
-            const float kv = ks[lane][c];
+            const float kv = ks[pg][c];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = fmaf(qs[wave * 4 + j][c], kv, acc[j]);
+            for (int j = 0; j < 4; ++j) acc[j] = fmaf(qs[slot + 8 * j][c], kv, acc[j]);
         }
-        const int P = P0 + lane;
+        const int P = P0 + pg;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = r0 + wave * 4 + j;
+            const int r = r0 + slot + 8 * j;
             if (r < R && P < dm.n_pages) {
                 const int h = g * dm.G + r / dm.n_a, a = r % dm.n_a;
                 scores[((static_cast<int64_t>(b) * dm.Hq + h) * dm.n_a + a) * dm.n_pages + P] = dm.scale * acc[j];
@@ -157,9 +195,49 @@ __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_
 }
 
 // ---- 3. per-row top-k pages into the kv head's bitmap -----------------------
-// One wave per (b, h, a) row, NPL scores per lane in registers (page
-// lane + 64 j).  Round k takes the best entry ordered after round k-1's pick
-// under (score desc, page asc), so nothing is marked or moved.
+// One wave per (b, h, a) row, NPL entries per lane in registers (page
+// lane + 64 j) as 64-bit keys: the order-preserving image of the score in the
+// high word, ~page in the low word, so a larger key is a better entry under
+// (score desc, page asc).  Round k takes the largest key below round k-1's
+// pick, so nothing is marked or moved.  Key 0 is "no entry".
+
+__device__ __forceinline__ uint64_t score_key(float v, int P) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (static_cast<uint64_t>(ord) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(P));
+}
+
+// Wave-wide max of a 64-bit key in registers: DPP moves pair every lane with
+// one in the other half of its 2, 4, 8 and 16 lanes, then v_permlane16_swap
+// and v_permlane32_swap bring in the other row and the other half-wave.
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_with_dpp(uint64_t x) {
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(x >> 32), CTRL, 0xF, 0xF, false);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(x), CTRL, 0xF, 0xF, false);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    return o > x ? o : x;
+}
+
+__device__ __forceinline__ uint64_t max_of_pair(uint32_t h0, uint32_t l0, uint32_t h1, uint32_t l1) {
+    const uint64_t a = (static_cast<uint64_t>(h0) << 32) | l0, b = (static_cast<uint64_t>(h1) << 32) | l1;
+    return a > b ? a : b;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    x = max_with_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    x = max_with_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    x = max_with_dpp<0x141>(x);  // row_half_mirror
+    x = max_with_dpp<0x140>(x);  // row_mirror
+    uint32_t hi = static_cast<uint32_t>(x >> 32), lo = static_cast<uint32_t>(x);
+    const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    x = max_of_pair(h16[0], l16[0], h16[1], l16[1]);
+    hi = static_cast<uint32_t>(x >> 32);
+    lo = static_cast<uint32_t>(x);
+    const auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    const auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    return max_of_pair(h32[0], l32[0], h32[1], l32[1]);
+}
 
 template <int NPL>
 __global__ __launch_bounds__(256) void losa_topk_kernel(Dims dm, const float* __restrict__ scores,
@@ -170,42 +248,26 @@ __global__ __launch_bounds__(256) void losa_topk_kernel(Dims dm, const float* __
     const int64_t bh = row / dm.n_a;  // b * Hq + h
     const int b = static_cast<int>(bh / dm.Hq), h = static_cast<int>(bh % dm.Hq);
     const float* sr = scores + row * dm.n_pages;
-    float vals[NPL];
+    uint64_t keys[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const int P = lane + 64 * j;
-        vals[j] = P < dm.n_pages ? sr[P] : 0.f;
+        keys[j] = P < dm.n_pages ? score_key(sr[P], P) : 0ull;
     }
     uint32_t* bm = bitmap + (static_cast<int64_t>(b) * dm.Hkv + h / dm.G) * n_words;
-    float pv = INFINITY;
-    int pp = -1;
+    uint64_t prev = ~0ull;
     for (int k = 0; k < dm.kpq; ++k) {
-        float bv = -INFINITY;
-        int bp = INT_MAX;
+        uint64_t best = 0ull;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
-            const int P = lane + 64 * j;
-            const float v = vals[j];
-            const bool after = v < pv || (v == pv && P > pp);
-            const bool better = v > bv || (v == bv && P < bp);
-            if (P < dm.n_pages && after && better) {
-                bv = v;
-                bp = P;
-            }
+            const uint64_t x = keys[j];
+            best = (x < prev && x > best) ? x : best;
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int op = __shfl_xor(bp, off, 64);
-            if (ov > bv || (ov == bv && op < bp)) {
-                bv = ov;
-                bp = op;
-            }
-        }
-        if (bp >= dm.n_pages) break;  // no orderable entry left (non-finite scores)
-        pv = bv;
-        pp = bp;
-        if (lane == 0) atomicOr(&bm[bp >> 5], 1u << (bp & 31));
+        best = wave_max_u64(best);
+        if (best == 0ull) break;  // fewer orderable entries than kpq
+        prev = best;
+        const int P = static_cast<int>(~static_cast<uint32_t>(best));
+        if (lane == 0) atomicOr(&bm[P >> 5], 1u << (P & 31));
     }
 }
 
@@ -230,7 +292,11 @@ __global__ __launch_bounds__(256) void losa_union_kernel(int Hkv, const uint32_t
     if (threadIdx.x == 0) union_count[kvh] = total;
 }
 
-// ---- 5. partial softmax of a 64-row tile over one key chunk -------------------
+// ---- 5. partial softmax of a row tile over one key chunk ---------------------
+// RPT rows per thread row-block: a tile of RT = 16 * RPT query rows (32 or
+// 64).  Scores: thread (row block t / 16, key column t % 16) holds RPT rows x
+// keys {t % 16 + 16 j}.  Softmax: 256 / RT lanes per row.  PV: the same row
+// block x D / 16 output channels.
 
 struct AttendArgs {
     Dims dm;
@@ -242,21 +308,24 @@ struct AttendArgs {
     const int32_t* active;       // Active list [B][n_a]; unused when dense
     const int32_t* upages;       // union pages [B][Hkv][cap]; unused when dense
     const int32_t* ucount;       // union lengths [B][Hkv]; unused when dense
-    float* part;                 // partials [B][Hkv][row_tiles*64][n_chunks+1][D+2]
+    float* part;                 // partials [B][Hkv][row_tiles*RT][n_chunks+1][D+4]: o, m, l, 2 pad
     int cap, R, row_tiles, chunk, n_chunks, dense;
     float scale_log2;            // scale * log2(e)
 };
 
-template <int D>
+template <int D, int RPT>
 __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
-    constexpr int QW = D / 2 + 4;  // LDS row stride of Q and K tiles in 32-bit words (16-byte aligned, odd bank step)
-    constexpr int VU = D / 8;      // 16-byte units per row
-    constexpr int DT = D / 16;     // output dims per thread
-    __shared__ __align__(16) uint32_t qs[kRowTile * QW];
+    constexpr int RT = 16 * RPT;      // rows per tile
+    constexpr int QW = D / 2 + 4;     // LDS row stride of Q and K tiles in 32-bit words (16-byte aligned, odd bank step)
+    constexpr int VU = D / 8;         // 16-byte units per row
+    constexpr int DT = D / 16;        // output channels per thread
+    constexpr int TPR = 256 / RT;     // softmax lanes per row
+    constexpr int KPL = kKeyTile / TPR;
+    __shared__ __align__(16) uint32_t qs[RT * QW];
     __shared__ __align__(16) uint32_t ks[kKeyTile * QW];
     __shared__ __align__(16) uint4 vs[kKeyTile * VU];
-    __shared__ float ss[kRowTile][kKeyTile + 1];
-    __shared__ float m_s[kRowTile], l_s[kRowTile], al_s[kRowTile];
+    __shared__ float ss[RT][kKeyTile + 1];
+    __shared__ float m_s[RT], l_s[RT], al_s[RT];
 
     const Dims& dm = a.dm;
     const int c = blockIdx.x;
@@ -271,12 +340,12 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         n_keys = min(a.chunk, total - c * a.chunk);
         if (n_keys <= 0) return;  // past the union: the merge reads only chunks below its length
     }
-    const int r0 = rt * kRowTile;
-    const int nrows = min(kRowTile, a.R - r0);
+    const int r0 = rt * RT;
+    const int nrows = min(RT, a.R - r0);
     const int n_a = a.dense ? dm.Bs : dm.n_a;
     const int t = threadIdx.x;
 
-    for (int idx = t; idx < kRowTile * VU; idx += 256) {
+    for (int idx = t; idx < RT * VU; idx += 256) {
         const int rr = idx / VU, u = idx - rr * VU;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (rr < nrows) {
@@ -287,15 +356,15 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         }
         *reinterpret_cast<uint4*>(&qs[rr * QW + u * 4]) = v;
     }
-    if (t < kRowTile) {
+    if (t < RT) {
         m_s[t] = -INFINITY;
         l_s[t] = 0.f;
     }
 
-    const int rb = t >> 4, kb = t & 15;  // scores: rows 4rb..4rb+3, keys kb + 16j; PV: dims kb*DT..
-    float o[4][DT];
+    const int rb = t >> 4, kb = t & 15;
+    float o[RPT][DT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RPT; ++i)
 #pragma unroll
         for (int e = 0; e < DT; ++e) o[i][e] = 0.f;
 
@@ -326,55 +395,49 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         }
         __syncthreads();
 
-        float acc[4][4];
+        float acc[RPT][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < RPT; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+        // q.k over channel pairs: v_dot2_f32_bf16 takes the packed bf16 pairs as stored
+#pragma unroll 4
         for (int w2 = 0; w2 < D / 2; ++w2) {
-            float qlo[4], qhi[4], klo[4], khi[4];
+            bf16x2 qv[RPT], kv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = qs[(rb * 4 + i) * QW + w2];
-                qlo[i] = __uint_as_float(x << 16);
-                qhi[i] = __uint_as_float(x & 0xFFFF0000u);
-            }
+            for (int i = 0; i < RPT; ++i) qv[i] = __builtin_bit_cast(bf16x2, qs[(rb * RPT + i) * QW + w2]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t x = ks[(kb + 16 * j) * QW + w2];
-                klo[j] = __uint_as_float(x << 16);
-                khi[j] = __uint_as_float(x & 0xFFFF0000u);
-            }
+            for (int j = 0; j < 4; ++j) kv[j] = __builtin_bit_cast(bf16x2, ks[(kb + 16 * j) * QW + w2]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < RPT; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(qhi[i], khi[j], fmaf(qlo[i], klo[j], acc[i][j]));
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_fdot2_f32_bf16(qv[i], kv[j], acc[i][j], false);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < RPT; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                ss[rb * 4 + i][kb + 16 * j] = kb + 16 * j < nk ? acc[i][j] * a.scale_log2 : -INFINITY;
+                ss[rb * RPT + i][kb + 16 * j] = kb + 16 * j < nk ? acc[i][j] * a.scale_log2 : -INFINITY;
         __syncthreads();
 
-        {  // online softmax: 4 lanes per row, keys part + 4j
-            const int row = t >> 2, pt = t & 3;
+        {  // online softmax: TPR lanes per row, keys pt + TPR j
+            const int row = t / TPR, pt = t % TPR;
             float mx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, ss[row][pt + 4 * j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 2, 64));
+            for (int j = 0; j < KPL; ++j) mx = fmaxf(mx, ss[row][pt + TPR * j]);
+#pragma unroll
+            for (int off = 1; off < TPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
             const float m_old = m_s[row];
             const float m_new = fmaxf(m_old, mx);
             float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float p = exp2f(ss[row][pt + 4 * j] - m_new);
-                ss[row][pt + 4 * j] = p;
+            for (int j = 0; j < KPL; ++j) {
+                const float p = exp2f(ss[row][pt + TPR * j] - m_new);
+                ss[row][pt + TPR * j] = p;
                 sum += p;
             }
-            sum += __shfl_xor(sum, 1, 64);
-            sum += __shfl_xor(sum, 2, 64);
+#pragma unroll
+            for (int off = 1; off < TPR; off <<= 1) sum += __shfl_xor(sum, off, 64);
             if (pt == 0) {
                 const float alpha = exp2f(m_old - m_new);
                 l_s[row] = l_s[row] * alpha + sum;
@@ -385,8 +448,8 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         __syncthreads();
 
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float al = al_s[rb * 4 + i];
+        for (int i = 0; i < RPT; ++i) {
+            const float al = al_s[rb * RPT + i];
 #pragma unroll
             for (int e = 0; e < DT; ++e) o[i][e] *= al;
         }
@@ -410,8 +473,8 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = ss[rb * 4 + i][kk];
+            for (int i = 0; i < RPT; ++i) {
+                const float p = ss[rb * RPT + i][kk];
 #pragma unroll
                 for (int e = 0; e < DT; ++e) o[i][e] = fmaf(p, v[e], o[i][e]);
             }
@@ -421,10 +484,10 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
 
     const int parts = a.n_chunks + 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = rb * 4 + i;
+    for (int i = 0; i < RPT; ++i) {
+        const int rr = rb * RPT + i;
         if (rr >= nrows) continue;
-        float* dst = a.part + ((kvh * a.row_tiles * kRowTile + r0 + rr) * parts + c) * (D + 2);
+        float* dst = a.part + ((kvh * a.row_tiles * RT + r0 + rr) * parts + c) * (D + 4);
 #pragma unroll
         for (int e = 0; e < DT; ++e) dst[kb * DT + e] = o[i][e];
         if (kb == 0) {
@@ -435,6 +498,11 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
 }
 
 // ---- 6. merge of the partials -------------------------------------------------
+// One wave per query row.  The maximum M of the partials' m comes first
+// (lanes over partials); then lane (group cg = lane / 16, column cl =
+// lane % 16) accumulates channels cl*D/16 .. of partials cg, cg + 4, ... with
+// weight 2^(m - M), so four partials' loads are in flight per step; the four
+// groups are summed with shuffles.
 
 struct MergeArgs {
     Dims dm;
@@ -443,13 +511,14 @@ struct MergeArgs {
     const int32_t* ucount;
     uint16_t* o;
     float* lse;
-    int R, row_tiles, chunk, n_chunks, dense;
+    int R, RT, row_tiles, chunk, n_chunks, dense;
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void losa_merge_kernel(MergeArgs a) {
+    constexpr int DC = D / 16;  // channels per lane
     const Dims& dm = a.dm;
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, cg = lane >> 4, cl = lane & 15;
     const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int64_t n_rows = static_cast<int64_t>(dm.B) * dm.Hkv * a.R;
     if (row >= n_rows) return;
@@ -460,28 +529,49 @@ __global__ __launch_bounds__(256) void losa_merge_kernel(MergeArgs a) {
     const int h = g * dm.G + r / n_a, s = r % n_a;
     const int i = a.dense ? s : a.active[static_cast<int64_t>(b) * dm.n_a + s];
     const int parts = a.n_chunks + 1;
+    // entries k = 0 .. n_valid - 1 are prefix chunks, entry n_valid is the block's keys (chunk n_chunks)
     const int n_valid = a.dense ? a.n_chunks : (a.ucount[kvh] * dm.page + a.chunk - 1) / a.chunk;
-    const float* base = a.part + (kvh * a.row_tiles * kRowTile + r) * static_cast<int64_t>(parts) * (D + 2);
+    const float* base = a.part + (kvh * a.row_tiles * a.RT + r) * static_cast<int64_t>(parts) * (D + 4);
+    auto entry = [&](int k) { return base + static_cast<int64_t>(k == n_valid ? a.n_chunks : k) * (D + 4); };
 
-    float M = base[static_cast<int64_t>(a.n_chunks) * (D + 2) + D];  // the block's keys: always present
-    for (int c = 0; c < n_valid; ++c) M = fmaxf(M, base[static_cast<int64_t>(c) * (D + 2) + D]);
-    constexpr int E = D / 64;
-    float acc[E];
+    float M = -INFINITY;
+    for (int k = lane; k <= n_valid; k += 64) M = fmaxf(M, entry(k)[D]);
+    M = wave_max(M);
+    float acc[DC];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int e = 0; e < DC; ++e) acc[e] = 0.f;
     float L = 0.f;
-    for (int k = 0; k <= n_valid; ++k) {
-        const int c = k == n_valid ? a.n_chunks : k;
-        const float* p = base + static_cast<int64_t>(c) * (D + 2);
+#pragma unroll 2
+    for (int k = cg; k <= n_valid; k += 4) {
+        const float* p = entry(k);
         const float w = exp2f(p[D] - M);
-        L = fmaf(p[D + 1], w, L);
+        if (cl == 0) L = fmaf(p[D + 1], w, L);
+        const float4* x = reinterpret_cast<const float4*>(p + cl * DC);
 #pragma unroll
-        for (int e = 0; e < E; ++e) acc[e] = fmaf(p[lane + 64 * e], w, acc[e]);
+        for (int e = 0; e < DC / 4; ++e) {
+            const float4 v = x[e];
+            acc[4 * e] = fmaf(v.x, w, acc[4 * e]);
+            acc[4 * e + 1] = fmaf(v.y, w, acc[4 * e + 1]);
+            acc[4 * e + 2] = fmaf(v.z, w, acc[4 * e + 2]);
+            acc[4 * e + 3] = fmaf(v.w, w, acc[4 * e + 3]);
+        }
     }
-    const float inv = 1.f / L;
-    uint16_t* dst = a.o + ((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * D;
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[lane + 64 * e] = static_cast<uint16_t>(pack_bf16x2(acc[e] * inv, 0.f) & 0xFFFFu);
+    for (int e = 0; e < DC; ++e) {
+        acc[e] += __shfl_xor(acc[e], 16, 64);
+        acc[e] += __shfl_xor(acc[e], 32, 64);
+    }
+    L = wave_sum(L);
+    if (cg != 0) return;
+    const float inv = 1.f / L;
+    uint32_t packed[DC / 2];
+#pragma unroll
+    for (int e = 0; e < DC / 2; ++e) packed[e] = pack_bf16x2(acc[2 * e] * inv, acc[2 * e + 1] * inv);
+    uint16_t* dst = a.o + ((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * D + cl * DC;
+    if constexpr (DC == 8)
+        *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
     if (lane == 0) a.lse[(static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i] = (M + log2f(L)) * 0.6931471805599453f;
 }
 
@@ -490,12 +580,14 @@ __global__ __launch_bounds__(256) void losa_merge_kernel(MergeArgs a) {
 struct Plan {
     Dims dm;
     int n_words, cap, npl;
-    int R_s, rt_s, nch_s;      // later iterations
-    int R_d, rt_d, nch_d;      // first iteration
-    size_t off_scores, off_bits, off_part, ws_step, ws_dense;
+    int R_s, RT_s, rt_s, nch_s;    // later iterations: rows per kv head, tile rows, tiles, prefix chunks
+    int R_d, RT_d, rt_d, nch_d;    // first iteration
+    size_t off_scores, off_bits, off_delta, off_part, ws_step, ws_dense;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int tile_rows(int R) { return R <= 32 ? 32 : 64; }
 
 sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     if (p == nullptr) return fail(SDATTN_ERR_NULL, "problem must be non-NULL");
@@ -518,8 +610,8 @@ sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     if (!(scale > 0.f)) scale = 1.f / sqrtf(static_cast<float>(p->head_dim));
     if (!isfinite(scale)) return fail(SDATTN_ERR_SHAPE, "softmax_scale must be finite");
     const int64_t G = p->q_heads / p->kv_heads;
-    if (p->batch > 65535 || static_cast<int64_t>(p->kv_heads) * ((G * p->block_len + kRowTile - 1) / kRowTile) > 65535)
-        return fail(SDATTN_ERR_SHAPE, "batch and kv_heads * ceil(q_heads/kv_heads * block_len / 64) must be <= 65535");
+    if (p->batch > 65535 || static_cast<int64_t>(p->kv_heads) * ((G * p->block_len + 31) / 32) > 65535)
+        return fail(SDATTN_ERR_SHAPE, "batch and kv_heads * ceil(q_heads/kv_heads * block_len / 32) must be <= 65535");
 
     Plan pl;
     Dims& dm = pl.dm;
@@ -539,18 +631,22 @@ sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     pl.npl = 8;
     while (pl.npl * 64 < n_pages) pl.npl *= 2;
     pl.R_s = dm.G * dm.n_a;
-    pl.rt_s = (pl.R_s + kRowTile - 1) / kRowTile;
+    pl.RT_s = tile_rows(pl.R_s);
+    pl.rt_s = (pl.R_s + pl.RT_s - 1) / pl.RT_s;
     pl.cap = static_cast<int>(std::min<int64_t>(n_pages, static_cast<int64_t>(pl.R_s) * dm.kpq));
     pl.nch_s = static_cast<int>((static_cast<int64_t>(pl.cap) * dm.page + kChunkSparse - 1) / kChunkSparse);
     pl.R_d = dm.G * dm.Bs;
-    pl.rt_d = (pl.R_d + kRowTile - 1) / kRowTile;
+    pl.RT_d = tile_rows(pl.R_d);
+    pl.rt_d = (pl.R_d + pl.RT_d - 1) / pl.RT_d;
     pl.nch_d = (dm.Lp + kChunkDense - 1) / kChunkDense;
-    const size_t part_row = static_cast<size_t>(dm.D + 2) * sizeof(float);
+    const size_t part_row = static_cast<size_t>(dm.D + 4) * sizeof(float);  // 16-byte multiple
     pl.off_scores = 0;
     pl.off_bits = align256(static_cast<size_t>(dm.B) * dm.Hq * dm.n_a * n_pages * sizeof(float));
-    pl.off_part = pl.off_bits + align256(static_cast<size_t>(dm.B) * dm.Hkv * pl.n_words * sizeof(uint32_t));
-    pl.ws_step = pl.off_part + static_cast<size_t>(dm.B) * dm.Hkv * pl.rt_s * kRowTile * (pl.nch_s + 1) * part_row;
-    pl.ws_dense = static_cast<size_t>(dm.B) * dm.Hkv * pl.rt_d * kRowTile * (pl.nch_d + 1) * part_row;
+    pl.off_delta = pl.off_bits + align256(static_cast<size_t>(dm.B) * dm.Hkv * pl.n_words * sizeof(uint32_t));
+    pl.off_part = pl.off_delta + align256(static_cast<size_t>(dm.B) * dm.Bs * sizeof(double));
+    pl.ws_step = pl.off_part +
+                 static_cast<size_t>(dm.B) * dm.Hkv * pl.rt_s * pl.RT_s * (pl.nch_s + 1) * part_row;
+    pl.ws_dense = static_cast<size_t>(dm.B) * dm.Hkv * pl.rt_d * pl.RT_d * (pl.nch_d + 1) * part_row;
     *out = pl;
     return SDATTN_OK;
 }
@@ -579,12 +675,17 @@ void launch_attend_merge(const Plan& pl, bool dense, const void* q, const void* 
     a.part = part;
     a.cap = pl.cap;
     a.R = dense ? pl.R_d : pl.R_s;
+    const int RT = dense ? pl.RT_d : pl.RT_s;
     a.row_tiles = dense ? pl.rt_d : pl.rt_s;
     a.chunk = dense ? kChunkDense : kChunkSparse;
     a.n_chunks = dense ? pl.nch_d : pl.nch_s;
     a.dense = dense ? 1 : 0;
     a.scale_log2 = dm.scale * kLog2e;
-    hipLaunchKernelGGL(losa_attend_kernel<D>, dim3(a.n_chunks + 1, dm.Hkv * a.row_tiles, dm.B), dim3(256), 0, st, a);
+    const dim3 grid(a.n_chunks + 1, dm.Hkv * a.row_tiles, dm.B);
+    if (RT == 32)
+        hipLaunchKernelGGL((losa_attend_kernel<D, 2>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((losa_attend_kernel<D, 4>), grid, dim3(256), 0, st, a);
     MergeArgs m;
     m.dm = dm;
     m.part = part;
@@ -593,6 +694,7 @@ void launch_attend_merge(const Plan& pl, bool dense, const void* q, const void* 
     m.o = static_cast<uint16_t*>(o);
     m.lse = lse;
     m.R = a.R;
+    m.RT = RT;
     m.row_tiles = a.row_tiles;
     m.chunk = a.chunk;
     m.n_chunks = a.n_chunks;
@@ -630,12 +732,13 @@ sdattn_status sdattn_losa_pool_pages(const sdattn_losa_problem* p, const void* k
     if (k_cache == nullptr || kp == nullptr) return fail(SDATTN_ERR_NULL, "k_cache and kp must be non-NULL");
     const Dims& dm = pl.dm;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 grid(dm.n_pages, dm.Hkv, dm.B);
+    const int ppw = 256 / (dm.D / 8);  // pages per workgroup
+    const dim3 grid((dm.n_pages + ppw - 1) / ppw, dm.Hkv, dm.B);
     if (dm.D == 128)
-        hipLaunchKernelGGL(losa_pool_kernel<128>, grid, dim3(128), 0, st, static_cast<const uint16_t*>(k_cache), kp,
+        hipLaunchKernelGGL(losa_pool_kernel<128>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(k_cache), kp,
                            dm.Lp, dm.page, dm.n_pages);
     else
-        hipLaunchKernelGGL(losa_pool_kernel<64>, grid, dim3(64), 0, st, static_cast<const uint16_t*>(k_cache), kp,
+        hipLaunchKernelGGL(losa_pool_kernel<64>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(k_cache), kp,
                            dm.Lp, dm.page, dm.n_pages);
     return hip_status("sdattn_losa_pool_pages");
 }
@@ -685,9 +788,11 @@ sdattn_status sdattn_losa_step(const sdattn_losa_problem* p, const void* q, cons
     float* part = reinterpret_cast<float*>(w + pl.off_part);
     const uint16_t* q16 = static_cast<const uint16_t*>(q);
 
-    hipLaunchKernelGGL(losa_locality_kernel, dim3(dm.B), dim3(256), 0, st, dm, q16,
-                       static_cast<const uint16_t*>(q_prev), active_idx, locality, bits, pl.n_words);
-    const dim3 sgrid((dm.n_pages + 63) / 64, dm.Hkv, dm.B);
+    double* delta = reinterpret_cast<double*>(w + pl.off_delta);
+    hipLaunchKernelGGL(losa_delta_kernel, dim3(dm.Bs, dm.B), dim3(256), 0, st, dm, q16,
+                       static_cast<const uint16_t*>(q_prev), delta, locality);
+    hipLaunchKernelGGL(losa_active_kernel, dim3(dm.B), dim3(64), 0, st, dm, delta, active_idx, bits, pl.n_words);
+    const dim3 sgrid((dm.n_pages + 31) / 32, dm.Hkv, dm.B);
     if (dm.D == 128)
         hipLaunchKernelGGL(losa_scores_kernel<128>, sgrid, dim3(256), 0, st, dm, q16, active_idx, kp, scores);
     else
