@@ -323,8 +323,9 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
     constexpr int KPL = kKeyTile / TPR;
     __shared__ __align__(16) uint32_t qs[RT * QW];
     __shared__ __align__(16) uint32_t ks[kKeyTile * QW];
-    __shared__ __align__(16) uint4 vs[kKeyTile * VU];
+    __shared__ __align__(16) uint4 vp[(kKeyTile / 2) * (D / 4)];  // V as key pairs: word (m, c) = {v[2m][c], v[2m+1][c]}
     __shared__ float ss[RT][kKeyTile + 1];
+    __shared__ uint32_t ps[RT][kKeyTile / 2 + 1];                   // P as bf16 key pairs
     __shared__ float m_s[RT], l_s[RT], al_s[RT];
 
     const Dims& dm = a.dm;
@@ -368,30 +369,38 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int e = 0; e < DT; ++e) o[i][e] = 0.f;
 
+    // row of key kk of the current tile in its K/V tensor (the block's own, or the cache)
+    auto key_row = [&](int k0, int kk) -> int64_t {
+        if (suffix) return kvh * dm.Bs + k0 + kk;
+        const int j = c * a.chunk + k0 + kk;
+        const int pos = a.dense ? j : a.upages[kvh * a.cap + j / dm.page] * dm.page + j % dm.page;
+        return kvh * dm.Lp + pos;
+    };
+    const uint16_t* kbase = suffix ? a.kb : a.kc;
+    const uint16_t* vbase = suffix ? a.vb : a.vc;
+
     for (int k0 = 0; k0 < n_keys; k0 += kKeyTile) {
         const int nk = min(kKeyTile, n_keys - k0);
         for (int idx = t; idx < kKeyTile * VU; idx += 256) {
             const int kk = idx / VU, u = idx - kk * VU;
-            uint4 kv = make_uint4(0u, 0u, 0u, 0u), vv = kv;
-            if (kk < nk) {
-                int64_t row;
-                const uint16_t *kbase, *vbase;
-                if (suffix) {
-                    row = kvh * dm.Bs + k0 + kk;
-                    kbase = a.kb;
-                    vbase = a.vb;
-                } else {
-                    const int j = c * a.chunk + k0 + kk;
-                    const int pos = a.dense ? j : a.upages[kvh * a.cap + j / dm.page] * dm.page + j % dm.page;
-                    row = kvh * dm.Lp + pos;
-                    kbase = a.kc;
-                    vbase = a.vc;
-                }
-                kv = *reinterpret_cast<const uint4*>(kbase + row * D + u * 8);
-                vv = *reinterpret_cast<const uint4*>(vbase + row * D + u * 8);
-            }
+            uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+            if (kk < nk) kv = *reinterpret_cast<const uint4*>(kbase + key_row(k0, kk) * D + u * 8);
             *reinterpret_cast<uint4*>(&ks[kk * QW + u * 4]) = kv;
-            vs[kk * VU + u] = vv;
+        }
+        for (int idx = t; idx < (kKeyTile / 2) * VU; idx += 256) {
+            const int m = idx / VU, u = idx - m * VU;
+            uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
+            if (2 * m < nk) x0 = *reinterpret_cast<const uint4*>(vbase + key_row(k0, 2 * m) * D + u * 8);
+            if (2 * m + 1 < nk) x1 = *reinterpret_cast<const uint4*>(vbase + key_row(k0, 2 * m + 1) * D + u * 8);
+            const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
+            uint32_t w[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                w[2 * e] = (a0[e] & 0xFFFFu) | (a1[e] << 16);               // channel 2e of keys 2m, 2m+1
+                w[2 * e + 1] = (a0[e] >> 16) | (a1[e] & 0xFFFF0000u);      // channel 2e+1
+            }
+            vp[m * (D / 4) + 2 * u] = make_uint4(w[0], w[1], w[2], w[3]);
+            vp[m * (D / 4) + 2 * u + 1] = make_uint4(w[4], w[5], w[6], w[7]);
         }
         __syncthreads();
 
@@ -420,21 +429,25 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
                 ss[rb * RPT + i][kb + 16 * j] = kb + 16 * j < nk ? acc[i][j] * a.scale_log2 : -INFINITY;
         __syncthreads();
 
-        {  // online softmax: TPR lanes per row, keys pt + TPR j
+        {  // online softmax: TPR lanes per row, key pairs pt + TPR j; P stored as bf16 pairs
             const int row = t / TPR, pt = t % TPR;
             float mx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) mx = fmaxf(mx, ss[row][pt + TPR * j]);
+            for (int j = 0; j < KPL / 2; ++j) {
+                const int m = pt + TPR * j;
+                mx = fmaxf(mx, fmaxf(ss[row][2 * m], ss[row][2 * m + 1]));
+            }
 #pragma unroll
             for (int off = 1; off < TPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
             const float m_old = m_s[row];
             const float m_new = fmaxf(m_old, mx);
             float sum = 0.f;
 #pragma unroll
-            for (int j = 0; j < KPL; ++j) {
-                const float p = exp2f(ss[row][pt + TPR * j] - m_new);
-                ss[row][pt + TPR * j] = p;
-                sum += p;
+            for (int j = 0; j < KPL / 2; ++j) {
+                const int m = pt + TPR * j;
+                const float p0 = exp2f(ss[row][2 * m] - m_new), p1 = exp2f(ss[row][2 * m + 1] - m_new);
+                ps[row][m] = pack_bf16x2(p0, p1);
+                sum += p0 + p1;
             }
 #pragma unroll
             for (int off = 1; off < TPR; off <<= 1) sum += __shfl_xor(sum, off, 64);
@@ -453,30 +466,24 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
 #pragma unroll
             for (int e = 0; e < DT; ++e) o[i][e] *= al;
         }
-        for (int kk = 0; kk < nk; ++kk) {
-            float v[DT];
-            if constexpr (DT == 8) {
-                const uint4 x = vs[kk * VU + kb];
-                const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        // p.v over key pairs with v_dot2_f32_bf16: P pairs from ps, V pairs from vp
+        const int n_pairs = (nk + 1) / 2;
+        for (int m = 0; m < n_pairs; ++m) {
+            uint32_t vw[DT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[2 * e] = __uint_as_float(w[e] << 16);
-                    v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-                }
-            } else {
-                const uint2 x = reinterpret_cast<const uint2*>(vs)[kk * (D / 4) + kb];
-                const uint32_t w[2] = {x.x, x.y};
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    v[2 * e] = __uint_as_float(w[e] << 16);
-                    v[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-                }
+            for (int q4 = 0; q4 < DT / 4; ++q4) {
+                const uint4 x = vp[m * (D / 4) + kb * (DT / 4) + q4];
+                vw[4 * q4] = x.x;
+                vw[4 * q4 + 1] = x.y;
+                vw[4 * q4 + 2] = x.z;
+                vw[4 * q4 + 3] = x.w;
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const float p = ss[rb * RPT + i][kk];
+                const bf16x2 pp = __builtin_bit_cast(bf16x2, ps[rb * RPT + i][m]);
 #pragma unroll
-                for (int e = 0; e < DT; ++e) o[i][e] = fmaf(p, v[e], o[i][e]);
+                for (int e = 0; e < DT; ++e)
+                    o[i][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vw[e]), o[i][e], false);
             }
         }
         __syncthreads();
