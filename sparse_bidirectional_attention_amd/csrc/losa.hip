@@ -16,9 +16,9 @@
 // Kernels, in stream order for one later iteration:
 //   losa_delta_kernel        one workgroup per block token: its fp64
 //                            locality score;
-//   losa_active_kernel       one wave per batch row: the Active list
-//                            (ascending), and zeroes that row's page bitmaps;
-//   losa_scores_kernel       page scores of every Active query row (fp32 FMA);
+//   losa_scores_kernel       the Active list (ascending; every workgroup ranks
+//                            the block's tokens), page scores of every Active
+//                            query row (fp32 FMA), and clears the page bitmaps;
 //   losa_topk_kernel         one wave per Active query row: top-k pages by
 //                            (score desc, page asc), OR-ed into the bitmap;
 //   losa_union_kernel        one workgroup per (b, kv head): the ascending page
@@ -122,42 +122,46 @@ __global__ __launch_bounds__(256) void losa_delta_kernel(Dims dm, const uint16_t
     }
 }
 
-// One wave per batch row: rank of every token by (delta desc, index asc);
-// the n_active first are Active, listed ascending.  Also clears the row's
-// page bitmaps for the top-k kernel.
-__global__ __launch_bounds__(64) void losa_active_kernel(Dims dm, const double* __restrict__ delta,
-                                                         int32_t* __restrict__ active, uint32_t* __restrict__ bitmap,
-                                                         int n_words) {
-    const int b = blockIdx.x, lane = threadIdx.x;
-    uint32_t* bm = bitmap + static_cast<int64_t>(b) * dm.Hkv * n_words;
-    for (int w = lane; w < dm.Hkv * n_words; w += 64) bm[w] = 0u;
-    const double* dl = delta + static_cast<int64_t>(b) * dm.Bs;
-    const bool valid = lane < dm.Bs;
-    const double di = valid ? dl[lane] : 0.0;
-    int rank = 0;
-    for (int j = 0; j < dm.Bs; ++j) {
-        const double dj = dl[j];
-        rank += (dj > di || (dj == di && j < lane)) ? 1 : 0;
-    }
-    const bool act = valid && rank < dm.n_a;
-    const unsigned long long mask = __ballot(act);
-    if (act) active[static_cast<int64_t>(b) * dm.n_a + __popcll(mask & ((1ull << lane) - 1ull))] = lane;
-}
-
-// ---- 2. page scores of the Active query rows --------------------------------
-// Workgroup (32-page chunk, kv head g, b).  Group row r = (query head
-// g*G + r / n_a, Active slot r % n_a).  Thread = (page t % 32, row slot
-// t / 32); 32 rows per pass, 4 per thread.
+// ---- 2. the Active set and the page scores of its query rows ----------------
+// Workgroup (32-page chunk, kv head g, b).  Wave 0 ranks the block's tokens by
+// (delta desc, index asc) into the Active list (ascending); the workgroups of
+// chunk 0 also write that list out (kv head 0) and clear the kv head's page
+// bitmap for the top-k kernel.  Group row r = (query head g*G + r / n_a,
+// Active slot r % n_a).  Thread = (page t % 32, row slot t / 32); 32 rows per
+// pass, 4 per thread.
 
 template <int D>
 __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_t* __restrict__ q,
-                                                          const int32_t* __restrict__ active,
+                                                          const double* __restrict__ delta,
+                                                          int32_t* __restrict__ active_out,
+                                                          uint32_t* __restrict__ bitmap, int n_words,
                                                           const float* __restrict__ kp, float* __restrict__ scores) {
     __shared__ float ks[32][D + 1];
     __shared__ float qs[32][D];
+    __shared__ int act[kMaxBlockLen];
     const int P0 = blockIdx.x * 32, g = blockIdx.y, b = blockIdx.z;
     const int pg = threadIdx.x & 31, slot = threadIdx.x >> 5;
     const int64_t kvh = static_cast<int64_t>(b) * dm.Hkv + g;
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const double* dl = delta + static_cast<int64_t>(b) * dm.Bs;
+        const bool valid = lane < dm.Bs;
+        const double di = valid ? dl[lane] : 0.0;
+        int rank = 0;
+        for (int j = 0; j < dm.Bs; ++j) {
+            const double dj = dl[j];
+            rank += (dj > di || (dj == di && j < lane)) ? 1 : 0;
+        }
+        const bool is_act = valid && rank < dm.n_a;
+        const unsigned long long mask = __ballot(is_act);
+        if (is_act) {
+            const int pos = __popcll(mask & ((1ull << lane) - 1ull));
+            act[pos] = lane;
+            if (blockIdx.x == 0 && g == 0) active_out[static_cast<int64_t>(b) * dm.n_a + pos] = lane;
+        }
+    }
+    if (blockIdx.x == 0)
+        for (int w = threadIdx.x; w < n_words; w += 256) bitmap[kvh * n_words + w] = 0u;
     for (int idx = threadIdx.x; idx < 32 * D; idx += 256) {
         const int p = idx / D, c = idx - p * D;
         ks[p][c] = P0 + p < dm.n_pages ? kp[(kvh * dm.n_pages + P0 + p) * D + c] : 0.f;
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_
             const int rr = idx / D, c = idx - rr * D, r = r0 + rr;
             float v = 0.f;
             if (r < R) {
-                const int h = g * dm.G + r / dm.n_a, i = active[static_cast<int64_t>(b) * dm.n_a + r % dm.n_a];
+                const int h = g * dm.G + r / dm.n_a, i = act[r % dm.n_a];
                 v = bf16_to_f32(q[((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * D + c]);
             }
             qs[rr][c] = v;
@@ -798,12 +802,13 @@ sdattn_status sdattn_losa_step(const sdattn_losa_problem* p, const void* q, cons
     double* delta = reinterpret_cast<double*>(w + pl.off_delta);
     hipLaunchKernelGGL(losa_delta_kernel, dim3(dm.Bs, dm.B), dim3(256), 0, st, dm, q16,
                        static_cast<const uint16_t*>(q_prev), delta, locality);
-    hipLaunchKernelGGL(losa_active_kernel, dim3(dm.B), dim3(64), 0, st, dm, delta, active_idx, bits, pl.n_words);
     const dim3 sgrid((dm.n_pages + 31) / 32, dm.Hkv, dm.B);
     if (dm.D == 128)
-        hipLaunchKernelGGL(losa_scores_kernel<128>, sgrid, dim3(256), 0, st, dm, q16, active_idx, kp, scores);
+        hipLaunchKernelGGL(losa_scores_kernel<128>, sgrid, dim3(256), 0, st, dm, q16, delta, active_idx, bits,
+                           pl.n_words, kp, scores);
     else
-        hipLaunchKernelGGL(losa_scores_kernel<64>, sgrid, dim3(256), 0, st, dm, q16, active_idx, kp, scores);
+        hipLaunchKernelGGL(losa_scores_kernel<64>, sgrid, dim3(256), 0, st, dm, q16, delta, active_idx, bits,
+                           pl.n_words, kp, scores);
     switch (pl.npl) {
         case 8: launch_topk<8>(pl, scores, bits, st); break;
         case 16: launch_topk<16>(pl, scores, bits, st); break;
