@@ -443,10 +443,13 @@ def run_losa(args, w):
     losa_flops = 4.0 * G * w.n_active * d * (u_mean * w.page + B * Hkv * Bs) + 2.0 * B * Hq * w.n_active * n_pages * d
     kernels = {}
     if dense_call_ms:
-        a = dense_flops / (dense_call_ms * 1e9)
+        # bf16 MFMA at ~128 FLOP per byte of K/V, below the MFMA ridge (~312): bound by the K/V stream
+        a = dense_bytes / (dense_call_ms * 1e6)
+        tf = dense_flops / (dense_call_ms * 1e9)
         kernels["losa_dense_iteration"] = {
-            "bound": "alu", "achieved": round(a, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(a / PEAK_F32_TFLOPS, 4), "launch_ms": round(dense_call_ms, 4), "flops_per_launch": dense_flops,
+            "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(a / PEAK_HBM_GBS, 4), "launch_ms": round(dense_call_ms, 4), "bytes_per_launch": dense_bytes,
+            "flops_per_launch": dense_flops, "tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "kernels": "losa_attend_kernel (dense) + losa_merge_kernel; the page means (losa_pool_kernel) run "
                        "once per block before it", "traffic": None}
     if losa_ms:

@@ -297,10 +297,12 @@ __global__ __launch_bounds__(256) void losa_union_kernel(int Hkv, const uint32_t
 }
 
 // ---- 5. partial softmax of a row tile over one key chunk ---------------------
-// RPT rows per thread row-block: a tile of RT = 16 * RPT query rows (32 or
-// 64).  Scores: thread (row block t / 16, key column t % 16) holds RPT rows x
-// keys {t % 16 + 16 j}.  Softmax: 256 / RT lanes per row.  PV: the same row
-// block x D / 16 output channels.
+// A tile of RT = 16 * RPT query rows (32 or 64) against 64-key tiles of the
+// chunk.  Scores: 32x32 blocks S^T = K Q^T with v_mfma_f32_32x32x16_bf16, one
+// block per wave (RT/32 row blocks x 2 key blocks), scaled into LDS.
+// Softmax: 256 / RT lanes per row, P packed to bf16 key pairs.  Output:
+// 32-channel x 32-row blocks O^T += V^T P^T on MFMA, the V^T operand read
+// from V stored as key-pair words, the P^T operand as four pair words.
 
 struct AttendArgs {
     Dims dm;
@@ -319,17 +321,21 @@ struct AttendArgs {
 
 template <int D, int RPT>
 __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
-    constexpr int RT = 16 * RPT;      // rows per tile
-    constexpr int QW = D / 2 + 4;     // LDS row stride of Q and K tiles in 32-bit words (16-byte aligned, odd bank step)
+    constexpr int RT = 16 * RPT;      // rows per tile (32 or 64)
+    constexpr int QW = D / 2 + 4;     // LDS row stride of Q and K tiles in 32-bit words (16-byte aligned)
     constexpr int VU = D / 8;         // 16-byte units per row
-    constexpr int DT = D / 16;        // output channels per thread
     constexpr int TPR = 256 / RT;     // softmax lanes per row
     constexpr int KPL = kKeyTile / TPR;
+    constexpr int PW = kKeyTile / 2 + 4;     // P pair row stride in words (16-byte aligned)
+    constexpr int NSB = (RT / 32) * 2;       // 32x32 score blocks per tile (row block x key block)
+    constexpr int NOB = (RT / 32) * (D / 32);  // 32-row x 32-channel output blocks
+    constexpr int OPW = (NOB + 3) / 4;       // output blocks per wave
+    constexpr int DK = D / 16;               // MFMA k-steps of q.k
     __shared__ __align__(16) uint32_t qs[RT * QW];
     __shared__ __align__(16) uint32_t ks[kKeyTile * QW];
     __shared__ __align__(16) uint4 vp[(kKeyTile / 2) * (D / 4)];  // V as key pairs: word (m, c) = {v[2m][c], v[2m+1][c]}
     __shared__ float ss[RT][kKeyTile + 1];
-    __shared__ uint32_t ps[RT][kKeyTile / 2 + 1];                   // P as bf16 key pairs
+    __shared__ __align__(16) uint32_t ps[RT * PW];                 // P as bf16 key pairs
     __shared__ float m_s[RT], l_s[RT], al_s[RT];
 
     const Dims& dm = a.dm;
@@ -348,7 +354,7 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
     const int r0 = rt * RT;
     const int nrows = min(RT, a.R - r0);
     const int n_a = a.dense ? dm.Bs : dm.n_a;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, l32 = lane & 31, hl = lane >> 5;
 
     for (int idx = t; idx < RT * VU; idx += 256) {
         const int rr = idx / VU, u = idx - rr * VU;
@@ -366,13 +372,6 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         l_s[t] = 0.f;
     }
 
-    const int rb = t >> 4, kb = t & 15;
-    float o[RPT][DT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-#pragma unroll
-        for (int e = 0; e < DT; ++e) o[i][e] = 0.f;
-
     // row of key kk of the current tile in its K/V tensor (the block's own, or the cache)
     auto key_row = [&](int k0, int kk) -> int64_t {
         if (suffix) return kvh * dm.Bs + k0 + kk;
@@ -382,6 +381,13 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
     };
     const uint16_t* kbase = suffix ? a.kb : a.kc;
     const uint16_t* vbase = suffix ? a.vb : a.vc;
+
+    // output blocks of this wave: block ob = wave + 4 j -> rows 32 (ob / (D/32)), channels 32 (ob % (D/32))
+    f32x16 oacc[OPW];
+#pragma unroll
+    for (int j = 0; j < OPW; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[j][r] = 0.f;
 
     for (int k0 = 0; k0 < n_keys; k0 += kKeyTile) {
         const int nk = min(kKeyTile, n_keys - k0);
@@ -408,29 +414,25 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         }
         __syncthreads();
 
-        float acc[RPT][4];
+        // S^T block (32 keys x 32 rows) = K Q^T: lane holds row l32 of the tile's row block,
+        // keys 8 (r / 4) + 4 hl + r % 4 of its key block
+        if (wave < NSB) {
+            const int rw = wave >> 1, kw = wave & 1;
+            f32x16 sacc;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-        // q.k over channel pairs: v_dot2_f32_bf16 takes the packed bf16 pairs as stored
-#pragma unroll 4
-        for (int w2 = 0; w2 < D / 2; ++w2) {
-            bf16x2 qv[RPT], kv[4];
+            for (int st = 0; st < DK; ++st) {
+                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&ks[(kw * 32 + l32) * QW + 8 * st + 4 * hl]);
+                const bf16x8 qop = *reinterpret_cast<const bf16x8*>(&qs[(rw * 32 + l32) * QW + 8 * st + 4 * hl]);
+                sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop, sacc, 0, 0, 0);
+            }
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) qv[i] = __builtin_bit_cast(bf16x2, qs[(rb * RPT + i) * QW + w2]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kv[j] = __builtin_bit_cast(bf16x2, ks[(kb + 16 * j) * QW + w2]);
-#pragma unroll
-            for (int i = 0; i < RPT; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_fdot2_f32_bf16(qv[i], kv[j], acc[i][j], false);
+            for (int r = 0; r < 16; ++r) {
+                const int key = kw * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                ss[rw * 32 + l32][key] = key < nk ? sacc[r] * a.scale_log2 : -INFINITY;
+            }
         }
-#pragma unroll
-        for (int i = 0; i < RPT; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                ss[rb * RPT + i][kb + 16 * j] = kb + 16 * j < nk ? acc[i][j] * a.scale_log2 : -INFINITY;
         __syncthreads();
 
         {  // online softmax: TPR lanes per row, key pairs pt + TPR j; P stored as bf16 pairs
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
             for (int j = 0; j < KPL / 2; ++j) {
                 const int m = pt + TPR * j;
                 const float p0 = exp2f(ss[row][2 * m] - m_new), p1 = exp2f(ss[row][2 * m + 1] - m_new);
-                ps[row][m] = pack_bf16x2(p0, p1);
+                ps[row * PW + m] = pack_bf16x2(p0, p1);
                 sum += p0 + p1;
             }
 #pragma unroll
@@ -464,47 +466,50 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
         }
         __syncthreads();
 
+        // O^T block (32 channels x 32 rows) += V^T P^T over the tile's 64 keys (4 k-steps of 16)
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const float al = al_s[rb * RPT + i];
+        for (int j = 0; j < OPW; ++j) {
+            const int ob = wave + 4 * j;
+            if (ob < NOB) {
+                const int rw = ob / (D / 32), dw = ob % (D / 32);
+                const int row = rw * 32 + l32;
+                const float al = al_s[row];
 #pragma unroll
-            for (int e = 0; e < DT; ++e) o[i][e] *= al;
-        }
-        // p.v over key pairs with v_dot2_f32_bf16: P pairs from ps, V pairs from vp
-        const int n_pairs = (nk + 1) / 2;
-        for (int m = 0; m < n_pairs; ++m) {
-            uint32_t vw[DT];
+                for (int r = 0; r < 16; ++r) oacc[j][r] *= al;
+                const uint32_t* vw = reinterpret_cast<const uint32_t*>(vp);
 #pragma unroll
-            for (int q4 = 0; q4 < DT / 4; ++q4) {
-                const uint4 x = vp[m * (D / 4) + kb * (DT / 4) + q4];
-                vw[4 * q4] = x.x;
-                vw[4 * q4 + 1] = x.y;
-                vw[4 * q4 + 2] = x.z;
-                vw[4 * q4 + 3] = x.w;
-            }
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const bf16x2 pp = __builtin_bit_cast(bf16x2, ps[rb * RPT + i][m]);
-#pragma unroll
-                for (int e = 0; e < DT; ++e)
-                    o[i][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vw[e]), o[i][e], false);
+                for (int kst = 0; kst < kKeyTile / 16; ++kst) {
+                    const int m0 = 8 * kst + 4 * hl;  // first key pair of this lane's 8 keys
+                    const uint32_t vv[4] = {vw[(m0 + 0) * D + dw * 32 + l32], vw[(m0 + 1) * D + dw * 32 + l32],
+                                            vw[(m0 + 2) * D + dw * 32 + l32], vw[(m0 + 3) * D + dw * 32 + l32]};
+                    const uint4 pp = *reinterpret_cast<const uint4*>(&ps[row * PW + m0]);
+                    oacc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv),
+                                                                     __builtin_bit_cast(bf16x8, pp), oacc[j], 0, 0, 0);
+                }
             }
         }
         __syncthreads();
     }
 
+    // partial (unnormalised o, m, l) of every row: lane holds row l32, channels 8 (r / 4) + 4 hl + r % 4
     const int parts = a.n_chunks + 1;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int rr = rb * RPT + i;
+    for (int j = 0; j < OPW; ++j) {
+        const int ob = wave + 4 * j;
+        if (ob >= NOB) continue;
+        const int rw = ob / (D / 32), dw = ob % (D / 32);
+        const int rr = rw * 32 + l32;
         if (rr >= nrows) continue;
-        float* dst = a.part + ((kvh * a.row_tiles * RT + r0 + rr) * parts + c) * (D + 4);
+        float* dst = a.part + ((kvh * a.row_tiles * RT + r0 + rr) * parts + c) * (D + 4) + dw * 32 + 4 * hl;
 #pragma unroll
-        for (int e = 0; e < DT; ++e) dst[kb * DT + e] = o[i][e];
-        if (kb == 0) {
-            dst[D] = m_s[rr];
-            dst[D + 1] = l_s[rr];
-        }
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<float4*>(dst + 8 * q4) =
+                make_float4(oacc[j][4 * q4], oacc[j][4 * q4 + 1], oacc[j][4 * q4 + 2], oacc[j][4 * q4 + 3]);
+    }
+    if (t < nrows) {
+        float* dst = a.part + ((kvh * a.row_tiles * RT + r0 + t) * parts + c) * (D + 4);
+        dst[D] = m_s[t];
+        dst[D + 1] = l_s[t];
     }
 }
 
