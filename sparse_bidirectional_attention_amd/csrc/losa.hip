@@ -19,8 +19,10 @@
 //   losa_scores_kernel       the Active list (ascending; every workgroup ranks
 //                            the block's tokens), page scores of every Active
 //                            query row (fp32 FMA), and clears the page bitmaps;
-//   losa_topk_kernel         one wave per Active query row: top-k pages by
-//                            (score desc, page asc), OR-ed into the bitmap;
+//   losa_topk4_kernel        one workgroup per Active query row (budgets up to
+//                            64 pages; losa_topk_kernel, one wave per row,
+//                            above): top-k pages by (score desc, page asc),
+//                            OR-ed into the bitmap;
 //   losa_union_kernel        one workgroup per (b, kv head): the ascending page
 //                            list of the bitmap and its length;
 //   losa_attend_kernel       one workgroup per (key chunk, kv head, 32- or
@@ -139,17 +141,19 @@ __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_
     __shared__ float ks[32][D + 1];
     __shared__ float qs[32][D];
     __shared__ int act[kMaxBlockLen];
+    __shared__ double dsh[kMaxBlockLen];
     const int P0 = blockIdx.x * 32, g = blockIdx.y, b = blockIdx.z;
     const int pg = threadIdx.x & 31, slot = threadIdx.x >> 5;
     const int64_t kvh = static_cast<int64_t>(b) * dm.Hkv + g;
+    if (threadIdx.x < dm.Bs) dsh[threadIdx.x] = delta[static_cast<int64_t>(b) * dm.Bs + threadIdx.x];
+    __syncthreads();
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
-        const double* dl = delta + static_cast<int64_t>(b) * dm.Bs;
         const bool valid = lane < dm.Bs;
-        const double di = valid ? dl[lane] : 0.0;
+        const double di = valid ? dsh[lane] : 0.0;
         int rank = 0;
         for (int j = 0; j < dm.Bs; ++j) {
-            const double dj = dl[j];
+            const double dj = dsh[j];
             rank += (dj > di || (dj == di && j < lane)) ? 1 : 0;
         }
         const bool is_act = valid && rank < dm.n_a;
@@ -261,12 +265,61 @@ __global__ __launch_bounds__(256) void losa_topk_kernel(Dims dm, const float* __
     uint32_t* bm = bitmap + (static_cast<int64_t>(b) * dm.Hkv + h / dm.G) * n_words;
     uint64_t prev = ~0ull;
     for (int k = 0; k < dm.kpq; ++k) {
-        uint64_t best = 0ull;
+        uint64_t bq[4] = {0ull, 0ull, 0ull, 0ull};  // four independent chains over j mod 4
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             const uint64_t x = keys[j];
-            best = (x < prev && x > best) ? x : best;
+            bq[j & 3] = (x < prev && x > bq[j & 3]) ? x : bq[j & 3];
         }
+        uint64_t best = bq[0] > bq[1] ? bq[0] : bq[1];
+        const uint64_t b23 = bq[2] > bq[3] ? bq[2] : bq[3];
+        best = best > b23 ? best : b23;
+        best = wave_max_u64(best);
+        if (best == 0ull) break;  // fewer orderable entries than kpq
+        prev = best;
+        const int P = static_cast<int>(~static_cast<uint32_t>(best));
+        if (lane == 0) atomicOr(&bm[P >> 5], 1u << (P & 31));
+    }
+}
+
+// One workgroup per row for budgets of at most 64 pages: wave w takes the
+// top-k keys of pages w*64 + lane + 256 j (NPL4 per lane) into LDS; wave 0
+// then takes the top-k of those 4k candidates, which hold the row's top-k.
+template <int NPL4>
+__global__ __launch_bounds__(256) void losa_topk4_kernel(Dims dm, const float* __restrict__ scores,
+                                                         uint32_t* __restrict__ bitmap, int n_words) {
+    __shared__ uint64_t cand[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
+    const int64_t bh = row / dm.n_a;  // b * Hq + h
+    const int b = static_cast<int>(bh / dm.Hq), h = static_cast<int>(bh % dm.Hq);
+    const float* sr = scores + row * dm.n_pages;
+    uint64_t keys[NPL4];
+#pragma unroll
+    for (int j = 0; j < NPL4; ++j) {
+        const int P = wave * 64 + lane + 256 * j;
+        keys[j] = P < dm.n_pages ? score_key(sr[P], P) : 0ull;
+    }
+    uint64_t prev = ~0ull;
+    for (int k = 0; k < dm.kpq; ++k) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int j = 0; j < NPL4; ++j) best = (keys[j] < prev && keys[j] > best) ? keys[j] : best;
+        best = wave_max_u64(best);
+        if (lane == 0) cand[wave][k] = best;  // 0 once this quarter has no entry left
+        prev = best;
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    uint64_t c4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c4[q] = lane < dm.kpq ? cand[q][lane] : 0ull;
+    uint32_t* bm = bitmap + (static_cast<int64_t>(b) * dm.Hkv + h / dm.G) * n_words;
+    prev = ~0ull;
+    for (int k = 0; k < dm.kpq; ++k) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) best = (c4[q] < prev && c4[q] > best) ? c4[q] : best;
         best = wave_max_u64(best);
         if (best == 0ull) break;  // fewer orderable entries than kpq
         prev = best;
@@ -557,11 +610,21 @@ __global__ __launch_bounds__(256) void losa_merge_kernel(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < DC; ++e) acc[e] = 0.f;
     float L = 0.f;
-#pragma unroll 2
-    for (int k = cg; k <= n_valid; k += 4) {
-        const float* p = entry(k);
-        const float w = exp2f(p[D] - M);
-        if (cl == 0) L = fmaf(p[D + 1], w, L);
+    for (int k0 = 0; k0 <= n_valid; k0 += 64) {
+        // weight of entry k0 + lane, and its share of the denominator
+        float wl = 0.f;
+        if (k0 + lane <= n_valid) {
+            const float* p = entry(k0 + lane);
+            wl = exp2f(p[D] - M);
+            L = fmaf(p[D + 1], wl, L);
+        }
+        const int nb = min(n_valid, k0 + 63) - k0 + 1;  // entries in this batch of 64
+        // uniform trip count: every lane takes part in the shuffle, lanes past the batch skip the sum
+#pragma unroll 4
+    for (int i = 0; i < nb; i += 4) {
+        const float w = __shfl(wl, (i + cg) & 63, 64);
+        if (i + cg >= nb) continue;
+        const float* p = entry(k0 + i + cg);
         const float4* x = reinterpret_cast<const float4*>(p + cl * DC);
 #pragma unroll
         for (int e = 0; e < DC / 4; ++e) {
@@ -571,6 +634,7 @@ __global__ __launch_bounds__(256) void losa_merge_kernel(MergeArgs a) {
             acc[4 * e + 2] = fmaf(v.z, w, acc[4 * e + 2]);
             acc[4 * e + 3] = fmaf(v.w, w, acc[4 * e + 3]);
         }
+    }
     }
 #pragma unroll
     for (int e = 0; e < DC; ++e) {
@@ -814,11 +878,21 @@ sdattn_status sdattn_losa_step(const sdattn_losa_problem* p, const void* q, cons
     else
         hipLaunchKernelGGL(losa_scores_kernel<64>, sgrid, dim3(256), 0, st, dm, q16, delta, active_idx, bits,
                            pl.n_words, kp, scores);
-    switch (pl.npl) {
-        case 8: launch_topk<8>(pl, scores, bits, st); break;
-        case 16: launch_topk<16>(pl, scores, bits, st); break;
-        case 32: launch_topk<32>(pl, scores, bits, st); break;
-        default: launch_topk<64>(pl, scores, bits, st); break;
+    if (dm.kpq <= 64) {
+        const dim3 tgrid(static_cast<unsigned>(static_cast<int64_t>(dm.B) * dm.Hq * dm.n_a));
+        switch (pl.npl) {  // pages per lane over a quarter row: npl / 4
+            case 8: hipLaunchKernelGGL(losa_topk4_kernel<2>, tgrid, dim3(256), 0, st, dm, scores, bits, pl.n_words); break;
+            case 16: hipLaunchKernelGGL(losa_topk4_kernel<4>, tgrid, dim3(256), 0, st, dm, scores, bits, pl.n_words); break;
+            case 32: hipLaunchKernelGGL(losa_topk4_kernel<8>, tgrid, dim3(256), 0, st, dm, scores, bits, pl.n_words); break;
+            default: hipLaunchKernelGGL(losa_topk4_kernel<16>, tgrid, dim3(256), 0, st, dm, scores, bits, pl.n_words); break;
+        }
+    } else {
+        switch (pl.npl) {
+            case 8: launch_topk<8>(pl, scores, bits, st); break;
+            case 16: launch_topk<16>(pl, scores, bits, st); break;
+            case 32: launch_topk<32>(pl, scores, bits, st); break;
+            default: launch_topk<64>(pl, scores, bits, st); break;
+        }
     }
     hipLaunchKernelGGL(losa_union_kernel, dim3(dm.Hkv, dm.B), dim3(256), 0, st, dm.Hkv, bits, pl.n_words, union_pages,
                        union_count, pl.cap);
