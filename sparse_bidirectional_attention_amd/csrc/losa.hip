@@ -138,17 +138,25 @@ __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_
                                                           int32_t* __restrict__ active_out,
                                                           uint32_t* __restrict__ bitmap, int n_words,
                                                           const float* __restrict__ kp, float* __restrict__ scores) {
-    __shared__ float ks[32][D + 1];
-    __shared__ float qs[32][D];
+    constexpr int KW = D + 4;  // page-mean row stride in floats (16-byte aligned; lanes 0-15 hit distinct banks)
+    __shared__ __align__(16) float ks[32 * KW];
+    __shared__ __align__(16) float qs[32 * D];
     __shared__ int act[kMaxBlockLen];
     __shared__ double dsh[kMaxBlockLen];
     const int P0 = blockIdx.x * 32, g = blockIdx.y, b = blockIdx.z;
-    const int pg = threadIdx.x & 31, slot = threadIdx.x >> 5;
+    const int t = threadIdx.x, pg = t & 31, slot = t >> 5;
     const int64_t kvh = static_cast<int64_t>(b) * dm.Hkv + g;
-    if (threadIdx.x < dm.Bs) dsh[threadIdx.x] = delta[static_cast<int64_t>(b) * dm.Bs + threadIdx.x];
+    // the page means first: their loads overlap the ranking below
+    for (int idx = t; idx < 32 * (D / 4); idx += 256) {
+        const int p = idx / (D / 4), c4 = idx - p * (D / 4);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (P0 + p < dm.n_pages) v = *reinterpret_cast<const float4*>(kp + (kvh * dm.n_pages + P0 + p) * D + 4 * c4);
+        *reinterpret_cast<float4*>(&ks[p * KW + 4 * c4]) = v;
+    }
+    if (t < dm.Bs) dsh[t] = delta[static_cast<int64_t>(b) * dm.Bs + t];
     __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
+    if (t < 64) {
+        const int lane = t;
         const bool valid = lane < dm.Bs;
         const double di = valid ? dsh[lane] : 0.0;
         int rank = 0;
@@ -165,30 +173,36 @@ __global__ __launch_bounds__(256) void losa_scores_kernel(Dims dm, const uint16_
         }
     }
     if (blockIdx.x == 0)
-        for (int w = threadIdx.x; w < n_words; w += 256) bitmap[kvh * n_words + w] = 0u;
-    for (int idx = threadIdx.x; idx < 32 * D; idx += 256) {
-        const int p = idx / D, c = idx - p * D;
-        ks[p][c] = P0 + p < dm.n_pages ? kp[(kvh * dm.n_pages + P0 + p) * D + c] : 0.f;
-    }
+        for (int w = t; w < n_words; w += 256) bitmap[kvh * n_words + w] = 0u;
     const int R = dm.G * dm.n_a;
     for (int r0 = 0; r0 < R; r0 += 32) {
         __syncthreads();
-        for (int idx = threadIdx.x; idx < 32 * D; idx += 256) {
-            const int rr = idx / D, c = idx - rr * D, r = r0 + rr;
-            float v = 0.f;
+        for (int idx = t; idx < 32 * (D / 8); idx += 256) {
+            const int rr = idx / (D / 8), u = idx - rr * (D / 8), r = r0 + rr;
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
             if (r < R) {
                 const int h = g * dm.G + r / dm.n_a, i = act[r % dm.n_a];
-                v = bf16_to_f32(q[((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * D + c]);
+                x = *reinterpret_cast<const uint4*>(q + ((static_cast<int64_t>(b) * dm.Hq + h) * dm.Bs + i) * D + 8 * u);
             }
-            qs[rr][c] = v;
+            float4* dst = reinterpret_cast<float4*>(&qs[rr * D + 8 * u]);
+            dst[0] = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
+                                 __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
+            dst[1] = make_float4(__uint_as_float(x.z << 16), __uint_as_float(x.z & 0xFFFF0000u),
+                                 __uint_as_float(x.w << 16), __uint_as_float(x.w & 0xFFFF0000u));
         }
         __syncthreads();
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-        for (int c = 0; c < D; ++c) {
-            const float kv = ks[pg][c];
+#pragma unroll 4
+        for (int c4 = 0; c4 < D / 4; ++c4) {
+            const float4 kv = *reinterpret_cast<const float4*>(&ks[pg * KW + 4 * c4]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = fmaf(qs[slot + 8 * j][c], kv, acc[j]);
+            for (int j = 0; j < 4; ++j) {
+                const float4 qv = *reinterpret_cast<const float4*>(&qs[(slot + 8 * j) * D + 4 * c4]);
+                acc[j] = fmaf(qv.x, kv.x, acc[j]);
+                acc[j] = fmaf(qv.y, kv.y, acc[j]);
+                acc[j] = fmaf(qv.z, kv.z, acc[j]);
+                acc[j] = fmaf(qv.w, kv.w, acc[j]);
+            }
         }
         const int P = P0 + pg;
 #pragma unroll
