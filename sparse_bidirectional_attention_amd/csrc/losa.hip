@@ -456,20 +456,39 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[j][r] = 0.f;
 
-    for (int k0 = 0; k0 < n_keys; k0 += kKeyTile) {
+    // K/V of a tile pass through registers: the next tile's loads are issued
+    // before the current tile is computed, so their latency overlaps it
+    constexpr int KIT = kKeyTile * VU / 256;         // K units per thread
+    constexpr int VIT = (kKeyTile / 2) * VU / 256;   // V key-pair units per thread
+    uint4 kr[KIT], va[VIT], vb[VIT];
+    auto load_tile = [&](int k0) {
         const int nk = min(kKeyTile, n_keys - k0);
-        for (int idx = t; idx < kKeyTile * VU; idx += 256) {
-            const int kk = idx / VU, u = idx - kk * VU;
-            uint4 kv = make_uint4(0u, 0u, 0u, 0u);
-            if (kk < nk) kv = *reinterpret_cast<const uint4*>(kbase + key_row(k0, kk) * D + u * 8);
-            *reinterpret_cast<uint4*>(&ks[kk * QW + u * 4]) = kv;
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int idx = t + 256 * it, kk = idx / VU, u = idx - kk * VU;
+            kr[it] = kk < nk ? *reinterpret_cast<const uint4*>(kbase + key_row(k0, kk) * D + u * 8)
+                             : make_uint4(0u, 0u, 0u, 0u);
         }
-        for (int idx = t; idx < (kKeyTile / 2) * VU; idx += 256) {
-            const int m = idx / VU, u = idx - m * VU;
-            uint4 x0 = make_uint4(0u, 0u, 0u, 0u), x1 = x0;
-            if (2 * m < nk) x0 = *reinterpret_cast<const uint4*>(vbase + key_row(k0, 2 * m) * D + u * 8);
-            if (2 * m + 1 < nk) x1 = *reinterpret_cast<const uint4*>(vbase + key_row(k0, 2 * m + 1) * D + u * 8);
-            const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = t + 256 * it, m = idx / VU, u = idx - m * VU;
+            va[it] = 2 * m < nk ? *reinterpret_cast<const uint4*>(vbase + key_row(k0, 2 * m) * D + u * 8)
+                                : make_uint4(0u, 0u, 0u, 0u);
+            vb[it] = 2 * m + 1 < nk ? *reinterpret_cast<const uint4*>(vbase + key_row(k0, 2 * m + 1) * D + u * 8)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int it = 0; it < KIT; ++it) {
+            const int idx = t + 256 * it, kk = idx / VU, u = idx - kk * VU;
+            *reinterpret_cast<uint4*>(&ks[kk * QW + u * 4]) = kr[it];
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int idx = t + 256 * it, m = idx / VU, u = idx - m * VU;
+            const uint32_t a0[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
+            const uint32_t a1[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
             uint32_t w[8];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -479,7 +498,14 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
             vp[m * (D / 4) + 2 * u] = make_uint4(w[0], w[1], w[2], w[3]);
             vp[m * (D / 4) + 2 * u + 1] = make_uint4(w[4], w[5], w[6], w[7]);
         }
+    };
+
+    load_tile(0);
+    for (int k0 = 0; k0 < n_keys; k0 += kKeyTile) {
+        const int nk = min(kKeyTile, n_keys - k0);
+        store_tile();
         __syncthreads();
+        if (k0 + kKeyTile < n_keys) load_tile(k0 + kKeyTile);
 
         // S^T block (32 keys x 32 rows) = K Q^T: lane holds row l32 of the tile's row block,
         // keys 8 (r / 4) + 4 hl + r % 4 of its key block
