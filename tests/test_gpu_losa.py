@@ -203,3 +203,43 @@ def test_losa_unchanged_queries_pick_lowest_indices():
     _step(run, run.iters[1], run.iters[0], 1)
     assert run.active.cpu().tolist() == [[0, 1, 2, 3, 4]]
     assert np.all(run.loc.cpu().numpy() == 0.0)
+
+
+def test_losa_step_captured_in_a_graph_replays_like_eager():
+    """A LoSA iteration enqueues kernels only (the page bitmaps are cleared by a
+    kernel, not a memset): captured once, replayed on new inputs copied into
+    the captured buffers, it reproduces an eager run bit for bit, Active list
+    and unions included."""
+    w = scaled(SDAR, q_heads=8, kv_heads=2, prefix_len=4096, block_len=32, head_dim=128, page=16, n_active=8,
+               pages_per_query=4)
+    run = _Run(w, lambda base: [make_losa_iteration(w, t, base) for t in range(4)])
+    xs = [_dev(x) for x in run.iters]
+    sd.sdattn_losa_dense(run.p, xs[0]["q"], run.kc, run.vc, xs[0]["k_blk"], xs[0]["v_blk"], run.o, run.lse, run.ws)
+    torch.cuda.synchronize()
+    cur = {n: t.clone() for n, t in xs[1].items()}
+    prev_q = xs[0]["q"].clone()
+    o0, l0 = run.o.clone(), run.lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sd.sdattn_losa_step(run.p, cur["q"], prev_q, run.kc, run.vc, run.kp, cur["k_blk"], cur["v_blk"], run.o,
+                            run.lse, run.active, run.upages, run.ucount, run.ws)
+    for t in (1, 2, 3):
+        for n in cur:
+            cur[n].copy_(xs[t][n])
+        prev_q.copy_(xs[t - 1]["q"])
+        run.o.copy_(o0)
+        run.lse.copy_(l0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [x.clone() for x in (run.o, run.lse, run.active, run.ucount, run.upages)]
+        run.o.copy_(o0)
+        run.lse.copy_(l0)
+        sd.sdattn_losa_step(run.p, xs[t]["q"], xs[t - 1]["q"], run.kc, run.vc, run.kp, xs[t]["k_blk"],
+                            xs[t]["v_blk"], run.o, run.lse, run.active, run.upages, run.ucount, run.ws)
+        torch.cuda.synchronize()
+        eager = (run.o, run.lse, run.active, run.ucount, run.upages)
+        assert torch.equal(got[0].view(torch.int16), eager[0].view(torch.int16)), f"replay {t}: O"
+        for a, b_, name in zip(got[1:], eager[1:], ("lse", "active", "union_count", "union_pages")):
+            assert torch.equal(a, b_), f"replay {t}: {name}"
+        say(f"  replay {t}: bit-identical to eager, active {run.active[0].tolist()}")
