@@ -142,6 +142,8 @@ CASES = {
                                n_active=16, pages_per_query=2, n_moving=12),
     "one_active_one_page": dict(q_heads=4, kv_heads=1, prefix_len=1024, block_len=8, head_dim=128, page=64,
                                 n_active=1, pages_per_query=1, n_moving=1),
+    "d64_rows_48_of_64": dict(q_heads=8, kv_heads=2, prefix_len=2048, block_len=32, head_dim=64, page=32,
+                              n_active=12, pages_per_query=5, n_moving=10),
     "budget_over_64_pages": dict(q_heads=4, kv_heads=2, prefix_len=2048, block_len=16, head_dim=64, page=16,
                                  n_active=4, pages_per_query=100, n_moving=3),
     "pages_4096": dict(q_heads=2, kv_heads=1, prefix_len=65536, block_len=16, head_dim=64, page=16, n_active=4,
