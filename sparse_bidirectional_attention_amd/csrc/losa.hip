@@ -51,7 +51,7 @@ constexpr int kMaxBlockLen = 64;     // block tokens (one per lane of the locali
 constexpr int kMaxPages = 4096;      // prefix pages (rows of scores held in registers)
 constexpr int kKeyTile = 64;         // keys per LDS tile
 constexpr int kChunkSparse = 64;     // keys per attention workgroup, later iterations
-constexpr int kChunkDense = 512;     // keys per attention workgroup, first iteration
+constexpr int kChunkDense = 1024;    // keys per attention workgroup, first iteration
 
 struct Dims {
     int B, Hq, Hkv, G, Lp, Bs, D, page, n_pages, n_a, kpq;
