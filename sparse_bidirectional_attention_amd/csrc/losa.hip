@@ -50,7 +50,7 @@ namespace {
 constexpr int kMaxBlockLen = 64;     // block tokens (one per lane of the locality wave)
 constexpr int kMaxPages = 4096;      // prefix pages (rows of scores held in registers)
 constexpr int kKeyTile = 64;         // keys per LDS tile
-constexpr int kChunkSparse = 64;     // keys per attention workgroup, later iterations
+constexpr int kChunkSparse = 128;    // keys per attention workgroup, later iterations
 constexpr int kChunkDense = 1024;    // keys per attention workgroup, first iteration
 
 struct Dims {
@@ -732,6 +732,8 @@ sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     const int64_t G = p->q_heads / p->kv_heads;
     if (p->batch > 65535 || static_cast<int64_t>(p->kv_heads) * ((G * p->block_len + 31) / 32) > 65535)
         return fail(SDATTN_ERR_SHAPE, "batch and kv_heads * ceil(q_heads/kv_heads * block_len / 32) must be <= 65535");
+    if (static_cast<int64_t>(p->batch) * p->q_heads * p->n_active >= (int64_t{1} << 31))
+        return fail(SDATTN_ERR_SHAPE, "batch * q_heads * n_active must be < 2^31");
 
     Plan pl;
     Dims& dm = pl.dm;
