@@ -15,6 +15,11 @@ the dense steps and the selection step's tensors serve the selection and
 sparse steps (kernel time does not depend on the drift between steps; the
 pattern does, and it is computed from the real selection-step inputs).
 
+The block-wise workload (--workload losa_sdar8b_32k) is timed the same way
+over blocks of iterations on top of a cached prefix: the first iteration of a
+block dense, the others LoSA-style (Active tokens, page selection, page union,
+partial attention); see run_losa.
+
 The JSON line reports the whole-schedule ms per step (value), per-phase
 medians, effective TFLOP/s of the sparse steps on kept-block FLOPs, the dense
 schedule on the same GPU, a roofline object for the kernel that takes most
