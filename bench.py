@@ -456,7 +456,11 @@ def run_losa(args, w):
             "frac": round(a / PEAK_HBM_GBS, 4), "launch_ms": round(dense_call_ms, 4), "bytes_per_launch": dense_bytes,
             "flops_per_launch": dense_flops, "tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "kernels": "losa_attend_kernel (dense) + losa_merge_kernel; the page means (losa_pool_kernel) run "
-                       "once per block before it", "traffic": None}
+                       "once per block before it", "traffic": losa_traffic(w.name)}
+        tr = kernels["losa_dense_iteration"]["traffic"]
+        if tr:
+            kernels["losa_dense_iteration"]["traffic_gbs"] = round(tr / (dense_call_ms * 1e6), 1)
+            kernels["losa_dense_iteration"]["traffic_frac_of_hbm_peak"] = round(tr / (dense_call_ms * 1e6) / PEAK_HBM_GBS, 4)
     if losa_ms:
         a = losa_bytes / (losa_ms * 1e6)
         kernels["losa_step"] = {
@@ -501,6 +505,20 @@ def run_losa(args, w):
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline_losa(w, cache, iters_h)
     print(json.dumps(out), flush=True)
+
+
+def losa_traffic(workload):
+    """Calibrated L2-to-fabric bytes per dense-iteration call from the profile
+    counters, if they were taken on the current block-wise kernel sources."""
+    f = os.path.join(ROOT, "profiles", f"traffic_losa_dense_{workload}.json")
+    if not os.path.exists(f):
+        return None
+    t = json.load(open(f))
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_bidirectional_attention_amd", "csrc")
+    for name in ("losa.hip", "common.h"):
+        h.update(open(os.path.join(csrc, name), "rb").read())
+    return t["hbm_bytes_per_launch"] if t.get("kernel_source_hash") == h.hexdigest()[:16] else None
 
 
 def cpu_baseline_losa(w, cache, iters):

@@ -406,8 +406,14 @@ __global__ __launch_bounds__(256) void losa_attend_kernel(AttendArgs a) {
     __shared__ float m_s[RT], l_s[RT], al_s[RT];
 
     const Dims& dm = a.dm;
-    const int c = blockIdx.x;
-    const int g = blockIdx.y / a.row_tiles, rt = blockIdx.y - g * a.row_tiles, b = blockIdx.z;
+    // workgroup id -> (chunk, row tile): ids x and x + 8 share the chunk and take
+    // consecutive row tiles, so the tiles of one chunk run together on one XCD
+    // (ids go to the 8 XCDs in turn) and read its K/V through the same L2
+    const int x = blockIdx.x;
+    const int rt = (x >> 3) % a.row_tiles;
+    const int c = (x & 7) + 8 * (x / (8 * a.row_tiles));
+    if (c > a.n_chunks) return;
+    const int g = blockIdx.y, b = blockIdx.z;
     const int64_t kvh = static_cast<int64_t>(b) * dm.Hkv + g;
     const bool suffix = c == a.n_chunks;
     int n_keys;
@@ -729,9 +735,7 @@ sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     float scale = p->softmax_scale;
     if (!(scale > 0.f)) scale = 1.f / sqrtf(static_cast<float>(p->head_dim));
     if (!isfinite(scale)) return fail(SDATTN_ERR_SHAPE, "softmax_scale must be finite");
-    const int64_t G = p->q_heads / p->kv_heads;
-    if (p->batch > 65535 || static_cast<int64_t>(p->kv_heads) * ((G * p->block_len + 31) / 32) > 65535)
-        return fail(SDATTN_ERR_SHAPE, "batch and kv_heads * ceil(q_heads/kv_heads * block_len / 32) must be <= 65535");
+    if (p->batch > 65535 || p->kv_heads > 65535) return fail(SDATTN_ERR_SHAPE, "batch and kv_heads must be <= 65535");
     if (static_cast<int64_t>(p->batch) * p->q_heads * p->n_active >= (int64_t{1} << 31))
         return fail(SDATTN_ERR_SHAPE, "batch * q_heads * n_active must be < 2^31");
 
@@ -803,7 +807,7 @@ void launch_attend_merge(const Plan& pl, bool dense, const void* q, const void* 
     a.n_chunks = dense ? pl.nch_d : pl.nch_s;
     a.dense = dense ? 1 : 0;
     a.scale_log2 = dm.scale * kLog2e;
-    const dim3 grid(a.n_chunks + 1, dm.Hkv * a.row_tiles, dm.B);
+    const dim3 grid(((a.n_chunks + 1 + 7) / 8) * 8 * a.row_tiles, dm.Hkv, dm.B);
     if (RT == 32)
         hipLaunchKernelGGL((losa_attend_kernel<D, 2>), grid, dim3(256), 0, st, a);
     else
