@@ -467,7 +467,8 @@ def run_losa(args, w):
             "bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(a / PEAK_HBM_GBS, 4), "launch_ms": round(losa_ms, 4), "bytes_per_launch": losa_bytes,
             "flops_per_launch": losa_flops,
-            "kernels": "delta, active, scores, topk, union, attend, merge (seven launches)", "traffic": None}
+            "kernels": "delta, scores (with the Active ranking), topk, union, attend, merge (six launches)",
+            "traffic": None}
     # The roofline names the heaviest single kernel: the dense iteration's
     # attention (one C call = that kernel plus its merge, ~3% of the call).  A
     # LoSA iteration is seven short launches and stays under "kernels".
