@@ -470,7 +470,7 @@ def run_losa(args, w):
             "kernels": "delta, scores (with the Active ranking), topk, union, attend, merge (six launches)",
             "traffic": None}
     # The roofline names the heaviest single kernel: the dense iteration's
-    # attention (one C call = that kernel plus its merge, ~3% of the call).  A
+    # attention (one C call = that kernel plus its merge, ~10% of the call).  A
     # LoSA iteration is seven short launches and stays under "kernels".
     dom = "losa_dense_iteration" if "losa_dense_iteration" in kernels else "losa_step"
     roof = {k: v for k, v in kernels[dom].items() if k in ("bound", "achieved", "peak", "unit", "frac", "traffic")}
