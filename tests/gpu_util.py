@@ -78,6 +78,57 @@ def check_topk_rows(gpu_sets, scores, k, what=""):
     return n_exempt
 
 
+def near_cut_topk(s, k):
+    """The exact top-k of one row by (score desc, index asc), and the
+    candidates whose score lies within CUT_REL of the row's cut, relative to
+    the cut's magnitude (scores may be negative).  Returns (required,
+    allowed): the top-k without the near-cut candidates, and the top-k with
+    them.  A selection is valid when it holds every required index and only
+    allowed ones."""
+    s = np.asarray(s, np.float64)
+    order = np.lexsort((np.arange(len(s)), -s))
+    top = np.sort(order[:k])
+    cut = s[order[k - 1]]
+    near = np.nonzero(np.abs(s - cut) <= CUT_REL * abs(cut))[0]
+    if np.all(np.isin(near, top)):
+        return top, top  # no candidate outside the top-k is close to the cut: the set is exact
+    return np.setdiff1d(top, near), np.union1d(top, near)
+
+
+def check_union_of_topk(union, score_rows, k, what=""):
+    """A union of per-row top-k selections (the rows of one kv head) against
+    the exact per-row selections of the oracle's scores: it must hold every
+    index some row requires and only indices some row allows (near-cut
+    candidates may go either way).  Returns the number of near-cut indices
+    the union holds beyond the rows' exact selections."""
+    union = np.asarray(union)
+    assert np.all(np.diff(union) > 0), f"{what}: union not ascending / has duplicates"
+    required, allowed, exact = [], [], []
+    for s in score_rows:
+        r, a = near_cut_topk(s, k)
+        required.append(r)
+        allowed.append(a)
+        exact.append(np.lexsort((np.arange(len(s)), -np.asarray(s)))[:k])
+    req = np.unique(np.concatenate(required)) if required else np.zeros(0, np.int64)
+    alw = np.unique(np.concatenate(allowed)) if allowed else np.zeros(0, np.int64)
+    missing = np.setdiff1d(req, union)
+    extra = np.setdiff1d(union, alw)
+    assert missing.size == 0, f"{what}: union misses required indices {missing[:8]}"
+    assert extra.size == 0, f"{what}: union holds indices no row selects {extra[:8]}"
+    ex = np.unique(np.concatenate(exact)) if exact else np.zeros(0, np.int64)
+    return int(np.setxor1d(union, ex).size)
+
+
+def check_topk_set(sel, s, k, what=""):
+    """One top-k selection (any order, no duplicates, exactly k) against the
+    oracle's scores, up to near-cut candidates."""
+    sel = np.sort(np.asarray(sel))
+    assert len(sel) == k and np.all(np.diff(sel) > 0), f"{what}: {len(sel)} indices, expected {k} distinct"
+    req, alw = near_cut_topk(s, k)
+    assert np.all(np.isin(req, sel)), f"{what}: misses {np.setdiff1d(req, sel)}"
+    assert np.all(np.isin(sel, alw)), f"{what}: holds {np.setdiff1d(sel, alw)}"
+
+
 def csr_rows(row_ptr, col_idx):
     rp = np.asarray(row_ptr)
     ci = np.asarray(col_idx)

@@ -4,10 +4,13 @@ oracle (oracle/losa.py), through the C ABI.
 Each iteration is checked piece by piece:
   * page means of the cached keys against the oracle's pooling;
   * locality scores (fp64 on both sides) against the oracle's, and the Active
-    list exactly against the oracle's selection applied to the GPU's scores
-    (the decision taken in the kernel's precision);
-  * page scores (fp32) against the oracle's, and every kv head's page union
-    exactly against the oracle's top-k and union applied to the GPU's scores;
+    list against the oracle's selection from its own scores, exact except for
+    tokens within 1e-5 (relative) of the cut;
+  * page scores (fp32) against the oracle's, element by element, and every kv
+    head's page union against the oracle's per-row top-k of its own fp64 page
+    scores: the union holds every page some row of the group must keep and
+    only pages some row may keep (near-cut pages, within 1e-5 relative of a
+    row's cut, may go either way);
   * Active rows of o / lse against the oracle's attention over (union pages +
     block) given the GPU's Active list and unions; Stable rows bit for bit
     unchanged.
@@ -22,7 +25,7 @@ import torch
 import oracle
 import oracle.losa as olosa
 import sparse_bidirectional_attention_amd as sd
-from gpu_util import check_out, host_inputs, say, to_dev, to_np
+from gpu_util import check_out, check_topk_set, check_union_of_topk, host_inputs, say, to_dev, to_np
 from workloads import tiny_random
 from workloads.configs import LOSA_WORKLOADS, scaled
 from workloads.generate import make_losa_base, make_losa_cache, make_losa_iteration
@@ -96,20 +99,26 @@ def _step(run, x, x_prev, t, debug=True):
     for b in range(w.batch):
         for g in range(w.kv_heads):
             assert 1 <= counts[b, g] <= run.cap and np.all(np.diff(unions[b][g]) > 0), f"union {b},{g} malformed"
+    # The Active set and the page unions against the oracle's own fp64
+    # locality and page scores: exact, except for candidates within CUT_REL
+    # of a cut (LoSA, section 3, core principles).
+    loc_ref = olosa.locality_scores(x["q"], x_prev["q"])
+    for b in range(w.batch):
+        check_topk_set(active[b], loc_ref[b], w.n_active, f"iteration {t} Active b={b}")
+    kp_ref = olosa.pool_pages(run.cache["k_cache"], w.page)
+    s_ref = olosa.page_scores(x["q"], active, kp_ref)
+    G = w.q_heads // w.kv_heads
+    n_near = 0
+    for b in range(w.batch):
+        for g in range(w.kv_heads):
+            rows = s_ref[b, g * G:(g + 1) * G].reshape(-1, s_ref.shape[-1])
+            n_near += check_union_of_topk(unions[b][g], rows, w.pages_per_query, f"iteration {t} union b={b} g={g}")
     if debug:
         loc = run.loc.cpu().numpy()
-        loc_ref = olosa.locality_scores(x["q"], x_prev["q"])
         np.testing.assert_allclose(loc, loc_ref, rtol=1e-12, atol=1e-300)
-        np.testing.assert_array_equal(active, olosa.select_active(loc, w.n_active))
-        kp_ref = olosa.pool_pages(run.cache["k_cache"], w.page)
-        s_ref = olosa.page_scores(x["q"], active, kp_ref)
         s_gpu = run.scores.cpu().numpy().astype(np.float64)
         err = np.abs(s_gpu - s_ref).max()
         assert err <= 1e-5 * max(1.0, np.abs(s_ref).max()), f"page scores max-abs {err:.3e}"
-        ref_unions = olosa.union_pages(olosa.select_pages(s_gpu, w.pages_per_query), w.kv_heads)
-        for b in range(w.batch):
-            for g in range(w.kv_heads):
-                np.testing.assert_array_equal(unions[b][g], ref_unions[b][g], err_msg=f"union b={b} g={g}")
     o_ref, l_ref = olosa.losa_attention(x["q"], run.cache["k_cache"], run.cache["v_cache"], x["k_blk"], x["v_blk"],
                                         active, unions, w.page, oracle.decode_bf16(o_prev), l_prev)
     o_new, l_new = host_inputs(run.o), to_np(run.lse)
@@ -119,7 +128,8 @@ def _step(run, x, x_prev, t, debug=True):
         assert np.array_equal(o_new[b][:, stable[b]], o_prev[b][:, stable[b]]), f"iteration {t}: Stable O changed"
         assert np.array_equal(l_new[b][:, stable[b]], l_prev[b][:, stable[b]]), f"iteration {t}: Stable lse changed"
     e = check_out(oracle.decode_bf16(o_new), o_ref, l_new, l_ref, "bf16", f"{w.name} iteration {t}")
-    say(f"  iteration {t}: active {active[0].tolist()} union sizes {counts.ravel().tolist()} O max-abs {e[0]:.2e}")
+    say(f"  iteration {t}: active {active[0].tolist()} union sizes {counts.ravel().tolist()} near-cut pages {n_near} "
+        f"O max-abs {e[0]:.2e}")
 
 
 def _block(w, n_iter=4):

@@ -10,9 +10,13 @@ schedule; skipped steps never select, so the pattern in force is the one a
 full run would have.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import oracle
 import sparse_bidirectional_attention_amd as sd
@@ -29,7 +33,30 @@ def _sample(n, k):
     return s
 
 
+def _check_column_groups(w, xh, cols, kcol, groups):
+    """The column selection of each kv group in `groups` against the top-kcol
+    of the oracle's fp64 column scores, which read the oracle's own dense
+    log-sum-exp (PulseCol, Abstract).  The groups are independent, so the
+    oracle runs them on a thread pool (numpy's ufuncs and BLAS release the
+    interpreter lock); the results are the plain serial ones."""
+    G = w.q_heads // w.kv_heads
+
+    def one(g):
+        sl = slice(g * G, (g + 1) * G)
+        _, rl = oracle.dense_attention(xh["q"][:, sl], xh["k"][:, g:g + 1], xh["v"][:, g:g + 1])
+        C = oracle.column_scores(xh["q"][:, sl], xh["k"][:, g:g + 1], rl)
+        return check_topk_rows(cols[0, g:g + 1], C[0], kcol, f"columns g={g}")
+
+    if len(groups) <= 1:
+        return [one(g) for g in groups]
+    with threadpool_limits(limits=max(1, (os.cpu_count() or 4) // len(groups)), user_api="blas"):
+        with ThreadPoolExecutor(len(groups)) as ex:
+            return list(ex.map(one, groups))
+
+
 def _run_steps(w, steps, n_qblocks=8, n_rows=32, col_groups=None):
+    """col_groups: for a column workload, {step: [kv groups whose selection is
+    checked]}; None checks every group at every selection step."""
     base = make_base(w)
     p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
     acts = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
@@ -70,12 +97,8 @@ def _run_steps(w, steps, n_qblocks=8, n_rows=32, col_groups=None):
                     pattern = (rp, ci)
                 else:
                     cols = _d2h(ci_ptr, w.batch * w.kv_heads * kcol).reshape(w.batch, w.kv_heads, kcol)
-                    G = H // w.kv_heads
-                    for g in (col_groups if col_groups is not None else range(w.kv_heads)):
-                        sl = slice(g * G, (g + 1) * G)
-                        _, rl = oracle.dense_attention(xh["q"][:, sl], xh["k"][:, g:g + 1], xh["v"][:, g:g + 1])
-                        C = oracle.column_scores(xh["q"][:, sl], xh["k"][:, g:g + 1], rl)
-                        n_ex = check_topk_rows(cols[0, g:g + 1], C[0], kcol, f"columns g={g}")
+                    groups = list(range(w.kv_heads)) if col_groups is None else col_groups.get(t, [])
+                    for g, n_ex in zip(groups, _check_column_groups(w, xh, cols, kcol, groups)):
                         say(f"  columns g={g}: exempt={n_ex}")
                     pending = cols
             # outputs on samples
@@ -113,5 +136,19 @@ def test_sparsed_64k_topk():
     _run_steps(WORKLOADS["sparsed_64k"], [204, 205, 1023], n_qblocks=8, n_rows=16)
 
 
-def test_pulsecol_16k_columns():
-    _run_steps(WORKLOADS["pulsecol_dream7b_16k"], [0, 1, 63, 64, 65, 191], n_rows=64, col_groups=[0])
+def test_pulsecol_16k_columns_first_selection():
+    """Step 0 selects the columns of all four kv groups: every group's
+    selection against the oracle, then the sparse steps that reuse it."""
+    _run_steps(WORKLOADS["pulsecol_dream7b_16k"], [0, 1, 63], n_rows=64, col_groups={0: [0, 1, 2, 3]})
+
+
+def test_pulsecol_16k_columns_refresh_64():
+    """The refresh at step 64 selects from its own dense pass: kv group 1's
+    selection against the oracle, then the sparse step that reuses it."""
+    _run_steps(WORKLOADS["pulsecol_dream7b_16k"], [64, 65], n_rows=64, col_groups={64: [1]})
+
+
+def test_pulsecol_16k_columns_refresh_128():
+    """The refresh at step 128: kv group 2's selection against the oracle,
+    then sparse steps up to the schedule's last."""
+    _run_steps(WORKLOADS["pulsecol_dream7b_16k"], [128, 129, 191], n_rows=64, col_groups={128: [2]})
