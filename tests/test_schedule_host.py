@@ -24,9 +24,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 @pytest.fixture(scope="module")
 def fake():
-    if not os.path.exists(sdbuild.FAKE_LIB):
+    # SDATTN_FAKE_LIB names another build of the same sources (the sanitized
+    # one, tests/test_sanitize_host.py); by default the plain build is used
+    path = os.environ.get("SDATTN_FAKE_LIB") or sdbuild.FAKE_LIB
+    if path == sdbuild.FAKE_LIB and not os.path.exists(path):
         sdbuild.build_fake()
-    lib = sd.declare(ctypes.CDLL(sdbuild.FAKE_LIB), required=False)
+    lib = sd.declare(ctypes.CDLL(path), required=False)
     lib.sdattn_fake_log_entry.restype = ctypes.c_char_p
     lib.sdattn_fake_log_entry.argtypes = [ctypes.c_int]
     lib.sdattn_fake_reset.argtypes = [ctypes.c_int, ctypes.c_int]
