@@ -7,7 +7,15 @@ library's schedule driver (C ABI): dense warm-up steps, the pattern
 selection step, then sparse steps reusing the pattern (refreshes where the
 schedule has them).  K steps form one schedule: with K equal to the
 workload's step count it is exactly that schedule; otherwise the schedule is
-rescaled to K steps with the same warm-up fraction and refresh spacing.
+rescaled to K steps with the same warm-up fraction (rounded to the nearest
+step) and refresh spacing.  The step actions come from the library's own
+driver (sdattn_schedule_action).  Beside the measured K-step schedule, the
+line gives the workload's full schedule modelled from the per-action median
+step times (modelled_native_schedule_ms_per_step).
+
+By default the 64K headline is followed by the metric's other contexts, the
+8K, 16K and 32K workloads, each run for the same K steps and reported under
+"configs" (--no-sweep skips them).
 
 Inputs are the seeded synthetic tensors of the workload (planted per-head
 structure), resident in HBM before timing starts: the step-0 tensors serve
@@ -54,13 +62,19 @@ def rescaled(w, K):
     if K == w.total_steps:
         return w
     f = K / w.total_steps
-    dense = min(K, int(math.ceil(w.dense_steps * f)))
-    sel = min(dense, int(math.ceil(w.select_step * f))) if w.select_step else 0
+
+    def nearest(x):  # round half up: keeps the warm-up share (205 of 1024 -> 4 of 20)
+        return int(math.floor(x + 0.5))
+
+    dense = min(K, nearest(w.dense_steps * f))
+    if w.dense_steps > 0:
+        dense = max(dense, 1)
+    sel = min(dense, nearest(w.select_step * f)) if w.select_step else 0
     sel = min(sel, K - 1)
     if w.refresh_dense and w.selector != "blocks" and dense > 0:
         sel = min(sel, dense - 1)  # these selectors read a dense pass's lse: the selection step is dense
-    interval = max(1, int(round(w.refresh_interval * f))) if w.refresh_interval else 0
-    refresh = tuple(sorted({min(K - 1, int(round(t * f))) for t in w.refresh_steps} - {sel}))
+    interval = max(1, nearest(w.refresh_interval * f)) if w.refresh_interval else 0
+    refresh = tuple(sorted({min(K - 1, nearest(t * f)) for t in w.refresh_steps} - {sel}))
     return scaled(w, total_steps=K, dense_steps=dense, select_step=sel, refresh_interval=interval,
                   refresh_steps=refresh)
 
@@ -118,16 +132,26 @@ class GpuMonitor:
         if self._thread.is_alive():
             self._thread.join(timeout=30)
 
+    MIN_REGION_S = 2.0    # shorter timed regions report no clock/power statistics
+    MIN_SAMPLES = 3
+    SETTLE_S = 0.5        # readings that start this early in the region may describe the idle GPU before it
+
     def summary(self):
-        """Statistics of the samples taken wholly inside the timed region."""
+        """Statistics of the samples taken wholly inside the timed region,
+        after its first SETTLE_S seconds; none unless the region lasts at least
+        MIN_REGION_S and at least MIN_SAMPLES readings qualify (amd-smi reports
+        averages over its own sampling window, so a lone reading in a short
+        region can describe the idle GPU before the work)."""
         import numpy as np
         if not self._thread.ident:
             return {"samples": 0, "error": self.error or ("amd-smi not found" if not self.exe
                                                           else "not sampled (--no-gpu-monitor)")}
-        inside = [s for s in self.samples if s[0] >= self.t_begin and s[1] <= self.t_end]
-        if not inside:
+        region = self.t_end - self.t_begin
+        inside = [s for s in self.samples if s[0] >= self.t_begin + self.SETTLE_S and s[1] <= self.t_end]
+        if region < self.MIN_REGION_S or len(inside) < self.MIN_SAMPLES:
             return {"samples": 0, "error": self.error or (
-                f"no amd-smi reading fell inside the {self.t_end - self.t_begin:.2f} s timed region")}
+                f"timed region {region:.2f} s with {len(inside)} settled amd-smi readings: at least "
+                f"{self.MIN_REGION_S:g} s and {self.MIN_SAMPLES} readings are needed")}
         pw = np.array([s[2] for s in inside])
         ck = np.array([s[3] for s in inside if s[3] is not None])
         out = {"samples": len(inside), "tool": "amd-smi metric -p -c",
@@ -550,59 +574,44 @@ def cpu_baseline_losa(w, cache, iters):
             "per_step_ms": {"dense": round(1e3 * t_dense, 1), "losa": round(1e3 * t_step, 1)}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="sparsed_64k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--selector", choices=["pooled", "exact"], default="pooled",
-                    help="block workloads: pattern from pooled scores (default) or from the exact block mass of "
-                         "the last dense step")
-    ap.add_argument("--no-gpu-monitor", action="store_true",
-                    help="do not sample power and clocks with amd-smi (e.g. under a profiler)")
-    ap.add_argument("--no-sdpa-baseline", action="store_true",
-                    help="skip timing torch's own SDPA (flash backend) on the dense step for context")
-    ap.add_argument("--probe-interval", type=int, default=None,
-                    help="adaptive anchors (block workloads): probe the pattern every N steps after the selection")
-    ap.add_argument("--min-overlap", type=float, default=0.9,
-                    help="with --probe-interval: adopt a probe whose overlap with the cached pattern is below this")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="first run one plain device-to-device copy of this many MiB (a known-size "
-                         "kernel that scales the profiler's HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
-              "(sharding the heads across GPUs is not implemented); use --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    from workloads.configs import LOSA_WORKLOADS
-    if args.workload in LOSA_WORKLOADS:
-        run_losa(args, LOSA_WORKLOADS[args.workload])
-        return
+def schedule_actions(sd, p, w):
+    """The action of every step of workload w's schedule, from the library's
+    own driver (sdattn_schedule_action on a handle of that schedule)."""
+    h = sd.sdattn_schedule_create(p, schedule_desc(sd, w))
+    try:
+        return [sd.sdattn_schedule_action(h, t) for t in range(w.total_steps)]
+    finally:
+        sd.sdattn_schedule_destroy(h)
 
+
+def d2h_int32(ptr, n):
+    """n int32 values from a device pointer (a borrowed schedule buffer)."""
+    import ctypes
+    import numpy as np
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    out = np.zeros(n, np.int32)
+    rc = hip.hipMemcpy(out.ctypes.data, ptr, 4 * n, 2)  # hipMemcpyDeviceToHost
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed ({rc})")
+    return out
+
+
+def run_schedule(args, w0, K, warmup, with_gpu_state=True):
+    """One workload's schedule of K steps through the C-ABI driver, timed with
+    HIP events per step and over the whole schedule.  Returns the JSON record
+    (without the oracle leg) and the host inputs (for the oracle leg)."""
     import numpy as np
     import torch
 
     import sparse_bidirectional_attention_amd as sd
-    from workloads import get_workload, make_base, make_step
-    import oracle
+    from workloads import make_base, make_step
 
-    w0 = get_workload(args.workload)
-    from workloads.configs import scaled
-    if args.selector == "exact":
-        if w0.selector != "blocks" or w0.dense_steps < 1:
-            print("--selector exact needs a block workload with at least one dense step", file=sys.stderr)
-            sys.exit(2)
-        # the exact mass reads the lse of a dense pass: select on the last dense step at the latest
-        w0 = scaled(w0, selector="blocks_exact", refresh_dense=True, select_step=min(w0.select_step, w0.dense_steps - 1))
-    if args.probe_interval is not None:
-        w0 = scaled(w0, probe_interval=args.probe_interval, min_overlap=args.min_overlap)
-    K = args.steps if args.steps is not None else w0.total_steps
     w = rescaled(w0, K)
-    acts = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
-                                   w.refresh_steps, w.refresh_dense, w.probe_interval)
-    torch.cuda.set_device(0)
+    p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
+    acts = schedule_actions(sd, p, w)
+    native_acts = schedule_actions(sd, p, w0)
     log(f"workload {w.name}: L={w.seq_len} Hq={w.q_heads} Hkv={w.kv_heads} d={w.head_dim} {w.dtype} "
         f"block={w.block}; schedule of {K} steps: " + ", ".join(f"{a} x{acts.count(a)}" for a in sorted(set(acts))))
     t0 = time.time()
@@ -615,20 +624,17 @@ def main():
     xs = {n: to_dev(a) for n, a in xsh.items()}
     o = torch.empty_like(x0["q"])
     lse = torch.empty(x0["q"].shape[:3], dtype=torch.float32, device="cuda")
-    p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
 
-    def inputs_for(t, a):
+    def inputs_for(a):
         return x0 if a == "DENSE" else xs
 
     # warm-up: W untimed steps of a schedule of the same shape
-    if args.warmup > 0:
-        ww = rescaled(w0, max(2, args.warmup))
+    if warmup > 0:
+        ww = rescaled(w0, max(2, warmup))
         hw = sd.sdattn_schedule_create(p, schedule_desc(sd, ww))
-        acts_w = oracle.schedule_actions(ww.total_steps, ww.dense_steps, ww.select_step, ww.refresh_interval,
-                                         ww.refresh_steps, ww.refresh_dense, ww.probe_interval)
-        for t in range(args.warmup):
-            x = inputs_for(t, acts_w[t])
-            sd.sdattn_schedule_step(hw, t, x["q"], x["k"], x["v"], o, lse)
+        for t in range(warmup):
+            x = inputs_for(sd.sdattn_schedule_action(hw, t % ww.total_steps))
+            sd.sdattn_schedule_step(hw, t % ww.total_steps, x["q"], x["k"], x["v"], o, lse)
         torch.cuda.synchronize()
         sd.sdattn_schedule_destroy(hw)
 
@@ -646,14 +652,14 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     monitor = GpuMonitor()
-    if not args.no_gpu_monitor:
+    if with_gpu_state and not args.no_gpu_monitor:
         monitor.start()
     t_wall = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for t in range(K):
-        x = inputs_for(t, acts[t])
+        x = inputs_for(acts[t])
         ev[t][0].record()
         sd.sdattn_schedule_step(h, t, x["q"], x["k"], x["v"], o, lse)
         ev[t][1].record()
@@ -666,23 +672,16 @@ def main():
     stats, last_sel = sd.sdattn_schedule_stats(h)
     n_probes, n_adopted, last_overlap = sd.sdattn_schedule_probe_stats(h)
 
-    # pattern size for the kept-FLOP count
+    # pattern size for the kept-FLOP count, read back from the driver's buffers
     L, H, Hkv, d = w.seq_len, w.q_heads, w.kv_heads, w.head_dim
-    kept_flops = None
+    rp_ptr, ci_ptr, cap = sd.sdattn_schedule_mask(h)
     if w.selector != "columns":
-        rp_ptr, ci_ptr, cap = sd.sdattn_schedule_mask(h)
         rows = w.batch * H * (-(-L // w.block))
-        last = torch.empty(1, dtype=torch.int32, device="cuda")
-        import ctypes
-        hip = ctypes.CDLL("libamdhip64.so")
-        hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
-        nnz = np.zeros(1, np.int32)
-        hip.hipMemcpy(nnz.ctypes.data, rp_ptr + 4 * rows, 4, 2)
-        nnz = int(nnz[0])
+        nnz = int(d2h_int32(rp_ptr + 4 * rows, 1)[0])
         kept_flops = 4.0 * d * w.block * w.block * nnz
         density = nnz / (rows * (-(-L // w.block)))
     else:
-        kcol = oracle.count_from_fraction(w.column_keep_frac, L)
+        kcol = cap // (w.batch * Hkv)  # the column list holds [B][Hkv][kcol]
         kept_flops = 4.0 * d * L * kcol * H * w.batch
         nnz = kcol * Hkv
         density = kcol / L
@@ -697,15 +696,13 @@ def main():
     sparse_ms = med(step_ms[idx["SPARSE"]]) if idx.get("SPARSE") else None
     dense_ms = med(step_ms[idx["DENSE"]]) if idx.get("DENSE") else None
     # dense baseline on the same GPU: the dense forward for every step
-    pd = sd.problem(w.batch, H, Hkv, L, d, w.dtype)
     nd = 3 if L >= 32768 else 10
-    for _ in range(1):
-        sd.sdattn_forward_dense(pd, x0["q"], x0["k"], x0["v"], o, lse)
+    sd.sdattn_forward_dense(p, x0["q"], x0["k"], x0["v"], o, lse)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(nd):
-        sd.sdattn_forward_dense(pd, x0["q"], x0["k"], x0["v"], o, lse)
+        sd.sdattn_forward_dense(p, x0["q"], x0["k"], x0["v"], o, lse)
     e1.record()
     torch.cuda.synchronize()
     dense_base_ms = e0.elapsed_time(e1) / nd
@@ -721,13 +718,21 @@ def main():
 
     probe_ms = med(step_ms[idx["PROBE_SPARSE"]]) if idx.get("PROBE_SPARSE") else None
     ms_per_step = total_ms / K
-    # per action: median and p10/p90 of the step times; the schedule modelled
-    # from the medians, beside the measured one
+    # per action: median and p10/p90 of the step times; the K-step schedule
+    # modelled from the medians (beside the measured one), and the workload's
+    # own full schedule modelled from the same medians
     step_stats = {a: {"n": len(v), "median_ms": round(float(np.median(step_ms[v])), 4),
                       "p10_ms": round(float(np.percentile(step_ms[v], 10)), 4),
                       "p90_ms": round(float(np.percentile(step_ms[v], 90)), 4)} for a, v in sorted(idx.items())}
-    modelled_ms = sum(len(v) * float(np.median(step_ms[v])) for v in idx.values()) / K
+    medians = {a: float(np.median(step_ms[v])) for a, v in idx.items()}
+    modelled_ms = sum(len(v) * medians[a] for a, v in idx.items()) / K
+    native_counts = {a: native_acts.count(a) for a in sorted(set(native_acts))}
+    if all(a in medians for a in native_counts):
+        native_ms = sum(n * medians[a] for a, n in native_counts.items()) / len(native_acts)
+    else:  # an action of the full schedule did not occur in the K steps
+        native_ms = None
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+
     # Roofline figures use each kernel's average launch inside the timed region:
     # a SPARSE step is one sparse forward, a DENSE step one dense forward.
     def mean(a):
@@ -767,19 +772,29 @@ def main():
     roof["kernel"] = dom
 
     # the MFMA peak scales with the graphics clock: the published peak is at 2.4 GHz
-    gpu_state = monitor.summary()
-    if "gfx_clock_mhz" in gpu_state:
+    gpu_state = monitor.summary() if with_gpu_state else None
+    if gpu_state and "gfx_clock_mhz" in gpu_state:
         clk = gpu_state["gfx_clock_mhz"]["median"]
-        gpu_state["peak_at_median_clock_tflops"] = round(peak * clk / MAX_GFX_CLOCK_MHZ, 1)
-        gpu_state["frac_of_peak_at_median_clock"] = {
-            k: round(v["achieved"] / (peak * clk / MAX_GFX_CLOCK_MHZ), 4) for k, v in kernels.items() if v["achieved"]}
+        scaled_peak = peak * clk / MAX_GFX_CLOCK_MHZ
+        fr = {k: v["achieved"] / scaled_peak for k, v in kernels.items() if v["achieved"]}
+        if any(f > 1.0 for f in fr.values()):
+            # a kernel above the clock-scaled peak: the clock readings do not describe the timed work
+            gpu_state["peak_at_median_clock_tflops"] = None
+            gpu_state["frac_of_peak_at_median_clock"] = None
+            gpu_state["note"] = "clock readings inconsistent with the measured throughput; not used"
+        else:
+            gpu_state["peak_at_median_clock_tflops"] = round(scaled_peak, 1)
+            gpu_state["frac_of_peak_at_median_clock"] = {k: round(f, 4) for k, f in fr.items()}
+    budget = (f"top-{w.keep_frac:g}" if w.budget == "topk" and w.selector != "columns"
+              else f"mass {w.mass:g} cap {w.max_mean_density:g}" if w.selector != "columns"
+              else f"columns {w.column_keep_frac:g}")
     out = {
         "metric": METRIC,
         "value": round(ms_per_step, 4),
         "unit": "ms/denoise step",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": False,
         "scaling": "weak",
@@ -787,11 +802,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w0.name, "batch": w.batch, "q_heads": H, "kv_heads": Hkv, "seq_len": L,
-                   "head_dim": d, "block": w.block,
-                   "selector": w.selector, "budget": (f"top-{w.keep_frac:g}" if w.budget == "topk" and w.selector != "columns"
-                                                      else f"mass {w.mass:g} cap {w.max_mean_density:g}"
-                                                      if w.selector != "columns" else f"columns {w.column_keep_frac:g}"),
-                   "schedule": {a: acts.count(a) for a in sorted(set(acts))}},
+                   "head_dim": d, "block": w.block, "selector": w.selector, "budget": budget,
+                   "schedule": {a: acts.count(a) for a in sorted(set(acts))},
+                   "native_schedule": native_counts},
         "roofline": roof,
         "phases": {"dense_step_ms": round(dense_ms, 3) if dense_ms else None,
                    "select_ms": round(select_ms, 3) if select_ms else None,
@@ -807,19 +820,108 @@ def main():
         "dense_baseline": {"ms_per_step": round(dense_base_ms, 3), "tflops": round(dense_base_tflops, 1),
                            "mfma_frac": round(dense_base_tflops / peak, 4),
                            "schedule_speedup": round(dense_base_ms / ms_per_step, 3),
+                           "native_schedule_speedup": round(dense_base_ms / native_ms, 3) if native_ms else None,
                            "sparse_step_speedup": round(dense_base_ms / sparse_ms, 3) if sparse_ms else None},
         "kernels": kernels,
         "step_times": step_stats,
         "modelled_ms_per_step": round(modelled_ms, 4),
+        "modelled_native_schedule_ms_per_step": round(native_ms, 4) if native_ms else None,
         "wall_s": round(wall, 2),
         "gpu_state": gpu_state,
         "schedule_stats": stats,
     }
     if not args.no_sdpa_baseline and w.dtype == "bf16":
         out["sdpa_dense_baseline"] = sdpa_dense_baseline(x0, w, dense_launch_ms)
+    del x0, xs, o, lse
+    torch.cuda.empty_cache()
+    return out, (acts, x0h, xsh)
+
+
+# The other contexts of the metric (8K-64K), run after the 64K headline with
+# the same step count: one compact record each.
+SWEEP = ("llada8b_8k", "pulsecol_dream7b_16k", "sparsed_32k")
+
+
+def compact(rec):
+    ph = rec["phases"]
+    return {"ms_per_step": rec["value"], "steps": rec["steps"], "schedule": rec["config"]["schedule"],
+            "modelled_native_schedule_ms_per_step": rec["modelled_native_schedule_ms_per_step"],
+            "native_schedule": rec["config"]["native_schedule"],
+            "dense_step_ms": ph["dense_step_ms"], "select_ms": ph["select_ms"], "sparse_step_ms": ph["sparse_step_ms"],
+            "sparse_effective_tflops": ph["sparse_effective_tflops"], "sparse_mfma_frac": ph["sparse_mfma_frac"],
+            "kept_density": ph["kept_density"],
+            "dense_tflops": rec["kernels"]["flash_fwd_bf16_dense"]["achieved"],
+            "dense_mfma_frac": rec["kernels"]["flash_fwd_bf16_dense"]["frac"],
+            "sparse_traffic": next(iter(rec["kernels"].values()))["traffic"],
+            "dense_baseline_ms_per_step": rec["dense_baseline"]["ms_per_step"],
+            "native_schedule_speedup_vs_dense": rec["dense_baseline"]["native_schedule_speedup"],
+            "sparse_step_speedup_vs_dense": rec["dense_baseline"]["sparse_step_speedup"],
+            "sdpa_dense_ms": (rec.get("sdpa_dense_baseline") or {}).get("ms_per_step")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="sparsed_64k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--selector", choices=["pooled", "exact"], default="pooled",
+                    help="block workloads: pattern from pooled scores (default) or from the exact block mass of "
+                         "the last dense step")
+    ap.add_argument("--no-gpu-monitor", action="store_true",
+                    help="do not sample power and clocks with amd-smi (e.g. under a profiler)")
+    ap.add_argument("--no-sdpa-baseline", action="store_true",
+                    help="skip timing torch's own SDPA (flash backend) on the dense step for context")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="time only the named workload (by default the 64K headline is followed by the 8K, 16K "
+                         "and 32K workloads, reported under 'configs')")
+    ap.add_argument("--probe-interval", type=int, default=None,
+                    help="adaptive anchors (block workloads): probe the pattern every N steps after the selection")
+    ap.add_argument("--min-overlap", type=float, default=0.9,
+                    help="with --probe-interval: adopt a probe whose overlap with the cached pattern is below this")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a known-size "
+                         "kernel that scales the profiler's HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(sharding the heads across GPUs is not implemented); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    from workloads.configs import LOSA_WORKLOADS
+    if args.workload in LOSA_WORKLOADS:
+        run_losa(args, LOSA_WORKLOADS[args.workload])
+        return
+
+    import torch
+
+    from workloads import get_workload
+    from workloads.configs import scaled
+
+    w0 = get_workload(args.workload)
+    if args.selector == "exact":
+        if w0.selector != "blocks" or w0.dense_steps < 1:
+            print("--selector exact needs a block workload with at least one dense step", file=sys.stderr)
+            sys.exit(2)
+        # the exact mass reads the lse of a dense pass: select on the last dense step at the latest
+        w0 = scaled(w0, selector="blocks_exact", refresh_dense=True, select_step=min(w0.select_step, w0.dense_steps - 1))
+    if args.probe_interval is not None:
+        w0 = scaled(w0, probe_interval=args.probe_interval, min_overlap=args.min_overlap)
+    K = args.steps if args.steps is not None else w0.total_steps
+    torch.cuda.set_device(0)
+    out, (acts, x0h, xsh) = run_schedule(args, w0, K, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         out["cpu_baseline"] = cpu_baseline(w0, acts, x0h, xsh)
+    del x0h, xsh
+    sweep = (args.workload == "sparsed_64k" and args.selector == "pooled" and args.probe_interval is None
+             and not args.no_sweep and args.copy_calibration_mib == 0)
+    if sweep:
+        cfgs = {}
+        for name in SWEEP:
+            rec, _ = run_schedule(args, get_workload(name), K, args.warmup, with_gpu_state=False)
+            cfgs[name] = compact(rec)
+        out["configs"] = cfgs
     print(json.dumps(out), flush=True)
 
 
