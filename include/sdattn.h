@@ -413,8 +413,12 @@ SDATTN_API void sdattn_schedule_destroy(sdattn_schedule* s);
  * prefix_len/page <= 4096, 1 <= n_active <= block_len (else
  * SDATTN_ERR_BUDGET), 1 <= pages_per_query <= prefix_len/page (else
  * SDATTN_ERR_BUDGET).  softmax_scale <= 0 means 1/sqrt(head_dim).  Launch
- * grids bound batch <= 65535, kv_heads <= 65535 and
- * batch * q_heads * n_active < 2^31 (else SDATTN_ERR_SHAPE).
+ * grids bound batch <= 65535 and kv_heads <= 65535, and every launch of a
+ * call must fit 2^32 work-items per grid dimension: the top-k launch takes
+ * 256 work-items per (batch, query head, Active token) row, so
+ * batch * q_heads * n_active < 2^24, and the merge takes 64 per (batch,
+ * query head, block token) row (else SDATTN_ERR_SHAPE, before anything is
+ * enqueued).
  * Calls that share a workspace must be ordered on one stream. */
 typedef struct {
     int32_t batch, q_heads, kv_heads, prefix_len, block_len, head_dim;

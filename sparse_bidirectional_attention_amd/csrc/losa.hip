@@ -736,8 +736,6 @@ sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     if (!(scale > 0.f)) scale = 1.f / sqrtf(static_cast<float>(p->head_dim));
     if (!isfinite(scale)) return fail(SDATTN_ERR_SHAPE, "softmax_scale must be finite");
     if (p->batch > 65535 || p->kv_heads > 65535) return fail(SDATTN_ERR_SHAPE, "batch and kv_heads must be <= 65535");
-    if (static_cast<int64_t>(p->batch) * p->q_heads * p->n_active >= (int64_t{1} << 31))
-        return fail(SDATTN_ERR_SHAPE, "batch * q_heads * n_active must be < 2^31");
 
     Plan pl;
     Dims& dm = pl.dm;
@@ -773,6 +771,18 @@ sdattn_status check_losa(const sdattn_losa_problem* p, Plan* out) {
     pl.ws_step = pl.off_part +
                  static_cast<size_t>(dm.B) * dm.Hkv * pl.rt_s * pl.RT_s * (pl.nch_s + 1) * part_row;
     pl.ws_dense = static_cast<size_t>(dm.B) * dm.Hkv * pl.rt_d * pl.RT_d * (pl.nch_d + 1) * part_row;
+    // Every launch of a call must fit HIP's limit of 2^32 work-items per grid
+    // dimension; checked here, before anything is enqueued, so that a call
+    // that fails writes nothing.
+    constexpr int64_t kMaxItems = int64_t{1} << 32;
+    const int64_t topk_rows = static_cast<int64_t>(dm.B) * dm.Hq * dm.n_a;
+    const int64_t topk_items = dm.kpq <= 64 ? topk_rows * 256 : (topk_rows + 3) / 4 * 256;
+    const int64_t merge_items = (static_cast<int64_t>(dm.B) * dm.Hkv * std::max(pl.R_s, pl.R_d) + 3) / 4 * 256;
+    const int64_t attend_s = static_cast<int64_t>((pl.nch_s + 1 + 7) / 8) * 8 * pl.rt_s * 256;
+    const int64_t attend_d = static_cast<int64_t>((pl.nch_d + 1 + 7) / 8) * 8 * pl.rt_d * 256;
+    if (topk_items >= kMaxItems || merge_items >= kMaxItems || attend_s >= kMaxItems || attend_d >= kMaxItems)
+        return fail(SDATTN_ERR_SHAPE, "problem too large for one launch: batch * q_heads * n_active (and "
+                                      "batch * q_heads * block_len / 4) must stay below 2^24");
     *out = pl;
     return SDATTN_OK;
 }

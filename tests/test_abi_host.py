@@ -206,6 +206,9 @@ def test_losa_validation():
         (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 0), 4),      # pages_per_query
         (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 2049), 4),
         (sd.losa_problem(1, 32, 8, 32768, 32, 128, 16, 8, 8, "bf16", float("inf")), 2),
+        # 2^24 (batch, query head, Active token) rows: below the old 2^31 bound, but the top-k
+        # launch would need 2^32 work-items
+        (sd.losa_problem(2048, 256, 8, 4096, 64, 64, 16, 32, 8), 2),
     ]
     for p, code in cases:
         assert lib.sdattn_losa_workspace(ctypes.byref(p), ctypes.byref(ws), ctypes.byref(cap)) == code, \
@@ -222,3 +225,7 @@ def test_losa_validation():
     assert lib.sdattn_losa_step(ctypes.byref(good), *step_missing, None, None, BAD, ctypes.c_size_t(1 << 40),
                                 None) == 1
     assert "union_pages" in sd.sdattn_last_error()
+    # one row fewer than 2^24 at the same shape passes the launch bounds
+    near = sd.losa_problem(2047, 256, 8, 4096, 64, 64, 16, 32, 8)
+    assert lib.sdattn_losa_workspace(ctypes.byref(near), ctypes.byref(ws), ctypes.byref(cap)) == 0, \
+        sd.sdattn_last_error()
