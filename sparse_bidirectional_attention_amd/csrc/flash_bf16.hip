@@ -63,9 +63,33 @@ constexpr int SG_VALU = 0x002;
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DSR = 0x100;
 
-template <int D, int NW, int KT, int NST, int MODE>
+constexpr int gcd_c(int a, int b) { return b ? gcd_c(b, a % b) : a; }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_from(F& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_from<0, N>(f);
+}
+
+// Block indices and row pointers are read through the constant address
+// space: they are uniform and read-only for the kernel's lifetime, so the
+// loads become scalar loads (an SGPR result, counted apart from the tile
+// DMAs' vector-memory counter).
+typedef const __attribute__((address_space(4))) int32_t cint32;
+
+template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
-    // KT keys per tile (32 or 64), NST LDS stages (tiles in flight: NST - 1)
+    // KT keys per tile (32 or 64), NST LDS stages (tiles in flight: NST - 1);
+    // the pipelined pass over 32-key tiles uses a ring of NK K slots and NV V
+    // slots instead (K fetched NK - 1 units ahead, V NV - 1)
     constexpr int KB = KT / 32;             // 32-key MFMA blocks per tile
     constexpr int T = NW * 64;
     constexpr int DK = D / 16;
@@ -80,12 +104,23 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     constexpr int STAGEB = 2 * TILEB;       // K tile then V tile
     static_assert(NDMA * T == SLOTS && T % UNITS == 0 && ROWS_PER_DMA % 4 == 0, "DMA tiling");
     static_assert(NW * 32 * OPITCH <= NST * STAGEB, "epilogue staging fits in the stages");
+    // 32-key piped pass: K ring slots 0..NK-1, then V ring slots 0..NV-1
+    constexpr bool RING = KT == 32 && MODE == MODE_BLOCK;
+    constexpr int RINGB = (NK + NV) * TILEB;
+    constexpr int SMEMB = RING && RINGB > NST * STAGEB ? RINGB : NST * STAGEB;
+    static_assert(!RING || (NK >= 2 && NV >= 2 && RINGB >= NST * STAGEB), "ring holds the checked pass's stages");
+    // with a K ring of three or more slots the redo flags sit in it, past the
+    // epilogue's staging rows, so the shared memory is exactly the ring (see
+    // the flag exchange below)
+    constexpr int FLAGOFF = NW * 32 * OPITCH;
+    constexpr bool FLAGS_IN_RING = RING && FLAGOFF + NW * 4 <= NK * TILEB;
 
-    __shared__ __attribute__((aligned(16))) char smem[NST * STAGEB];
+    __shared__ __attribute__((aligned(16))) char smem[SMEMB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // the same value, as a scalar
     const int l32 = lane & 31;
     const int hl = lane >> 5;
 
@@ -101,6 +136,25 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const uint32_t head_bytes = static_cast<uint32_t>(kv_len) * ROWB;
     const u32x4 rk = buffer_rsrc(p.k + kvoff, head_bytes);
     const u32x4 rv = buffer_rsrc(p.v + kvoff, head_bytes);
+    // contiguous tile sources: the descriptor of tile bytes [tb, head_bytes)
+    // of the head, so the lanes' offsets within a tile stay fixed and rows
+    // past the head's end (all of a tile past the last, tb = head_bytes)
+    // read as zero
+    // a uniform 64-bit value as two scalar dwords (readfirstlane returns a
+    // signed int: each half is taken back to uint32 before widening, so the
+    // low half does not sign-extend into the high one)
+    auto uniform64 = [](uint64_t x) __attribute__((always_inline)) -> uint64_t {
+        const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32)));
+        const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x)));
+        return (static_cast<uint64_t>(hi) << 32) | lo;
+    };
+    const uint64_t kaddr = uniform64(reinterpret_cast<uint64_t>(p.k + kvoff));
+    const uint64_t vaddr = uniform64(reinterpret_cast<uint64_t>(p.v + kvoff));
+    auto tile_rsrc = [&](uint64_t base, uint32_t tb) __attribute__((always_inline)) -> u32x4 {
+        return buffer_rsrc(reinterpret_cast<const void*>(base + tb), head_bytes - tb);
+    };
+    // LDS address (M0) of this wave's first DMA slot in the shared array
+    const uint32_t lds_wave = lds_addr((LDS_AS char*)smem) + static_cast<uint32_t>(wave_u) * 64 * 16;
     const int q0 = qt * (NW * 32);
 
     // ---- tile source ------------------------------------------------------
@@ -109,20 +163,26 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // rows are ascending) or the end of the column list can be partial.
     int n_tiles = 0, n_full = 0, e0 = 0, ne = 0, sub_shift = 0;
     int j_first = 0;  // block form: the row's first kept block
+    int jwin = 0;     // ring pass: lane i holds the row's i-th kept block (rows of at most 64 blocks)
     const int32_t* cb = nullptr;
     if constexpr (MODE == MODE_DENSE) {
         n_tiles = (L + KT - 1) / KT;
         n_full = L / KT;
     } else if constexpr (MODE == MODE_BLOCK) {
         const int r = bh * p.n_qtiles + qt;
-        e0 = p.row_ptr[r];
-        ne = p.row_ptr[r + 1] - e0;
+        const cint32* rp = (const cint32*)(p.row_ptr);
+        e0 = rp[r];
+        ne = rp[r + 1] - e0;
         // block_k / KT tiles per kept key block (block_k in {64, 128}, KT in {32, 64})
         sub_shift = (p.block_k == 128 ? 1 : 0) + (KT == 32 ? 1 : 0);
+        if constexpr (RING) {
+            if (ne > 0 && ne <= 64) jwin = p.col_idx[e0 + min(lane, ne - 1)];
+        }
         if (ne > 0) {
             // the first and the last kept block, loaded together
-            j_first = p.col_idx[e0];
-            const int rem = L - p.col_idx[e0 + ne - 1] * p.block_k;  // keys of the last block in range
+            const cint32* cx = (const cint32*)(p.col_idx);
+            j_first = cx[e0];
+            const int rem = L - cx[e0 + ne - 1] * p.block_k;  // keys of the last block in range
             const int per = 1 << sub_shift;
             n_tiles = ((ne - 1) << sub_shift) + min(per, (rem + KT - 1) / KT);
             n_full = ((ne - 1) << sub_shift) + min(per, rem / KT);
@@ -149,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
             return max(0, min(KT, L - key0));
     };
     auto block_of = [&](int u) __attribute__((always_inline)) -> int {
-        return p.col_idx[e0 + min(u >> sub_shift, ne - 1)];
+        return ((const cint32*)(p.col_idx))[e0 + min(u >> sub_shift, ne - 1)];
     };
 
     // LDS layouts (16-byte units, XOR-swizzled so that reads hit distinct banks):
@@ -196,19 +256,24 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     auto dma_rows = [&](char* stage, int u, const Src& sr, auto is_v) __attribute__((always_inline)) {
         const bool live = u < n_tiles;
         const int key0 = tile_key0(u, sr.j);
-        const int nv = tile_valid(key0);
+        if constexpr (MODE == MODE_COLUMN) {
+            // gathered rows: each lane's row has its own offset
+            const int nv = tile_valid(key0);
 #pragma unroll
-        for (int i = 0; i < NDMA; ++i) {
-            LDS_AS char* dst = (LDS_AS char*)(stage) + (is_v.value ? TILEB : 0) + (i * T + wave * 64) * 16;
-            uint32_t base;
-            if constexpr (MODE == MODE_COLUMN)
-                base = (live && dr0 + i * ROWS_PER_DMA < nv) ? static_cast<uint32_t>(sr.kn[i]) * ROWB : kOOB;
-            else
-                base = live ? static_cast<uint32_t>(key0) * ROWB : kOOB;
-            if constexpr (is_v.value)
-                dma_load16(rv, lds_addr(dst), base + vslot[i]);
-            else
-                dma_load16(rk, lds_addr(dst), base + kslot[i]);
+            for (int i = 0; i < NDMA; ++i) {
+                LDS_AS char* dst = (LDS_AS char*)(stage) + (is_v.value ? TILEB : 0) + (i * T + wave * 64) * 16;
+                const uint32_t base =
+                    (live && dr0 + i * ROWS_PER_DMA < nv) ? static_cast<uint32_t>(sr.kn[i]) * ROWB : kOOB;
+                dma_load16(is_v.value ? rv : rk, lds_addr(dst), base + (is_v.value ? vslot[i] : kslot[i]));
+            }
+        } else {
+            const uint32_t m0 = lds_wave + static_cast<uint32_t>((stage - smem) + (is_v.value ? TILEB : 0));
+            // a contiguous tile: its start goes into the descriptor, the lanes keep their offsets
+            const uint32_t tb = live ? static_cast<uint32_t>(key0) * ROWB : head_bytes;
+            const u32x4 r = tile_rsrc(is_v.value ? vaddr : kaddr, tb);
+#pragma unroll
+            for (int i = 0; i < NDMA; ++i)
+                dma_load16(r, m0 + i * T * 16, is_v.value ? vslot[i] : kslot[i]);
         }
     };
     Src sn;  // source of the next tile (one-stage-ring passes)
@@ -628,17 +693,175 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         }
         __builtin_amdgcn_s_waitcnt(0);
     };
+    // Unchecked pass over 32-key tiles (64-query blocks), software-pipelined
+    // in units through a ring of NK K slots and NV V slots.  Unit t computes
+    // QK of tile t+1 beside the second half of tile t's softmax, then PV of
+    // tile t beside the first half of tile t+1's.  At unit t's barrier every
+    // wave is done with K(t) and V(t-1), so K(t+NK) is fetched into K(t)'s
+    // slot and V(t+NV-1) into V(t-1)'s: K arrives NK-1 units ahead of its
+    // use, V NV-1.  Tile 0 is scored before the first unit and sets the
+    // reference to its maximum; the last tile gets a half unit (the rest of
+    // its softmax and its PV).  Block indices come from the row's register
+    // window by v_readlane, so the loop issues no memory operation besides
+    // the tile DMAs, and each unit waits for exactly the DMAs it needs.
+    auto run_pass_ring = [&]() __attribute__((always_inline)) {
+        constexpr int U = lcm_c(lcm_c(NK, NV), 2);  // units per unrolled group: every slot offset constant
+        // DMAs that may stay in flight at a unit's start: those issued after
+        // the later of V(t) (issued NV-1 units earlier, before that unit's K)
+        // and K(t+1) (issued NK-1 units earlier)
+        constexpr int WAIT = NK > NV ? NDMA * (1 + 2 * (NV - 2)) : 2 * NDMA * (NK - 2);
+        static_assert(WAIT < 64, "vmcnt range");
+        const int n = n_tiles;
+        constexpr std::integral_constant<int, 0> lo{};
+        constexpr std::integral_constant<int, 1> hi{};
+        auto J = [&](int u) __attribute__((always_inline)) -> int {
+            return __builtin_amdgcn_readlane(jwin, min(u >> sub_shift, ne - 1));
+        };
+        // K (is_v false) or V rows of tile u into the ring slot at byte offset `off`
+        // (tiles past the last read as zeros)
+        auto dma_ring = [&](int u, int off, auto is_v) __attribute__((always_inline)) {
+            const uint32_t tb = u < n ? static_cast<uint32_t>(tile_key0(u, J(u))) * ROWB : head_bytes;
+            const u32x4 r = tile_rsrc(is_v.value ? vaddr : kaddr, tb);
+            const uint32_t m0 = lds_wave + static_cast<uint32_t>(off);
+#pragma unroll
+            for (int i = 0; i < NDMA; ++i) dma_load16(r, m0 + i * T * 16, is_v.value ? vslot[i] : kslot[i]);
+        };
+        auto fence = [&](auto is_pv) __attribute__((always_inline)) {
+            __builtin_amdgcn_sched_group_barrier(SG_DSR, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                if (is_pv.value && i < 6) __builtin_amdgcn_sched_group_barrier(SG_DSR, 2, 0);
+                if (!is_pv.value && i < 4) __builtin_amdgcn_sched_group_barrier(SG_DSR, 1, 0);
+                if (i & 1)
+                    __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+                else
+                    __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        // unit t at phase PH = t mod U: (s, pk, ta) hold tile t's scores, the
+        // first half of its P and that half's sum; (sn, pkn, tn) receive tile
+        // t+1's.  Only the last unit (LASTU) scores the last tile, the one tile
+        // that can be partial.
+        auto unit = [&](int t, auto PH, auto LASTU, f32x16& s, uint32_t (&pk)[8], float& ta, f32x16& sn,
+                        uint32_t (&pkn)[8], float& tn) __attribute__((always_inline)) {
+            constexpr int ph = decltype(PH)::value;
+            wait_vmcnt<WAIT>();
+            __syncthreads();
+            dma_ring(t + NV - 1, (NK + (ph + NV - 1) % NV) * TILEB, std::true_type{});  // V(t+NV-1)
+            dma_ring(t + NK, (ph % NK) * TILEB, std::false_type{});                    // K(t+NK)
+            __builtin_amdgcn_sched_barrier(0);
+            qk(smem + ((ph + 1) % NK) * TILEB, 0, sn);  // S(t+1)
+            const float tb = exps_half(s, hi, mc, pk);  // P(t), second half
+            fence(std::false_type{});
+            if constexpr (decltype(LASTU)::value) {
+                if (n_full < n) mask(0, tile_valid(tile_key0(t + 1, J(t + 1))), sn);
+            }
+            pv(smem + (NK + ph % NV) * TILEB - TILEB, 0, pk);  // O += V(t)^T P(t)^T (voff holds the V offset)
+            tn = exps_half(sn, lo, mc, pkn);                    // P(t+1), first half
+            fence(std::true_type{});
+            l_acc += ta + tb;
+        };
+        auto last = [&](auto PH, f32x16& s, uint32_t (&pk)[8], float& ta) __attribute__((always_inline)) {
+            constexpr int ph = decltype(PH)::value;
+            wait_vmcnt<WAIT>();
+            __syncthreads();
+            const float tb = exps_half(s, hi, mc, pk);
+            pv(smem + (NK + ph % NV) * TILEB - TILEB, 0, pk);
+            l_acc += ta + tb;
+        };
+
+        // tile 0's K, then the pseudo-units -(NK-1) .. -1 with the unit's
+        // order (V(u+NV-1), K(u+NK)); a V tile before the first goes to its
+        // slot as zeros, ahead of the real tile that later fills that slot
+        dma_ring(0, 0, std::false_type{});
+#pragma unroll
+        for (int u = -(NK - 1); u < 0; ++u) {
+            const int vt = u + NV - 1;
+            dma_ring(vt >= 0 ? vt : n, (NK + ((vt % NV) + NV) % NV) * TILEB, std::true_type{});
+            dma_ring(u + NK, ((u + NK) % NK) * TILEB, std::false_type{});
+        }
+        wait_vmcnt<2 * NDMA * (NK - 1)>();  // K(0) is in; the rest may still be in flight
+        __syncthreads();
+        f32x16 sa, sb;
+        uint32_t pka[8], pkb[8];
+        float taa = 0.f, tab = 0.f;
+        qk(smem, 0, sa);
+        if (n_full == 0) mask(0, tile_valid(tile_key0(0, J(0))), sa);
+        {
+            float mt = -kInf;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, sa[r]);
+            m_ref = max_with_half_swap(mt);
+            mc = m_ref * c;
+        }
+        taa = exps_half(sa, lo, mc, pka);
+        // units 0 .. n-2 in groups of U, the state alternating between a and b
+        constexpr std::false_type MID{};
+        constexpr std::true_type LASTU{};
+        auto unit_at = [&](int t0, auto PH, auto is_last) __attribute__((always_inline)) {
+            constexpr int ph = decltype(PH)::value;
+            if constexpr (ph % 2 == 0)
+                unit(t0 + ph, PH, is_last, sa, pka, taa, sb, pkb, tab);
+            else
+                unit(t0 + ph, PH, is_last, sb, pkb, tab, sa, pka, taa);
+        };
+        const int nu = n - 1;
+        int t = 0;
+        // groups of U units that hold neither the last unit nor the last tile
+        for (; t + U < nu; t += U)
+            static_for<U>([&](auto PH) __attribute__((always_inline)) { unit_at(t, PH, MID); });
+        // the remaining r units (1 <= r <= U, or none for a one-tile row): phases
+        // 0 .. r-2, the last unit at phase r-1, then the last tile's half unit
+        auto tail = [&](auto R) __attribute__((always_inline)) {
+            constexpr int rr = decltype(R)::value;
+            if constexpr (rr >= 1) {
+                static_for<rr - 1>([&](auto PH) __attribute__((always_inline)) { unit_at(t, PH, MID); });
+                unit_at(t, std::integral_constant<int, rr - 1>{}, LASTU);
+            }
+            constexpr std::integral_constant<int, rr % U> PL{};
+            if constexpr (rr % 2 == 0)
+                last(PL, sa, pka, taa);
+            else
+                last(PL, sb, pkb, tab);
+        };
+        const int r = nu - t;
+        static_for<U + 1>([&](auto R) __attribute__((always_inline)) {
+            if (r == decltype(R)::value) tail(R);
+        });
+        __builtin_amdgcn_s_waitcnt(0);  // K fetches past the last tile
+    };
     // Unchecked pass: probabilities relative to tile 0's maximum are not
     // bounded, so a lane whose row sum leaves [0, 2^32] (including inf and
     // NaN) sends the whole workgroup through a second, checked pass.
     if constexpr (KB == 2) {
         if (n_tiles > 0) run_pass_piped();
+    } else if constexpr (RING) {
+        if (n_tiles > 0) {
+            if (ne <= 64) {
+                run_pass_ring();
+            } else {
+                run_pass(std::false_type{});
+                // the flags below may sit in a stage another wave still reads
+                if constexpr (FLAGS_IN_RING) __syncthreads();
+            }
+        }
     } else {
         run_pass(std::false_type{});
     }
     // one flag per wave and one barrier; the barrier also ends every wave's
-    // reads of the stages, which the epilogue reuses
-    __shared__ int redo_flag[NW];
+    // reads of the stages, which the epilogue reuses.  With a deep enough K
+    // ring the flags live in it, past the epilogue's staging rows: every read
+    // of the K slots and every DMA has ended before a flag is written, and
+    // the epilogue's staging does not reach them.
+    int* redo_flag;
+    if constexpr (FLAGS_IN_RING) {
+        redo_flag = reinterpret_cast<int*>(smem + FLAGOFF);
+    } else {
+        __shared__ int flags[NW];
+        redo_flag = flags;
+    }
     const bool wave_redo = __any(!(l_acc <= kBigRow));
     if (lane == 0) redo_flag[wave] = wave_redo ? 1 : 0;
     __syncthreads();
@@ -653,6 +876,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         for (int db = 0; db < ND; ++db)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+        if constexpr (FLAGS_IN_RING) __syncthreads();  // every wave has read the flags before the DMAs
         run_pass(std::true_type{});
         __syncthreads();
     }
@@ -696,11 +920,16 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     }
 }
 
-template <int D, int NW, int KT, int NST, int MODE>
+template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST>
 hipError_t launch_one(const FlashParams& fp, hipStream_t st) {
-    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE>), dim3(fp.n_items), dim3(NW * 64), 0, st, fp);
+    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE, NK, NV>), dim3(fp.n_items), dim3(NW * 64), 0, st, fp);
     return hipGetLastError();
 }
+
+// K and V ring slots of the 64-query block form's pipelined pass: K fetched
+// two units ahead, V one; five 8 KiB slots (d = 128) fill the 160 KiB of LDS
+// with four workgroups per CU.
+constexpr int kRingK = 3, kRingV = 2;
 
 // Query tile of a launch: 64- or 128-query blocks for the block-sparse form,
 // 256 queries otherwise.
@@ -710,7 +939,8 @@ inline int query_tile(AttnMode mode, const SparseIndex& ix) { return mode == MOD
 //   256-query tiles (dense, column): 8 waves, 64-key tiles, two stages (64 KiB);
 //   128-query blocks: 4 waves, 64-key tiles, two stages (64 KiB, two
 //   workgroups per CU);
-//   64-query blocks: 2 waves, 32-key tiles, two stages (32 KiB).
+//   64-query blocks: 2 waves, 32-key tiles through a ring of kRingK K and
+//   kRingV V slots (40 KiB at d = 128, four workgroups per CU).
 template <int D>
 hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st) {
     switch (mode) {
@@ -718,7 +948,7 @@ hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st
         case MODE_COLUMN: return launch_one<D, 8, 64, 2, MODE_COLUMN>(fp, st);
         case MODE_COLUMN_PACKED: return launch_one<D, 8, 64, 2, MODE_COLUMN_PACKED>(fp, st);
         case MODE_BLOCK:
-            if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK>(fp, st);
+            if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK, kRingK, kRingV>(fp, st);
             return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st);
     }
     return hipErrorInvalidValue;
