@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SDATTN_ABI_VERSION 3
+#define SDATTN_ABI_VERSION 4
 
 /* Exported entry points (the library is built with hidden visibility). */
 #define SDATTN_API __attribute__((visibility("default")))
@@ -168,6 +168,27 @@ SDATTN_API sdattn_status sdattn_select_blocks(const sdattn_problem* p, const voi
                                    int32_t block_q, int32_t block_k, const sdattn_budget* budget,
                                    int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
                                    float* block_mass, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sdattn_select_blocks without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and errors as
+ * sdattn_select_blocks, without ws/ws_bytes: the workspace is a static
+ * device array of SDATTN_NOALLOC_SCRATCH_BYTES inside the library, one copy
+ * per GPU, held until the process ends (its address is looked up once per
+ * device, at the first call on that device).  The call allocates nothing.
+ * A selection whose workspace (sdattn_select_blocks_workspace) exceeds
+ * SDATTN_NOALLOC_SCRATCH_BYTES fails with SDATTN_ERR_WORKSPACE before
+ * anything is enqueued.  The work runs on the stream's device (the current
+ * device for the NULL stream).  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (unordered streams or threads)
+ * race and must be serialised by the caller.
+ */
+#define SDATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+SDATTN_API sdattn_status sdattn_select_blocks_noalloc(const sdattn_problem* p, const void* q, const void* k,
+                                           int32_t block_q, int32_t block_k, const sdattn_budget* budget,
+                                           int32_t* row_ptr, int32_t* col_idx, int64_t col_capacity,
+                                           float* block_mass, void* stream);
 
 /*
  * Exact block mass, the alternative to pooled scores (SparseD, abstract:

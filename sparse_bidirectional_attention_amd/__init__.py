@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdattn.so")
 
 # ABI of include/sdattn.h that this binding marshals for (SDATTN_ABI_VERSION)
-SDATTN_ABI_VERSION = 3
+SDATTN_ABI_VERSION = 4
 
 # ---- enums ------------------------------------------------------------------
 SDATTN_OK = 0
@@ -27,6 +27,8 @@ STATUS_NAMES = ["SDATTN_OK", "SDATTN_ERR_NULL", "SDATTN_ERR_SHAPE", "SDATTN_ERR_
 SDATTN_F32, SDATTN_BF16 = 0, 1
 SDATTN_BUDGET_TOPK, SDATTN_BUDGET_MASS = 0, 1
 SDATTN_SEL_BLOCKS, SDATTN_SEL_COLUMNS, SDATTN_SEL_BLOCKS_EXACT = 0, 1, 2
+# bytes of the static scratch behind sdattn_select_blocks_noalloc (SDATTN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 SEL_KINDS = {"blocks": SDATTN_SEL_BLOCKS, "columns": SDATTN_SEL_COLUMNS, "blocks_exact": SDATTN_SEL_BLOCKS_EXACT}
 ACTIONS = ("DENSE", "DENSE_SELECT", "SELECT_SPARSE", "SPARSE", "PROBE_SPARSE")
 
@@ -77,6 +79,8 @@ _SIGS = {
     "sdattn_select_blocks": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(Budget), _P, _P, ctypes.c_int64, _P, _P, ctypes.c_size_t,
                                             _P]),
+    "sdattn_select_blocks_noalloc": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.POINTER(Budget), _P, _P, ctypes.c_int64, _P, _P]),
     "sdattn_select_blocks_exact_workspace": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32,
                                                             ctypes.POINTER(Budget), ctypes.POINTER(ctypes.c_size_t),
                                                             ctypes.POINTER(ctypes.c_int64)]),
@@ -228,6 +232,17 @@ def sdattn_select_blocks(p, q, k, block_q, block_k, budget, row_ptr, col_idx, co
     _check(lib().sdattn_select_blocks(ctypes.byref(p), _ptr(q), _ptr(k), block_q, block_k, ctypes.byref(budget),
                                       _ptr(row_ptr), _ptr(col_idx), col_capacity, _ptr(block_mass), _ptr(ws),
                                       ws_bytes, _stream(stream)), "sdattn_select_blocks")
+
+
+def sdattn_select_blocks_noalloc(p, q, k, block_q, block_k, budget, row_ptr, col_idx, col_capacity=None,
+                                 block_mass=None, stream=None):
+    """sdattn_select_blocks with the library's static scratch as workspace
+    (no allocation; NOALLOC_SCRATCH_BYTES at most)."""
+    if col_capacity is None:
+        col_capacity = col_idx.numel()
+    _check(lib().sdattn_select_blocks_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), block_q, block_k,
+                                              ctypes.byref(budget), _ptr(row_ptr), _ptr(col_idx), col_capacity,
+                                              _ptr(block_mass), _stream(stream)), "sdattn_select_blocks_noalloc")
 
 
 def sdattn_select_blocks_exact_workspace(p, block_q, block_k, budget):

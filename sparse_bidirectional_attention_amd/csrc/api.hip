@@ -8,6 +8,7 @@
 
 #include "host_common.h"
 #include "exact.h"
+#include "select_api.h"
 #include "launch.h"
 #include "probe.h"
 #include "schedule.h"
@@ -44,6 +45,47 @@ sdattn_status run_attention(AttnMode mode, const Problem& pr, const void* q, con
 
 }  // namespace
 
+namespace sdattn {
+
+sdattn_status plan_select_blocks(const sdattn_problem* p, const void* q, const void* k, int32_t block_q,
+                                 int32_t block_k, const sdattn_budget* budget, int32_t* row_ptr, int32_t* col_idx,
+                                 int64_t col_capacity, SelectBlocksPlan* out) {
+    SelectBlocksPlan sp;
+    sdattn_status s = check_problem(p, &sp.pr);
+    if (s != SDATTN_OK) return s;
+    s = check_blocks(sp.pr, block_q, block_k, budget, &sp.plan);
+    if (s != SDATTN_OK) return s;
+    sp.block_q = block_q;
+    sp.block_k = block_k;
+    sp.ws_bytes = 0;
+    if (sp.pr.L > 0) {
+        if (q == nullptr || k == nullptr || row_ptr == nullptr || col_idx == nullptr)
+            return fail(SDATTN_ERR_NULL, "q, k, row_ptr and col_idx must be non-NULL");
+        if (col_capacity < sp.plan.max_nnz) {
+            char buf[160];
+            snprintf(buf, sizeof buf, "col_capacity %lld < worst-case kept blocks %lld",
+                     static_cast<long long>(col_capacity), static_cast<long long>(sp.plan.max_nnz));
+            return fail(SDATTN_ERR_CAPACITY, buf);
+        }
+        sp.ws_bytes = select_blocks_ws_layout(shape_of(sp.pr), block_q, block_k, sp.plan.mass).total;
+    }
+    *out = sp;
+    return SDATTN_OK;
+}
+
+sdattn_status launch_planned_select_blocks(const SelectBlocksPlan& sp, const void* q, const void* k,
+                                           const sdattn_budget* budget, int32_t* row_ptr, int32_t* col_idx,
+                                           float* block_mass, void* ws, void* stream, const char* name) {
+    hipError_t e = launch_select_blocks(shape_of(sp.pr), sp.pr.dtype == SDATTN_BF16, q, k, sp.block_q, sp.block_k,
+                                        sp.plan.mass, static_cast<int>(sp.plan.topk),
+                                        static_cast<float>(budget->mass), sp.plan.cap_extra, row_ptr, col_idx,
+                                        block_mass, ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, name);
+    return SDATTN_OK;
+}
+
+}  // namespace sdattn
+
 extern "C" {
 
 sdattn_status sdattn_forward_dense(const sdattn_problem* p, const void* q, const void* k, const void* v,
@@ -74,33 +116,16 @@ sdattn_status sdattn_select_blocks(const sdattn_problem* p, const void* q, const
                                    int32_t block_k, const sdattn_budget* budget, int32_t* row_ptr,
                                    int32_t* col_idx, int64_t col_capacity, float* block_mass, void* ws,
                                    size_t ws_bytes, void* stream) {
-    Problem pr;
-    sdattn_status s = check_problem(p, &pr);
-    if (s != SDATTN_OK) return s;
-    BlockPlan plan;
-    s = check_blocks(pr, block_q, block_k, budget, &plan);
-    if (s != SDATTN_OK) return s;
-    if (pr.L == 0) return SDATTN_OK;
-    if (q == nullptr || k == nullptr || row_ptr == nullptr || col_idx == nullptr)
-        return fail(SDATTN_ERR_NULL, "q, k, row_ptr and col_idx must be non-NULL");
-    if (col_capacity < plan.max_nnz) {
+    SelectBlocksPlan sp;
+    sdattn_status s = plan_select_blocks(p, q, k, block_q, block_k, budget, row_ptr, col_idx, col_capacity, &sp);
+    if (s != SDATTN_OK || sp.pr.L == 0) return s;
+    if (ws_bytes < sp.ws_bytes || (sp.ws_bytes > 0 && ws == nullptr)) {
         char buf[160];
-        snprintf(buf, sizeof buf, "col_capacity %lld < worst-case kept blocks %lld", static_cast<long long>(col_capacity),
-                 static_cast<long long>(plan.max_nnz));
-        return fail(SDATTN_ERR_CAPACITY, buf);
-    }
-    const size_t need = select_blocks_ws_layout(shape_of(pr), block_q, block_k, plan.mass).total;
-    if (ws_bytes < need || (need > 0 && ws == nullptr)) {
-        char buf[160];
-        snprintf(buf, sizeof buf, "workspace of %zu bytes < required %zu", ws_bytes, need);
+        snprintf(buf, sizeof buf, "workspace of %zu bytes < required %zu", ws_bytes, sp.ws_bytes);
         return fail(SDATTN_ERR_WORKSPACE, buf);
     }
-    hipError_t e = launch_select_blocks(shape_of(pr), pr.dtype == SDATTN_BF16, q, k, block_q, block_k, plan.mass,
-                                        static_cast<int>(plan.topk), static_cast<float>(budget->mass),
-                                        plan.cap_extra, row_ptr, col_idx, block_mass, ws,
-                                        static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "sdattn_select_blocks");
-    return SDATTN_OK;
+    return launch_planned_select_blocks(sp, q, k, budget, row_ptr, col_idx, block_mass, ws, stream,
+                                        "sdattn_select_blocks");
 }
 
 namespace {

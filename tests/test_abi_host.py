@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 26
+    assert len(names) == 27
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
     assert set(names) == exported  # nothing missing, nothing extra
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 3
+    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 4
     hdr = open(os.path.join(ROOT, "include", "sdattn.h")).read()
     assert f"#define SDATTN_ABI_VERSION {sd.SDATTN_ABI_VERSION}" in hdr
     for i, name in enumerate(sd.STATUS_NAMES):
