@@ -21,7 +21,10 @@ Inputs are the seeded synthetic tensors of the workload (planted per-head
 structure), resident in HBM before timing starts: the step-0 tensors serve
 the dense steps and the selection step's tensors serve the selection and
 sparse steps (kernel time does not depend on the drift between steps; the
-pattern does, and it is computed from the real selection-step inputs).
+pattern does, and it is computed from the real selection-step inputs).  With
+--probe-interval the probes' decisions do depend on it, so each step after
+the selection gets its own inputs: the workload's random-walk drift continued
+on the device from the selection step's tensors, generated before timing.
 
 The block-wise workload (--workload losa_sdar8b_32k) is timed the same way
 over blocks of iterations on top of a cached prefix: the first iteration of a
@@ -50,6 +53,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 MAX_GFX_CLOCK_MHZ = 2400.0  # the clock the MFMA peak is quoted at
+WALK_BYTES_MAX = 64 << 30   # device memory for per-step inputs of a probed schedule
 
 
 def log(*a):
@@ -625,7 +629,36 @@ def run_schedule(args, w0, K, warmup, with_gpu_state=True):
     o = torch.empty_like(x0["q"])
     lse = torch.empty(x0["q"].shape[:3], dtype=torch.float32, device="cuda")
 
-    def inputs_for(a):
+    # With probes (adaptive anchors), every step after the selection gets its
+    # own inputs: the random walk of the workload's step drift continued on
+    # the device from the selection step's tensors, X_t = X_{t-1} + sigma N_t
+    # for Q and K (V fixed), rounded to the input dtype, all generated before
+    # the timed region.  Otherwise kernel time does not depend on the drift:
+    # the dense steps take the step-0 tensors and the rest the selection
+    # step's.
+    walk = {}
+    walk_note = None
+    if w.probe_interval and w.selector == "blocks" and w.step_noise == "walk":
+        n_walk = K - 1 - w.select_step
+        need = n_walk * (xs["q"].numel() + xs["k"].numel()) * xs["q"].element_size()
+        if need <= WALK_BYTES_MAX:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(1_000_003 * w.wid + 7)
+            qf, kf = xs["q"].float(), xs["k"].float()
+            for t in range(w.select_step + 1, K):
+                qf.add_(torch.randn(qf.shape, generator=gen, device="cuda"), alpha=w.step_sigma)
+                kf.add_(torch.randn(kf.shape, generator=gen, device="cuda"), alpha=w.step_sigma)
+                walk[t] = {"q": qf.to(xs["q"].dtype), "k": kf.to(xs["k"].dtype), "v": xs["v"]}
+            del qf, kf
+            torch.cuda.synchronize()
+            walk_note = (f"steps {w.select_step + 1}..{K - 1}: own inputs, a random walk (sigma {w.step_sigma:g} per "
+                         f"step) on the device from the selection step's tensors ({need / 2**30:.1f} GiB)")
+        else:
+            walk_note = f"the per-step inputs would need {need / 2**30:.0f} GiB; selection-step tensors reused"
+
+    def inputs_for(a, t=-1):
+        if t in walk:
+            return walk[t]
         return x0 if a == "DENSE" else xs
 
     # warm-up: W untimed steps of a schedule of the same shape
@@ -659,7 +692,7 @@ def run_schedule(args, w0, K, warmup, with_gpu_state=True):
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for t in range(K):
-        x = inputs_for(acts[t])
+        x = inputs_for(acts[t], t)
         ev[t][0].record()
         sd.sdattn_schedule_step(h, t, x["q"], x["k"], x["v"], o, lse)
         ev[t][1].record()
@@ -816,7 +849,7 @@ def run_schedule(args, w0, K, warmup, with_gpu_state=True):
         "probes": ({"probe_step_ms": round(probe_ms, 4), "probe_overhead_ms": round(probe_ms - sparse_ms, 4)
                     if sparse_ms else None, "n_probes": n_probes, "n_adopted": n_adopted,
                     "last_overlap": round(last_overlap, 6), "min_overlap": w.min_overlap,
-                    "probe_interval": w.probe_interval} if probe_ms is not None else None),
+                    "probe_interval": w.probe_interval, "inputs": walk_note} if probe_ms is not None else None),
         "dense_baseline": {"ms_per_step": round(dense_base_ms, 3), "tflops": round(dense_base_tflops, 1),
                            "mfma_frac": round(dense_base_tflops / peak, 4),
                            "schedule_speedup": round(dense_base_ms / ms_per_step, 3),
@@ -832,7 +865,7 @@ def run_schedule(args, w0, K, warmup, with_gpu_state=True):
     }
     if not args.no_sdpa_baseline and w.dtype == "bf16":
         out["sdpa_dense_baseline"] = sdpa_dense_baseline(x0, w, dense_launch_ms)
-    del x0, xs, o, lse
+    del x0, xs, o, lse, walk
     torch.cuda.empty_cache()
     return out, (acts, x0h, xsh)
 

@@ -72,3 +72,51 @@ def test_planting_follows_the_kv_groups():
     for t in range(w.total_steps):
         x = make_step(w, t, base)
         assert x["q"].shape == (1, 4, 1000, 128) and x["k"].shape == (1, 2, 1000, 128)
+
+
+def _cov(T, s, t):
+    from workloads.generate import walk_nodes
+    cs, ct = dict(walk_nodes(T, s)), dict(walk_nodes(T, t))
+    return sum(c * ct.get(k, 0.0) for k, c in cs.items())
+
+
+def test_walk_has_the_covariance_of_a_unit_step_random_walk():
+    """Cov(W_s, W_t) = min(s, t) for every pair of steps, exactly (the node
+    draws are independent standard normals): W_0 = 0 and the increments are
+    independent with unit variance.  Checked over whole schedules, including
+    lengths that are not powers of two."""
+    for T in (1, 4, 7, 32, 192):
+        for s in range(T + 1):
+            for t in range(s, T + 1):
+                assert abs(_cov(T, s, t) - s) < 1e-9, (T, s, t)
+    for s, t in ((204, 205), (205, 1023), (0, 1023), (511, 512), (1023, 1024)):
+        assert abs(_cov(1024, s, t) - min(s, t)) < 1e-9
+
+
+def test_walk_steps_drift_by_sigma_per_step():
+    """Generated tensors: consecutive steps differ by sigma N(0, 1) per element,
+    successive increments are uncorrelated, and V stays fixed."""
+    w = scaled(WORKLOADS["llada8b_8k"], seq_len=2048, q_heads=4, kv_heads=4, dtype="f32", total_steps=64)
+    base = make_base(w)
+    xs = [make_step(w, t, base) for t in (30, 31, 32, 33)]
+    for n in "qk":
+        d1 = (xs[1][n] - xs[0][n]).astype(np.float64).ravel()
+        d2 = (xs[2][n] - xs[1][n]).astype(np.float64).ravel()
+        d3 = (xs[3][n] - xs[2][n]).astype(np.float64).ravel()
+        for d in (d1, d2, d3):
+            assert abs(d.std() / w.step_sigma - 1.0) < 0.01 and abs(d.mean()) < 0.01 * w.step_sigma
+        for a, b in ((d1, d2), (d2, d3)):
+            assert abs(np.corrcoef(a, b)[0, 1]) < 0.01
+        drift = (xs[3][n] - base[n]).astype(np.float64).ravel()
+        assert abs(drift.std() / (w.step_sigma * np.sqrt(33)) - 1.0) < 0.01
+    np.testing.assert_array_equal(xs[0]["v"], xs[3]["v"])
+
+
+def test_walk_does_not_depend_on_the_thread_pool(monkeypatch):
+    w = scaled(WORKLOADS["sparsed_64k"], seq_len=4096, q_heads=2, kv_heads=2, total_steps=1024)
+    base = make_base(w)
+    a = make_step(w, 205, base)
+    monkeypatch.setattr("os.cpu_count", lambda: 1)
+    b = make_step(w, 205, base)
+    for n in "qkv":
+        assert _h(a[n]) == _h(b[n])

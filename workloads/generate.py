@@ -18,9 +18,21 @@ Recipe (all draws from numpy PCG64 seeded by SeedSequence):
   * columns       : per kv head g, n random single tokens get K += 3u_g and
                     every Q of the group's query heads += 3u_g.
   * steps         : "fresh_qv": Q_t = Q_0 + s N_t, V_t = V_0 + s N_t, K fixed.
-                    "walk": Q_t = Q_0 + s sqrt(t) N_t, K_t likewise, V fixed
-                    (the marginal of a random walk with step s, so any step
-                    can be produced without replaying the earlier ones).
+                    "walk": Q_t = Q_0 + s W_t, K_t likewise (independent
+                    walks), V fixed, where W is a Gaussian random walk:
+                    W_0 = 0 and the increments W_t - W_{t-1} are independent
+                    N(0, 1) per element.  W is built by the dyadic (Levy)
+                    Brownian-bridge construction on [0, T2], T2 the smallest
+                    power of two >= the step count: W_T2 = sqrt(T2) Z_root,
+                    and the midpoint c of a dyadic interval [a, b] takes
+                    W_c = (W_a + W_b) / 2 + sqrt((b - a) / 4) Z_(a, b).  So
+                    any step is a fixed combination of at most log2(T2) + 1
+                    seeded standard-normal tensors, computable without
+                    replaying the earlier steps, and consecutive steps differ
+                    by s N(0, 1) per element.  Each node tensor is drawn in
+                    chunks of 2^22 elements, chunk c of node (a, b) of tensor
+                    n from SeedSequence([wid, 1000 + n, a, b, c]) (the root
+                    is node (T2, T2)).
   * bf16          : the fp32 step tensor rounded to nearest-even.
   * block-wise (LoSA workloads): prefix K/V caches N(0, 1) and a block's Q/K/V
     N(0, 1) from SeedSequence([wid, 0, tensor]); kv head types by g mod 4:
@@ -160,6 +172,58 @@ def _noise(w: Workload, step: int, tensor: int, shape, scale: float, out):
     return n
 
 
+_WALK_CHUNK = 1 << 22
+
+
+def walk_nodes(total_steps: int, t: int):
+    """W_t of the dyadic bridge construction as a combination of node
+    tensors: a list of ((a, b), coefficient), where node (T2, T2) is the root
+    (W_T2 = sqrt(T2) Z_root) and node (a, b), a < b, the midpoint draw of
+    [a, b]."""
+    T2 = 1
+    while T2 < max(1, total_steps):
+        T2 *= 2
+    if not 0 <= t <= T2:
+        raise ValueError(f"step {t} outside [0, {T2}]")
+    wa, wb = {}, {(T2, T2): float(np.sqrt(T2))}  # W_a, W_b as {node: coefficient}
+    a, b = 0, T2
+    while t not in (a, b):
+        c = (a + b) // 2
+        wc = {k: 0.5 * v for k, v in wa.items()}
+        for k, v in wb.items():
+            wc[k] = wc.get(k, 0.0) + 0.5 * v
+        wc[(a, b)] = wc.get((a, b), 0.0) + float(np.sqrt((b - a) / 4.0))
+        if t < c:
+            b, wb = c, wc
+        else:
+            a, wa = c, wc
+    return sorted((wa if t == a else wb).items())
+
+
+def _walk(w: Workload, step: int, tensor: int, x0, sigma: float):
+    """x0 + sigma W_step (float32), the node draws generated and
+    accumulated chunk by chunk on a thread pool (numpy releases the
+    interpreter lock while filling); the result does not depend on the pool."""
+    from concurrent.futures import ThreadPoolExecutor
+    import os
+    nodes = walk_nodes(w.total_steps, step)
+    out = np.array(x0, dtype=np.float32, copy=True)
+    flat = out.reshape(-1)
+    n_chunks = -(-flat.size // _WALK_CHUNK)
+
+    def fill(c):
+        seg = flat[c * _WALK_CHUNK:(c + 1) * _WALK_CHUNK]
+        z = np.empty(seg.size, dtype=np.float32)
+        for (a, b), coef in nodes:
+            _rng(w.wid, 1000 + tensor, a, b, c).standard_normal(out=z, dtype=np.float32)
+            z *= np.float32(sigma * coef)
+            seg += z
+
+    with ThreadPoolExecutor(max(1, min(16, os.cpu_count() or 1, n_chunks))) as ex:
+        list(ex.map(fill, range(n_chunks)))
+    return out
+
+
 def make_step(w: Workload, step: int, base=None, as_float: bool = False):
     """Inputs of denoising step `step`: dict q, k, v as stored (f32 or bf16 bits).
 
@@ -173,9 +237,8 @@ def make_step(w: Workload, step: int, base=None, as_float: bool = False):
             q = _noise(w, step, _T_Q, q.shape, w.step_sigma, q)
             v = _noise(w, step, _T_V, v.shape, w.step_sigma, v)
         elif w.step_noise == "walk":
-            s = w.step_sigma * float(np.sqrt(step))
-            q = _noise(w, step, _T_Q, q.shape, s, q)
-            k = _noise(w, step, _T_K, k.shape, s, k)
+            q = _walk(w, step, _T_Q, q, w.step_sigma)
+            k = _walk(w, step, _T_K, k, w.step_sigma)
         else:
             raise ValueError(w.step_noise)
     out = {"q": q, "k": k, "v": v}
