@@ -892,6 +892,65 @@ def compact(rec):
             "sdpa_dense_ms": (rec.get("sdpa_dense_baseline") or {}).get("ms_per_step")}
 
 
+def operand_study(args, w0):
+    """The dense forward, one instruction stream, on three operand sets: the
+    workload's inputs, all zeros and all ones (K and V; Q as given), each for
+    a few seconds while amd-smi samples the socket power and graphics clock.
+    The chip runs at its package power limit under sustained MFMA load, so
+    what an MFMA costs depends on its operands' switching activity: the same
+    kernel that is power-limited on real data runs faster on constant data.
+    Reports each set's launch time, TFLOP/s, fraction of the 2.5 PF peak,
+    the median clock and power, and the fraction of the peak scaled to that
+    clock."""
+    import numpy as np
+    import torch
+
+    import sparse_bidirectional_attention_amd as sd
+    from workloads import make_base, make_step
+
+    w = w0
+    p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
+    base = make_base(w)
+    xh = make_step(w, 0, base)
+    del base
+    x = {n: to_dev(a) for n, a in xh.items()}
+    del xh
+    o = torch.empty_like(x["q"])
+    lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device="cuda")
+    flops = 4.0 * w.batch * w.q_heads * w.seq_len ** 2 * w.head_dim
+    sets = {"workload": (x["q"], x["k"], x["v"]),
+            "zeros": (x["q"], torch.zeros_like(x["k"]), torch.zeros_like(x["v"])),
+            "ones": (x["q"], torch.ones_like(x["k"]), torch.ones_like(x["v"]))}
+    out = {"kind": "dense forward on three operand sets, same kernel", "workload": w.name, "sets": {}}
+    for name, (q, k, v) in sets.items():
+        sd.sdattn_forward_dense(p, q, k, v, o, lse)
+        torch.cuda.synchronize()
+        n = max(8, int(math.ceil(args.operand_seconds * 1e3 / 55.0 * (65536 / w.seq_len) ** 2)))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        mon = GpuMonitor()
+        if not args.no_gpu_monitor:
+            mon.start()
+        for e0, e1 in evs:
+            e0.record()
+            sd.sdattn_forward_dense(p, q, k, v, o, lse)
+            e1.record()
+        torch.cuda.synchronize()
+        mon.stop()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        med = float(np.median(ms))
+        tf = flops / (med * 1e9)
+        rec = {"launches": n, "median_ms": round(med, 3), "tflops": round(tf, 1),
+               "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gpu_state": mon.summary()}
+        gs = rec["gpu_state"]
+        if "gfx_clock_mhz" in gs:
+            sp = PEAK_BF16_TFLOPS * gs["gfx_clock_mhz"]["median"] / MAX_GFX_CLOCK_MHZ
+            rec["peak_at_median_clock_tflops"] = round(sp, 1)
+            rec["frac_of_peak_at_median_clock"] = round(tf / sp, 4) if tf <= sp else None
+        out["sets"][name] = rec
+        log(f"operand set {name}: {med:.3f} ms, {tf:.1f} TFLOP/s")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -913,6 +972,11 @@ def main():
                     help="adaptive anchors (block workloads): probe the pattern every N steps after the selection")
     ap.add_argument("--min-overlap", type=float, default=0.9,
                     help="with --probe-interval: adopt a probe whose overlap with the cached pattern is below this")
+    ap.add_argument("--operand-study", action="store_true",
+                    help="instead of the schedule: the dense forward on the workload's inputs, all-zero and all-one "
+                         "K/V, each for --operand-seconds, with clock and power (how far operand data moves a "
+                         "power-limited kernel)")
+    ap.add_argument("--operand-seconds", type=float, default=4.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
                          "kernel that scales the profiler's HBM byte counters)")
@@ -942,6 +1006,9 @@ def main():
         w0 = scaled(w0, probe_interval=args.probe_interval, min_overlap=args.min_overlap)
     K = args.steps if args.steps is not None else w0.total_steps
     torch.cuda.set_device(0)
+    if args.operand_study:
+        operand_study(args, w0)
+        return
     out, (acts, x0h, xsh) = run_schedule(args, w0, K, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")

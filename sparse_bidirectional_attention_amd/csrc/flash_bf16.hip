@@ -904,15 +904,20 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const size_t obase = (static_cast<size_t>(b) * p.Hq + h) * L;
     constexpr int CHUNKS = 32 * D * 2 / 16;
+    // the wave's 32 output rows through one buffer descriptor: chunk cid sits
+    // at byte 16 cid of them, and rows past the sequence's end fall outside
+    // the descriptor's range, so the hardware drops those stores
+    const int qw0 = q0 + wave_u * 32;
+    const uint64_t obytes = uniform64(reinterpret_cast<uint64_t>(p.o + (obase + qw0) * D));
+    const int orange = __builtin_amdgcn_readfirstlane(max(0, min(32, L - qw0)) * ROWB);
+    const __amdgpu_buffer_rsrc_t rso = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(obytes), static_cast<short>(0), orange, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < CHUNKS / 64; ++i) {
         const int cid = lane + 64 * i;
         const int row = cid / UNITS, u = cid % UNITS;
-        const int qi = q0 + wave * 32 + row;
-        if (qi < L) {
-            const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + ((u ^ (row & (UNITS - 1))) << 4));
-            *reinterpret_cast<u32x4*>(p.o + (obase + qi) * D + u * 8) = val;
-        }
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OPITCH + ((u ^ (row & (UNITS - 1))) << 4));
+        __builtin_amdgcn_raw_buffer_store_b128(val, rso, cid * 16, 0, 0);
     }
     if (p.lse != nullptr && hl == 0) {
         const int qi = q0 + wave * 32 + l32;
@@ -976,7 +981,14 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.n_items = s.B * s.Hq * fp.n_qtiles;
     fp.block_k = ix.block_k;
     fp.kcol = ix.kcol;
-    fp.xcd_group = (fp.n_qtiles % 8 == 0) ? fp.n_qtiles : 0;
+    // XCD-aware order: the block form gives each XCD whole heads (eight heads
+    // per group of 8 * n_qtiles ids), so the rows in flight on an XCD share one
+    // head's K/V in its L2; the other forms give each XCD a contiguous run of
+    // every head's query tiles
+    if (mode == MODE_BLOCK && static_cast<long long>(fp.n_items) % (8LL * fp.n_qtiles) == 0)
+        fp.xcd_group = 8 * fp.n_qtiles;
+    else
+        fp.xcd_group = (fp.n_qtiles % 8 == 0) ? fp.n_qtiles : 0;
     fp.scale = s.scale;
     fp.c = s.scale * kLog2e;
     if (fp.n_items == 0) return hipSuccess;
