@@ -893,15 +893,16 @@ def compact(rec):
 
 
 def operand_study(args, w0):
-    """The dense forward, one instruction stream, on three operand sets: the
-    workload's inputs, all zeros and all ones (K and V; Q as given), each for
-    a few seconds while amd-smi samples the socket power and graphics clock.
-    The chip runs at its package power limit under sustained MFMA load, so
-    what an MFMA costs depends on its operands' switching activity: the same
-    kernel that is power-limited on real data runs faster on constant data.
-    Reports each set's launch time, TFLOP/s, fraction of the 2.5 PF peak,
-    the median clock and power, and the fraction of the peak scaled to that
-    clock."""
+    """The dense forward and the block-sparse forward (on the pattern the
+    pooled selection makes from the workload's inputs), each one instruction
+    stream, on three operand sets: the workload's inputs, all zeros and all
+    ones (K and V; Q as given), each for a few seconds while amd-smi samples
+    the socket power and graphics clock.  The chip runs at its package power
+    limit under sustained MFMA load, so what an MFMA costs depends on its
+    operands' switching activity: the same kernel that is power-limited on
+    real data runs faster on constant data.  Reports each set's launch time,
+    TFLOP/s, fraction of the 2.5 PF peak, the median clock and power, and the
+    fraction of the peak scaled to that clock."""
     import numpy as np
     import torch
 
@@ -917,37 +918,65 @@ def operand_study(args, w0):
     del xh
     o = torch.empty_like(x["q"])
     lse = torch.empty(x["q"].shape[:3], dtype=torch.float32, device="cuda")
-    flops = 4.0 * w.batch * w.q_heads * w.seq_len ** 2 * w.head_dim
+    dense_flops = 4.0 * w.batch * w.q_heads * w.seq_len ** 2 * w.head_dim
     sets = {"workload": (x["q"], x["k"], x["v"]),
             "zeros": (x["q"], torch.zeros_like(x["k"]), torch.zeros_like(x["v"])),
             "ones": (x["q"], torch.ones_like(x["k"]), torch.ones_like(x["v"]))}
-    out = {"kind": "dense forward on three operand sets, same kernel", "workload": w.name, "sets": {}}
-    for name, (q, k, v) in sets.items():
-        sd.sdattn_forward_dense(p, q, k, v, o, lse)
-        torch.cuda.synchronize()
-        n = max(8, int(math.ceil(args.operand_seconds * 1e3 / 55.0 * (65536 / w.seq_len) ** 2)))
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        mon = GpuMonitor()
-        if not args.no_gpu_monitor:
-            mon.start()
-        for e0, e1 in evs:
-            e0.record()
-            sd.sdattn_forward_dense(p, q, k, v, o, lse)
-            e1.record()
-        torch.cuda.synchronize()
-        mon.stop()
-        ms = np.array([a.elapsed_time(b) for a, b in evs])
-        med = float(np.median(ms))
-        tf = flops / (med * 1e9)
-        rec = {"launches": n, "median_ms": round(med, 3), "tflops": round(tf, 1),
-               "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gpu_state": mon.summary()}
-        gs = rec["gpu_state"]
-        if "gfx_clock_mhz" in gs:
-            sp = PEAK_BF16_TFLOPS * gs["gfx_clock_mhz"]["median"] / MAX_GFX_CLOCK_MHZ
-            rec["peak_at_median_clock_tflops"] = round(sp, 1)
-            rec["frac_of_peak_at_median_clock"] = round(tf / sp, 4) if tf <= sp else None
-        out["sets"][name] = rec
-        log(f"operand set {name}: {med:.3f} ms, {tf:.1f} TFLOP/s")
+    if w.selector == "columns":
+        raise SystemExit("--operand-study takes a block workload (its pooled block pattern)")
+    # the pooled selection's pattern of the workload's own inputs, kept fixed
+    # across the operand sets
+    nqb = -(-w.seq_len // w.block)
+    rows = w.batch * w.q_heads * nqb
+    budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
+    wsb, cap = sd.sdattn_select_blocks_workspace(p, w.block, w.block, budget)
+    rp = torch.empty(rows + 1, dtype=torch.int32, device="cuda")
+    ci = torch.empty(max(cap, 1), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    sd.sdattn_select_blocks(p, x["q"], x["k"], w.block, w.block, budget, rp, ci, cap, None, ws, wsb)
+    torch.cuda.synchronize()
+    del ws
+    kept_flops = 4.0 * w.head_dim * w.block * w.block * int(rp[rows].item())
+    forwards = {
+        "dense": (dense_flops, lambda q, k, v: sd.sdattn_forward_dense(p, q, k, v, o, lse)),
+        "block_sparse": (kept_flops, lambda q, k, v: sd.sdattn_forward_block_sparse(p, q, k, v, w.block, w.block,
+                                                                                    rp, ci, o, lse)),
+    }
+    out = {"kind": "dense and block-sparse forwards on three operand sets, same kernels, same pattern",
+           "workload": w.name, "forwards": {}}
+    for fname, (flops, fwd) in forwards.items():
+        recs = {}
+        for name, (q, k, v) in sets.items():
+            fwd(q, k, v)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fwd(q, k, v)
+            torch.cuda.synchronize()
+            one_ms = max(1e-3, (time.perf_counter() - t0) * 1e3)
+            n = max(8, int(math.ceil(args.operand_seconds * 1e3 / one_ms)))
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            mon = GpuMonitor()
+            if not args.no_gpu_monitor:
+                mon.start()
+            for e0, e1 in evs:
+                e0.record()
+                fwd(q, k, v)
+                e1.record()
+            torch.cuda.synchronize()
+            mon.stop()
+            ms = np.array([a.elapsed_time(b) for a, b in evs])
+            med = float(np.median(ms))
+            tf = flops / (med * 1e9)
+            rec = {"launches": n, "median_ms": round(med, 3), "tflops": round(tf, 1),
+                   "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gpu_state": mon.summary()}
+            gs = rec["gpu_state"]
+            if "gfx_clock_mhz" in gs:
+                sp = PEAK_BF16_TFLOPS * gs["gfx_clock_mhz"]["median"] / MAX_GFX_CLOCK_MHZ
+                rec["peak_at_median_clock_tflops"] = round(sp, 1)
+                rec["frac_of_peak_at_median_clock"] = round(tf / sp, 4) if tf <= sp else None
+            recs[name] = rec
+            log(f"{fname} operand set {name}: {med:.3f} ms, {tf:.1f} TFLOP/s")
+        out["forwards"][fname] = {"flops_per_launch": flops, "sets": recs}
     print(json.dumps(out), flush=True)
 
 

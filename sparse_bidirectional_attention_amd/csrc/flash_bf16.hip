@@ -49,6 +49,7 @@ struct FlashParams {
     const int32_t* row_ptr;
     const int32_t* col_idx;
     int Hq, Hkv, L, group, n_qtiles, n_items, block_k, kcol, xcd_group;
+    int n_pairs;  // block form, balanced order: (batch, head) pairs (0: the xcd_group order)
     float c;      // scale * log2(e)
     float scale;  // softmax scale
 };
@@ -84,6 +85,63 @@ __device__ __forceinline__ void static_for(F&& f) {
 // loads become scalar loads (an SGPR result, counted apart from the tile
 // DMAs' vector-memory counter).
 typedef const __attribute__((address_space(4))) int32_t cint32;
+
+// Balanced grid order of the block form.  Rows of one (batch, head) pair keep
+// the same number of kept blocks to within a few, but pairs differ (heads
+// concentrate their mass to different extents), and the grid's ids reach the
+// eight XCDs round robin (id mod 8).  Ids come in rounds of 8 * n_qtiles: in
+// round j, XCD x runs the n_qtiles query blocks of one pair, so each XCD works
+// through whole heads and keeps their K/V in its L2.  The pairs are ranked by
+// their kept-block totals (the row_ptr difference over their rows) and dealt
+// to the XCDs in snake order, largest first: ranks 0..7 to XCDs 0..7 in round
+// 0, ranks 8..15 to XCDs 7..0 in round 1, and so on, which evens the XCDs'
+// totals and leaves the shortest rows for the last round.  Equal totals are
+// ranked so that pair 8j + x still lands on XCD x in round j: with every
+// total equal (a top-k budget) the order is the plain one.  n_pairs <= 64
+// and a multiple of 8 (one key per lane); returns the same value in every
+// lane of the wave.
+__device__ __forceinline__ int snake_rank(int pair) {
+    const int j = pair >> 3, x = pair & 7;
+    return 8 * j + ((j & 1) ? 7 - x : x);
+}
+__device__ __forceinline__ int balanced_block_item(int id, int n_qtiles, int n_pairs,
+                                                   const int32_t* __restrict__ row_ptr, int lane) {
+    const int per_round = 8 * n_qtiles;
+    const int round = id / per_round;
+    const int w = id - round * per_round;
+    const int qt = w >> 3;
+    const int rank = snake_rank(8 * round + (w & 7));  // this id's rank in the snake
+    // key: total << 6 | (63 - snake_rank(pair)): unique, larger total first
+    constexpr int kTotalBits = 20;
+    const bool valid = lane < n_pairs;
+    uint32_t total = 0;
+    if (valid) {
+        const int lo = row_ptr[lane * n_qtiles];
+        const int hi = row_ptr[(lane + 1) * n_qtiles];
+        total = static_cast<uint32_t>(min(max(hi - lo, 0), (1 << kTotalBits) - 1));
+    }
+    uint64_t cand = __ballot(valid);
+    // every total equal: the plain order
+    const uint32_t t0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(total)));
+    if ((__ballot(total == t0) & cand) == cand) return (8 * round + (w & 7)) * n_qtiles + qt;
+    const uint32_t key = valid ? (total << 6) | static_cast<uint32_t>(63 - snake_rank(lane)) : 0u;
+    // the key of rank `rank` (0 = largest), bit by bit from the top over the
+    // candidates that share the bits found so far (ballots, no shuffles)
+    int k = rank;
+#pragma unroll
+    for (int b = kTotalBits + 5; b >= 0; --b) {
+        const uint64_t ones = __ballot((key >> b) & 1u) & cand;
+        const int c = __popcll(ones);
+        if (k < c) {
+            cand = ones;
+        } else {
+            k -= c;
+            cand &= ~ones;
+        }
+    }
+    const int pair = __ffsll(static_cast<unsigned long long>(cand)) - 1;  // the one lane left
+    return pair * n_qtiles + qt;
+}
 
 template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
@@ -124,7 +182,11 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int l32 = lane & 31;
     const int hl = lane >> 5;
 
-    const int item = xcd_remap(blockIdx.x, p.n_items, p.xcd_group);
+    int item;
+    if (MODE == MODE_BLOCK && p.n_pairs > 0)
+        item = balanced_block_item(blockIdx.x, p.n_qtiles, p.n_pairs, p.row_ptr, lane);
+    else
+        item = xcd_remap(blockIdx.x, p.n_items, p.xcd_group);
     const int qt = item % p.n_qtiles;
     const int bh = item / p.n_qtiles;
     const int h = bh % p.Hq;
@@ -989,6 +1051,10 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
         fp.xcd_group = 8 * fp.n_qtiles;
     else
         fp.xcd_group = (fp.n_qtiles % 8 == 0) ? fp.n_qtiles : 0;
+    // up to 64 (batch, head) pairs in whole rounds of eight: ranked by their
+    // kept blocks and dealt to the XCDs evenly (balanced_block_item)
+    const int n_pairs = s.B * s.Hq;
+    fp.n_pairs = (mode == MODE_BLOCK && n_pairs % 8 == 0 && n_pairs <= 64) ? n_pairs : 0;
     fp.scale = s.scale;
     fp.c = s.scale * kLog2e;
     if (fp.n_items == 0) return hipSuccess;

@@ -102,6 +102,50 @@ def test_block_sparse_matches_oracle(dtype, L, bq, bk, d):
     check_out(to_np(o), ro, to_np(lse), rl, dtype, "block_sparse")
 
 
+def _per_head_csr(rng, n_pairs, nqb, nkb, counts):
+    """CSR whose rows in (batch, head) pair i keep counts[i] blocks each
+    (clamped to nkb), a random ascending choice per row."""
+    kept, rp = [], [0]
+    for i in range(n_pairs):
+        for _ in range(nqb):
+            n = min(nkb, counts[i])
+            kept.append(np.sort(rng.choice(nkb, size=n, replace=False)))
+            rp.append(rp[-1] + n)
+    ci = np.concatenate(kept).astype(np.int32) if rp[-1] else np.zeros(0, np.int32)
+    return np.array(rp, np.int32), ci
+
+
+@pytest.mark.parametrize("counts_kind", ["uneven", "equal", "one_long"])
+@pytest.mark.parametrize("B,Hq,Hkv,L,bq", [(1, 8, 2, 777, 64), (2, 8, 8, 520, 128), (1, 64, 8, 300, 64)])
+def test_block_sparse_head_totals_order(counts_kind, B, Hq, Hkv, L, bq):
+    """Batch x heads a multiple of eight (up to 64): the block form ranks the
+    (batch, head) pairs by their kept-block totals and deals them to the
+    XCDs.  Every row is still computed once, by its own workgroup: the output
+    equals the oracle element by element whether the totals differ, are all
+    equal, or one pair dominates."""
+    say(f"block_sparse order {counts_kind} B={B} Hq={Hq} Hkv={Hkv} L={L} bq={bq}")
+    d = 128
+    rng = np.random.default_rng(B * 1000 + Hq + L + bq)
+    x = _inputs(L + Hq, B, Hq, Hkv, L, d, "bf16")
+    nqb = nkb = -(-L // bq)
+    n_pairs = B * Hq
+    if counts_kind == "uneven":
+        counts = [int(c) for c in rng.integers(0, nkb + 1, size=n_pairs)]
+    elif counts_kind == "equal":
+        counts = [max(1, nkb // 3)] * n_pairs
+    else:
+        counts = [1] * n_pairs
+        counts[n_pairs // 2 + 1] = nkb
+    rp, ci = _per_head_csr(rng, n_pairs, nqb, nkb, counts)
+    drp, dci = dev_csr(rp, ci)
+    o, lse = _out(x["q"], "bf16")
+    p = sd.problem_of(x["q"], x["k"])
+    sd.sdattn_forward_block_sparse(p, x["q"], x["k"], x["v"], bq, bq, drp, dci, o, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.block_sparse_attention(*(host_inputs(x[n]) for n in "qkv"), rp, ci, bq, bq)
+    check_out(to_np(o), ro, to_np(lse), rl, "bf16", f"block_sparse order {counts_kind}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Hq,Hkv,L,kcol,d", [(6, 2, 600, 100, 128), (4, 4, 300, 64, 64), (7, 1, 256, 1, 128),
                                              (2, 2, 130, 130, 128)])
