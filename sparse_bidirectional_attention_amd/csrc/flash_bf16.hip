@@ -48,8 +48,12 @@ struct FlashParams {
     float* lse;
     const int32_t* row_ptr;
     const int32_t* col_idx;
-    int Hq, Hkv, L, group, n_qtiles, n_items, block_k, kcol, xcd_group;
-    int n_pairs;  // block form, balanced order: (batch, head) pairs (0: the xcd_group order)
+    int Hq, Hkv, L, group, n_qtiles, n_items, block_k;
+    union {
+        int kcol;     // column forms: kept columns per kv head
+        int n_pairs;  // block form: (batch, head) pairs of the balanced order (0: the xcd_group order)
+    };
+    int xcd_group;
     float c;      // scale * log2(e)
     float scale;  // softmax scale
 };
@@ -1042,7 +1046,6 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.n_qtiles = (s.L + bq - 1) / bq;
     fp.n_items = s.B * s.Hq * fp.n_qtiles;
     fp.block_k = ix.block_k;
-    fp.kcol = ix.kcol;
     // XCD-aware order: the block form gives each XCD whole heads (eight heads
     // per group of 8 * n_qtiles ids), so the rows in flight on an XCD share one
     // head's K/V in its L2; the other forms give each XCD a contiguous run of
@@ -1051,10 +1054,17 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
         fp.xcd_group = 8 * fp.n_qtiles;
     else
         fp.xcd_group = (fp.n_qtiles % 8 == 0) ? fp.n_qtiles : 0;
-    // up to 64 (batch, head) pairs in whole rounds of eight: ranked by their
-    // kept blocks and dealt to the XCDs evenly (balanced_block_item)
-    const int n_pairs = s.B * s.Hq;
-    fp.n_pairs = (mode == MODE_BLOCK && n_pairs % 8 == 0 && n_pairs <= 64) ? n_pairs : 0;
+    // block form: up to 64 (batch, head) pairs in whole rounds of eight are
+    // ranked by their kept blocks and dealt to the XCDs evenly
+    // (balanced_block_item).  The pair count shares kcol's slot: with one
+    // more field in the parameters the dense launch's L2-to-fabric reads
+    // tripled (same instructions, same time)
+    if (mode == MODE_BLOCK) {
+        const int n_pairs = s.B * s.Hq;
+        fp.n_pairs = (n_pairs % 8 == 0 && n_pairs <= 64) ? n_pairs : 0;
+    } else {
+        fp.kcol = ix.kcol;
+    }
     fp.scale = s.scale;
     fp.c = s.scale * kLog2e;
     if (fp.n_items == 0) return hipSuccess;
