@@ -980,6 +980,77 @@ def operand_study(args, w0):
     print(json.dumps(out), flush=True)
 
 
+def mfma_ceiling(args):
+    """The MFMA-only ceiling: a probe kernel (libsdattn_probe.so) that keeps
+    its operands in registers and issues nothing but bf16 32x32x16 MFMAs,
+    run for a few seconds per operand set (random N(0, 1) values, all zeros,
+    all ones) while amd-smi samples power and clock.  Under the package power
+    limit the MFMA rate with random operands is what the attention kernels'
+    own MFMA work can reach at best; the zeros show the clock-limited peak."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    path = os.path.join(ROOT, "sparse_bidirectional_attention_amd", "libsdattn_probe.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built; run `python -m sparse_bidirectional_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    fn = lib.sdattn_probe_mfma_ceiling
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    grid = 768            # three waves per SIMD on 256 CUs
+    n_vals = grid * 4 * 8 * 2 * 64 * 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12345)
+    sets = {"random": torch.randn(n_vals, generator=gen, device="cuda").to(torch.bfloat16),
+            "zeros": torch.zeros(n_vals, dtype=torch.bfloat16, device="cuda"),
+            "ones": torch.ones(n_vals, dtype=torch.bfloat16, device="cuda")}
+    sink = torch.empty(grid * 4 * 64, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    iters = 4096
+    flops = float(grid) * 4 * iters * 8 * 32 * 32 * 16 * 2
+
+    def launch(ops):
+        rc = fn(ops.data_ptr(), grid, iters, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    out = {"kind": "MFMA-only probe: v_mfma_f32_32x32x16_bf16 back to back from registers",
+           "grid": grid, "iters": iters, "flops_per_launch": flops, "sets": {}}
+    for name, ops in sets.items():
+        launch(ops)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        launch(ops)
+        torch.cuda.synchronize()
+        one_ms = max(1e-3, (time.perf_counter() - t0) * 1e3)
+        n = max(8, int(math.ceil(args.operand_seconds * 1e3 / one_ms)))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        mon = GpuMonitor()
+        if not args.no_gpu_monitor:
+            mon.start()
+        for e0, e1 in evs:
+            e0.record()
+            launch(ops)
+            e1.record()
+        torch.cuda.synchronize()
+        mon.stop()
+        ms = np.array([a.elapsed_time(b) for a, b in evs])
+        med = float(np.median(ms))
+        tf = flops / (med * 1e9)
+        rec = {"launches": n, "median_ms": round(med, 3), "tflops": round(tf, 1),
+               "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "gpu_state": mon.summary()}
+        gs = rec["gpu_state"]
+        if "gfx_clock_mhz" in gs:
+            sp = PEAK_BF16_TFLOPS * gs["gfx_clock_mhz"]["median"] / MAX_GFX_CLOCK_MHZ
+            rec["peak_at_median_clock_tflops"] = round(sp, 1)
+            rec["frac_of_peak_at_median_clock"] = round(tf / sp, 4) if tf <= sp else None
+        out["sets"][name] = rec
+        log(f"MFMA-only probe, {name} operands: {med:.3f} ms, {tf:.1f} TFLOP/s")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1006,6 +1077,9 @@ def main():
                          "K/V, each for --operand-seconds, with clock and power (how far operand data moves a "
                          "power-limited kernel)")
     ap.add_argument("--operand-seconds", type=float, default=4.0)
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="run only the MFMA-only probe on three operand sets (random, zeros, ones) and print "
+                         "its throughput, clock and power")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
                          "kernel that scales the profiler's HBM byte counters)")
@@ -1037,6 +1111,9 @@ def main():
     torch.cuda.set_device(0)
     if args.operand_study:
         operand_study(args, w0)
+        return
+    if args.mfma_ceiling:
+        mfma_ceiling(args)
         return
     out, (acts, x0h, xsh) = run_schedule(args, w0, K, args.warmup)
     if not args.no_cpu_baseline:

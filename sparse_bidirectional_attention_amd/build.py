@@ -5,7 +5,9 @@
 compiles every .hip source of csrc/ for gfx950 and the plain C++ host sources,
 and links them into sparse_bidirectional_attention_amd/libsdattn.so.  It also
 builds libsdattn_fake.so (tests/host): the schedule driver and the argument
-checks linked against a recording fake backend, for CPU-only tests.
+checks linked against a recording fake backend, for CPU-only tests, and
+libsdattn_probe.so (csrc/probe): an MFMA-only throughput probe the bench
+uses to measure the power-limited MFMA ceiling.
 """
 
 import os
@@ -21,6 +23,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsdattn.so")
 FAKE_SRC = os.path.join(ROOT, "tests", "host", "fake_backend.cpp")
 FAKE_LIB = os.path.join(ROOT, "tests", "host", "libsdattn_fake.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "mfma_ceiling.hip")
+PROBE_LIB = os.path.join(PKG, "libsdattn_probe.so")
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -69,6 +73,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     build_fake(verbose)
+    build_probe(verbose)
     return LIB
 
 
@@ -79,6 +84,17 @@ def build_fake(verbose: bool = False) -> str:
     _run(["g++", *CXX_FLAGS, "-shared", "-I", CSRC, "-o", tmp, *srcs], verbose)
     os.replace(tmp, FAKE_LIB)
     return FAKE_LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The MFMA-only throughput probe (measurement aid, its own library),
+    built with the compiler's default accumulator registers (not forced into
+    arch VGPRs: the probe has no VALU work that reads them)."""
+    tmp = PROBE_LIB + ".tmp"
+    flags = [f for f in HIP_FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+    _run([HIPCC, *flags, "-shared", "-o", tmp, PROBE_SRC], verbose)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
