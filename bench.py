@@ -184,11 +184,11 @@ def to_dev(x):
 
 
 def kernel_source_hash():
-    """Hash of the sources the flash-forward kernel is built from (the
-    kernel whose counters the traffic files hold)."""
+    """Hash of the sources the flash-forward kernel and its dispatch order
+    are built from (the kernel whose counters the traffic files hold)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_bidirectional_attention_amd", "csrc")
-    for f in ("flash_bf16.hip", "common.h", "launch.h"):
+    for f in ("flash_bf16.hip", "common.h", "launch.h", "block_plan.hip"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SDATTN_ABI_VERSION 4
+#define SDATTN_ABI_VERSION 5
 
 /* Exported entry points (the library is built with hidden visibility). */
 #define SDATTN_API __attribute__((visibility("default")))
@@ -227,6 +227,36 @@ SDATTN_API sdattn_status sdattn_forward_block_sparse(const sdattn_problem* p, co
                                           const void* v, int32_t block_q, int32_t block_k,
                                           const int32_t* row_ptr, const int32_t* col_idx,
                                           void* o, float* lse, void* stream);
+
+/*
+ * Dispatch plan of the block-sparse forward for one pattern.  Under a
+ * head-adaptive budget (Step-dLLM, Abstract) heads keep very different
+ * numbers of key blocks, so the work of a block row depends on its head; the
+ * plan spreads that work evenly over the GPU's XCDs while keeping each XCD on
+ * consecutive rows of one head at a time (their K/V in its L2).  Computed on
+ * the device from row_ptr alone (one small kernel, enqueued on `stream`);
+ * worth computing once per pattern when the pattern is reused over many
+ * steps.  plan: device int32 [B*Hq*nQB], written (a permutation of the block
+ * rows: workgroup i of the planned forward computes row plan[i]).  Errors:
+ * SDATTN_ERR_UNSUPPORTED for block sizes other than 64/128, SDATTN_ERR_NULL
+ * for a NULL row_ptr or plan (L > 0), SDATTN_ERR_SHAPE when B*Hq*nQB does not
+ * fit in int32.  row_ptr is trusted as for the forward.
+ */
+SDATTN_API sdattn_status sdattn_block_plan(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                const int32_t* row_ptr, int32_t* plan, void* stream);
+
+/*
+ * sdattn_forward_block_sparse over a dispatch plan from sdattn_block_plan for
+ * the same row_ptr (same arguments, results and errors; plan NULL is the
+ * unplanned call).  The result does not depend on the plan: every row is
+ * computed by one workgroup either way.  Workgroups whose plan entry is not a
+ * block row of the problem write nothing.  bfloat16 problems use the plan;
+ * float32 problems accept it and compute rows in their natural order.
+ */
+SDATTN_API sdattn_status sdattn_forward_block_sparse_planned(const sdattn_problem* p, const void* q, const void* k,
+                                                  const void* v, int32_t block_q, int32_t block_k,
+                                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                                  const int32_t* plan, void* o, float* lse, void* stream);
 
 /*
  * Overlap of two block patterns (the test of an adaptive anchor: Step-dLLM,

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdattn.so")
 
 # ABI of include/sdattn.h that this binding marshals for (SDATTN_ABI_VERSION)
-SDATTN_ABI_VERSION = 4
+SDATTN_ABI_VERSION = 5
 
 # ---- enums ------------------------------------------------------------------
 SDATTN_OK = 0
@@ -89,6 +89,9 @@ _SIGS = {
                                                   ctypes.c_size_t, _P]),
     "sdattn_forward_block_sparse": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32,
                                                    ctypes.c_int32, _P, _P, _P, _P, _P]),
+    "sdattn_block_plan": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
+    "sdattn_forward_block_sparse_planned": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32,
+                                                           ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     "sdattn_select_columns_workspace": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32,
                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "sdattn_select_columns": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32, _P, _P, _P,
@@ -270,6 +273,19 @@ def sdattn_forward_block_sparse(p, q, k, v, block_q, block_k, row_ptr, col_idx, 
     _check(lib().sdattn_forward_block_sparse(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), block_q, block_k,
                                              _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(lse), _stream(stream)),
            "sdattn_forward_block_sparse")
+
+
+def sdattn_block_plan(p, block_q, block_k, row_ptr, plan, stream=None):
+    """plan: int32 device tensor of B*Hq*nQB entries <- the dispatch plan of row_ptr's pattern."""
+    _check(lib().sdattn_block_plan(ctypes.byref(p), block_q, block_k, _ptr(row_ptr), _ptr(plan), _stream(stream)),
+           "sdattn_block_plan")
+
+
+def sdattn_forward_block_sparse_planned(p, q, k, v, block_q, block_k, row_ptr, col_idx, plan, o, lse=None,
+                                        stream=None):
+    _check(lib().sdattn_forward_block_sparse_planned(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), block_q, block_k,
+                                                     _ptr(row_ptr), _ptr(col_idx), _ptr(plan), _ptr(o), _ptr(lse),
+                                                     _stream(stream)), "sdattn_forward_block_sparse_planned")
 
 
 def sdattn_select_columns_workspace(p, kcol):

@@ -39,7 +39,7 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-Wno-unused-parameter"]
 
-HIP_SOURCES = ["api.hip", "flash_bf16.hip", "flash_f32.hip", "losa.hip", "mask_overlap.hip", "noalloc.hip",
+HIP_SOURCES = ["api.hip", "block_plan.hip", "flash_bf16.hip", "flash_f32.hip", "losa.hip", "mask_overlap.hip", "noalloc.hip",
                "select_blocks.hip", "select_columns.hip", "select_exact.hip"]
 CXX_SOURCES = ["host_common.cpp", "schedule.cpp"]
 

@@ -194,6 +194,33 @@ sdattn_status sdattn_select_blocks_exact(const sdattn_problem* p, const void* q,
 sdattn_status sdattn_forward_block_sparse(const sdattn_problem* p, const void* q, const void* k, const void* v,
                                           int32_t block_q, int32_t block_k, const int32_t* row_ptr,
                                           const int32_t* col_idx, void* o, float* lse, void* stream) {
+    return sdattn_forward_block_sparse_planned(p, q, k, v, block_q, block_k, row_ptr, col_idx, nullptr, o, lse,
+                                               stream);
+}
+
+sdattn_status sdattn_block_plan(const sdattn_problem* p, int32_t block_q, int32_t block_k, const int32_t* row_ptr,
+                                int32_t* plan, void* stream) {
+    Problem pr;
+    sdattn_status s = check_problem(p, &pr);
+    if (s != SDATTN_OK) return s;
+    if ((block_q != 64 && block_q != 128) || (block_k != 64 && block_k != 128))
+        return fail(SDATTN_ERR_UNSUPPORTED, "block_q and block_k must be 64 or 128");
+    if (pr.L == 0) return SDATTN_OK;
+    if (row_ptr == nullptr || plan == nullptr) return fail(SDATTN_ERR_NULL, "row_ptr and plan must be non-NULL");
+    const int nqt = (pr.L + block_q - 1) / block_q;
+    const long long rows = static_cast<long long>(pr.B) * pr.Hq * nqt;
+    if (rows > INT32_MAX) return fail(SDATTN_ERR_SHAPE, "B * Hq * nQB must fit in int32");
+    hipError_t e = launch_block_plan(static_cast<int>(rows), nqt, block_q, row_ptr, plan,
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdattn_block_plan");
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_forward_block_sparse_planned(const sdattn_problem* p, const void* q, const void* k,
+                                                  const void* v, int32_t block_q, int32_t block_k,
+                                                  const int32_t* row_ptr, const int32_t* col_idx,
+                                                  const int32_t* plan, void* o, float* lse, void* stream) {
+    const char* name = plan ? "sdattn_forward_block_sparse_planned" : "sdattn_forward_block_sparse";
     Problem pr;
     sdattn_status s = check_problem(p, &pr);
     if (s != SDATTN_OK) return s;
@@ -208,7 +235,8 @@ sdattn_status sdattn_forward_block_sparse(const sdattn_problem* p, const void* q
     ix.block_k = block_k;
     ix.row_ptr = row_ptr;
     ix.col_idx = col_idx;
-    return run_attention(MODE_BLOCK, pr, q, k, v, o, lse, ix, stream, "sdattn_forward_block_sparse");
+    ix.order = plan;
+    return run_attention(MODE_BLOCK, pr, q, k, v, o, lse, ix, stream, name);
 }
 
 sdattn_status sdattn_select_columns_workspace(const sdattn_problem* p, int32_t kcol, size_t* ws_bytes) {
@@ -318,8 +346,13 @@ sdattn_status be_select_blocks(void*, const sdattn_problem* p, const void* q, co
     return sdattn_select_blocks(p, q, k, bq, bk, b, rp, ci, cap, nullptr, ws, wsb, st);
 }
 sdattn_status be_block_sparse(void*, const sdattn_problem* p, const void* q, const void* k, const void* v, int32_t bq,
-                              int32_t bk, const int32_t* rp, const int32_t* ci, void* o, float* lse, void* st) {
-    return sdattn_forward_block_sparse(p, q, k, v, bq, bk, rp, ci, o, lse, st);
+                              int32_t bk, const int32_t* rp, const int32_t* ci, const int32_t* plan, void* o,
+                              float* lse, void* st) {
+    return sdattn_forward_block_sparse_planned(p, q, k, v, bq, bk, rp, ci, plan, o, lse, st);
+}
+sdattn_status be_block_plan(void*, const sdattn_problem* p, int32_t bq, int32_t bk, const int32_t* rp, int32_t* plan,
+                            void* st) {
+    return sdattn_block_plan(p, bq, bk, rp, plan, st);
 }
 sdattn_status be_select_columns(void*, const sdattn_problem* p, const void* q, const void* k, const float* lse,
                                 int32_t kcol, int32_t* ci, void* ws, size_t wsb, void* st) {
@@ -391,7 +424,7 @@ sdattn_status be_column_packed(void*, const sdattn_problem* p, const void* q, co
 const Backend kHipBackend = {nullptr,          be_dense,       be_select_blocks, be_block_sparse, be_select_columns,
                              be_column_sparse, be_ws_blocks,   be_ws_columns,    be_alloc,        be_release,
                              be_overlap,       be_probe_adopt, be_probe_init,    be_probe_read,   be_select_blocks_exact,
-                             be_ws_blocks_exact, be_gather_columns, be_column_packed};
+                             be_ws_blocks_exact, be_gather_columns, be_column_packed, be_block_plan};
 
 }  // namespace
 

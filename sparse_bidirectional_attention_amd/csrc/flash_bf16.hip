@@ -48,6 +48,7 @@ struct FlashParams {
     float* lse;
     const int32_t* row_ptr;
     const int32_t* col_idx;
+    const int32_t* order;  // block form: block row of each workgroup id (a dispatch plan), or nullptr
     int Hq, Hkv, L, group, n_qtiles, n_items, block_k;
     union {
         int kcol;     // column forms: kept columns per kv head
@@ -187,7 +188,11 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int hl = lane >> 5;
 
     int item;
-    if (MODE == MODE_BLOCK && p.n_pairs > 0)
+    if (MODE == MODE_BLOCK && p.order != nullptr) {
+        item = ((const cint32*)(p.order))[blockIdx.x];
+        if (static_cast<unsigned>(item) >= static_cast<unsigned>(p.n_items)) return;  // not a plan: nothing read
+    }
+    else if (MODE == MODE_BLOCK && p.n_pairs > 0)
         item = balanced_block_item(blockIdx.x, p.n_qtiles, p.n_pairs, p.row_ptr, lane);
     else
         item = xcd_remap(blockIdx.x, p.n_items, p.xcd_group);
@@ -1006,6 +1011,14 @@ constexpr int kRingK = 3, kRingV = 2;
 // 256 queries otherwise.
 inline int query_tile(AttnMode mode, const SparseIndex& ix) { return mode == MODE_BLOCK ? ix.block_q : 256; }
 
+}  // namespace
+
+// Workgroups of the block-sparse form that share one CU (LDS and registers):
+// four of the 40 KiB 64-query form, two of the 64 KiB 128-query form.
+int block_rows_per_cu(int block_q) { return block_q == 64 ? 4 : 2; }
+
+namespace {
+
 // Tile shapes (waves, keys per tile, LDS stages):
 //   256-query tiles (dense, column): 8 waves, 64-key tiles, two stages (64 KiB);
 //   128-query blocks: 4 waves, 64-key tiles, two stages (64 KiB, two
@@ -1039,6 +1052,7 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.lse = lse;
     fp.row_ptr = ix.row_ptr;
     fp.col_idx = ix.col_idx;
+    fp.order = mode == MODE_BLOCK ? ix.order : nullptr;
     fp.Hq = s.Hq;
     fp.Hkv = s.Hkv;
     fp.L = s.L;

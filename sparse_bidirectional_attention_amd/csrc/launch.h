@@ -22,6 +22,7 @@ struct SparseIndex {
     const int32_t* row_ptr = nullptr;     // MODE_BLOCK
     const int32_t* col_idx = nullptr;     // MODE_BLOCK (CSR) / MODE_COLUMN ([B][Hkv][kcol])
     int kcol = 0;                         // MODE_COLUMN, MODE_COLUMN_PACKED
+    const int32_t* order = nullptr;       // MODE_BLOCK: dispatch plan (launch_block_plan), or computed in the kernel
 };
 
 // Flash-style forward; bf16 inputs (MFMA) or f32 inputs (VALU).
@@ -31,6 +32,14 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
 hipError_t launch_flash_f32(AttnMode mode, const AttnShape& s, const void* q, const void* k,
                             const void* v, void* o, float* lse, const SparseIndex& ix,
                             hipStream_t st);
+
+// Workgroups of the bf16 block-sparse forward per CU for this block size.
+int block_rows_per_cu(int block_q);
+// Dispatch plan of the block-sparse forward: plan[id] = the block row that
+// workgroup id computes, a permutation of [0, rows) that gives every XCD an
+// equal share of the kept blocks (see block_plan.hip).  rows = B*Hq*nqt.
+int block_plan_segment_rows(int block_q, int nqt);
+hipError_t launch_block_plan(int rows, int nqt, int block_q, const int32_t* row_ptr, int32_t* plan, hipStream_t st);
 
 // Block selection.  Workspace layout is defined by select_blocks_ws_layout.
 struct BlockSelectWs {

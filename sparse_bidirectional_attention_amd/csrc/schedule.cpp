@@ -28,6 +28,7 @@ struct sdattn_schedule {
     // pattern buffers (device)
     int32_t* row_ptr[2] = {nullptr, nullptr};
     int32_t* col_idx[2] = {nullptr, nullptr};
+    int32_t* plan[2] = {nullptr, nullptr};  // block patterns: dispatch plan of each buffer's forward
     int64_t nnz_cap = 0;
     int32_t kcol = 0;
     int active = -1;  // -1: no pattern yet
@@ -173,6 +174,9 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         if (rp_bytes) {
             st = s->be.alloc(s->be.ctx, rp_bytes, reinterpret_cast<void**>(&s->row_ptr[i]));
             if (st != SDATTN_OK) return cleanup_fail(st);
+            const size_t plan_bytes = static_cast<size_t>(std::max<int64_t>(s->rows, 1)) * sizeof(int32_t);
+            st = s->be.alloc(s->be.ctx, plan_bytes, reinterpret_cast<void**>(&s->plan[i]));
+            if (st != SDATTN_OK) return cleanup_fail(st);
         }
         st = s->be.alloc(s->be.ctx, ci_bytes, reinterpret_cast<void**>(&s->col_idx[i]));
         if (st != SDATTN_OK) return cleanup_fail(st);
@@ -220,11 +224,17 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
                     st = be.select_blocks_exact(be.ctx, p, q, k, l, s->desc.block_q, s->desc.block_k, &s->desc.budget,
                                                 s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes,
                                                 stream);
+                if (st == SDATTN_OK)
+                    st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[next], s->plan[next],
+                                       stream);
             } else if (blocks) {
                 st = be.dense(be.ctx, p, q, k, v, o, lse, stream);
                 if (st == SDATTN_OK)
                     st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
                                           s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
+                if (st == SDATTN_OK)
+                    st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[next], s->plan[next],
+                                       stream);
             } else {
                 float* l = lse != nullptr ? lse : s->lse;
                 st = be.dense(be.ctx, p, q, k, v, o, l, stream);
@@ -242,8 +252,11 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
             st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
                                   s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
             if (st == SDATTN_OK)
+                st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[next], s->plan[next],
+                                   stream);
+            if (st == SDATTN_OK)
                 st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[next],
-                                     s->col_idx[next], o, lse, stream);
+                                     s->col_idx[next], s->plan[next], o, lse, stream);
             if (st == SDATTN_OK) {
                 s->active = next;
                 s->last_select = step;
@@ -269,9 +282,12 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
                 st = be.probe_adopt(be.ctx, static_cast<int32_t>(s->rows), s->row_ptr[a], s->col_idx[a],
                                     s->row_ptr[next], s->col_idx[next], s->probe_buf, s->probe_buf + 4,
                                     s->desc.min_overlap, s->nnz_cap, stream);
+            // the cached pattern may have been replaced: plan it again
+            if (st == SDATTN_OK)
+                st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[a], s->plan[a], stream);
             if (st == SDATTN_OK)
                 st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[a],
-                                     s->col_idx[a], o, lse, stream);
+                                     s->col_idx[a], s->plan[a], o, lse, stream);
             if (st == SDATTN_OK) s->n_probes += 1;
             return st;
         }
@@ -279,7 +295,7 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
             if (s->active < 0) return fail(SDATTN_ERR_STATE, "sparse step before any pattern was selected");
             if (blocks)
                 st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[s->active],
-                                     s->col_idx[s->active], o, lse, stream);
+                                     s->col_idx[s->active], s->plan[s->active], o, lse, stream);
             else {
                 // the kept columns' K/V rows are gathered once, then streamed
                 // by every query tile of the group
@@ -336,6 +352,7 @@ void sdattn_schedule_destroy(sdattn_schedule* s) {
     if (s->probe_buf) be.release(be.ctx, s->probe_buf);
     for (int i = 0; i < 2; ++i) {
         if (s->row_ptr[i]) be.release(be.ctx, s->row_ptr[i]);
+        if (s->plan[i]) be.release(be.ctx, s->plan[i]);
         if (s->col_idx[i]) be.release(be.ctx, s->col_idx[i]);
     }
     if (s->ws) be.release(be.ctx, s->ws);

@@ -15,8 +15,8 @@ struct Backend {
                                    int32_t bk, const sdattn_budget*, int32_t* row_ptr, int32_t* col_idx,
                                    int64_t cap, void* ws, size_t ws_bytes, void* stream);
     sdattn_status (*block_sparse)(void* ctx, const sdattn_problem*, const void* q, const void* k, const void* v,
-                                  int32_t bq, int32_t bk, const int32_t* row_ptr, const int32_t* col_idx, void* o,
-                                  float* lse, void* stream);
+                                  int32_t bq, int32_t bk, const int32_t* row_ptr, const int32_t* col_idx,
+                                  const int32_t* plan, void* o, float* lse, void* stream);
     sdattn_status (*select_columns)(void* ctx, const sdattn_problem*, const void* q, const void* k,
                                     const float* lse, int32_t kcol, int32_t* col_idx, void* ws, size_t ws_bytes,
                                     void* stream);
@@ -50,6 +50,9 @@ struct Backend {
                                     const int32_t* col_idx, int32_t kcol, void* kc, void* vc, void* stream);
     sdattn_status (*column_packed)(void* ctx, const sdattn_problem*, const void* q, const void* kc, const void* vc,
                                    int32_t kcol, void* o, float* lse, void* stream);
+    // dispatch plan of the block-sparse forward for a pattern's row_ptr
+    sdattn_status (*block_plan)(void* ctx, const sdattn_problem*, int32_t bq, int32_t bk, const int32_t* row_ptr,
+                                int32_t* plan, void* stream);
 };
 
 // The backend used by sdattn_schedule_create (defined by the library build

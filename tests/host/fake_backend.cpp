@@ -48,8 +48,14 @@ sdattn_status f_select_blocks(void*, const sdattn_problem*, const void*, const v
                   " bq=" + std::to_string(bq) + " bk=" + std::to_string(bk));
 }
 sdattn_status f_block_sparse(void*, const sdattn_problem*, const void*, const void*, const void*, int32_t,
-                             int32_t, const int32_t* rp, const int32_t* ci, void* o, float*, void*) {
-    return record("block_sparse rp=" + ptr(rp) + " ci=" + ptr(ci) + " o=" + ptr(o));
+                             int32_t, const int32_t* rp, const int32_t* ci, const int32_t* plan, void* o, float*,
+                             void*) {
+    return record("block_sparse rp=" + ptr(rp) + " ci=" + ptr(ci) + " plan=" + ptr(plan) + " o=" + ptr(o));
+}
+sdattn_status f_block_plan(void*, const sdattn_problem*, int32_t bq, int32_t bk, const int32_t* rp, int32_t* plan,
+                           void*) {
+    return record("block_plan rp=" + ptr(rp) + " plan=" + ptr(plan) + " bq=" + std::to_string(bq) +
+                  " bk=" + std::to_string(bk));
 }
 sdattn_status f_select_columns(void*, const sdattn_problem*, const void*, const void*, const float* lse, int32_t kcol,
                                int32_t* ci, void*, size_t, void*) {
@@ -138,7 +144,7 @@ sdattn_status f_column_packed(void*, const sdattn_problem*, const void*, const v
 const sdattn::Backend kFake = {nullptr,          f_dense,          f_select_blocks, f_block_sparse, f_select_columns,
                                f_column_sparse,  f_ws_blocks,      f_ws_columns,    f_alloc,        f_release,
                                f_overlap,        f_probe_adopt,    f_probe_init,    f_probe_read,   f_select_blocks_exact,
-                               f_ws_blocks_exact, f_gather_columns, f_column_packed};
+                               f_ws_blocks_exact, f_gather_columns, f_column_packed, f_block_plan};
 
 }  // namespace
 

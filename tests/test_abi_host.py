@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 27
+    assert len(names) == 29
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
     assert set(names) == exported  # nothing missing, nothing extra
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 4
+    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 5
     hdr = open(os.path.join(ROOT, "include", "sdattn.h")).read()
     assert f"#define SDATTN_ABI_VERSION {sd.SDATTN_ABI_VERSION}" in hdr
     for i, name in enumerate(sd.STATUS_NAMES):
@@ -102,6 +102,16 @@ def test_sparse_and_column_validation():
     p = sd.problem(1, 28, 4, 16384, 128, "bf16")
     assert lib.sdattn_forward_block_sparse(ctypes.byref(p), BAD, BAD, BAD, 96, 128, BAD, BAD, BAD, None, None) == 8
     assert lib.sdattn_forward_block_sparse(ctypes.byref(p), BAD, BAD, BAD, 64, 64, None, BAD, BAD, None, None) == 1
+    # dispatch plan: block sizes, NULL row_ptr / plan, L == 0 a no-op; the planned forward checks as the plain one
+    assert lib.sdattn_block_plan(ctypes.byref(p), 96, 128, BAD, BAD, None) == 8
+    assert lib.sdattn_block_plan(ctypes.byref(p), 64, 64, None, BAD, None) == 1
+    assert lib.sdattn_block_plan(ctypes.byref(p), 64, 64, BAD, None, None) == 1
+    p0 = sd.problem(1, 28, 4, 0, 128, "bf16")
+    assert lib.sdattn_block_plan(ctypes.byref(p0), 64, 64, None, None, None) == 0
+    assert lib.sdattn_forward_block_sparse_planned(ctypes.byref(p), BAD, BAD, BAD, 96, 128, BAD, BAD, BAD, BAD, None,
+                                                   None) == 8
+    assert lib.sdattn_forward_block_sparse_planned(ctypes.byref(p), BAD, BAD, BAD, 64, 64, BAD, None, BAD, BAD, None,
+                                                   None) == 1
     assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, BAD, 0, BAD, None, None) == 4
     assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, BAD, 16385, BAD, None, None) == 4
     assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, None, 492, BAD, None, None) == 1

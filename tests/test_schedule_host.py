@@ -117,16 +117,24 @@ def test_block_schedule_reuses_and_refreshes(fake):
     sparse = [l for l in log if l.startswith("block_sparse")]
     assert len(sel) == 8 and len(sparse) == 255 and log[0].startswith("dense")
     assert all("cap=52428" in l for l in sel)
-    # every sparse step uses the CSR of the most recent selection; buffers alternate
-    cur = None
-    bufs = []
-    for l in log:
+    # every selection is followed by the dispatch plan of its row_ptr; every
+    # sparse step uses the CSR and the plan of the most recent selection;
+    # buffers alternate
+    cur = plan = None
+    bufs, plans = [], []
+    for i, l in enumerate(log):
         if l.startswith("select_blocks"):
             cur = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
             bufs.append(cur)
+            assert log[i + 1].startswith("block_plan") and re.search(r"rp=(\S+)", log[i + 1]).group(1) == cur[0]
+            assert "bq=64 bk=64" in log[i + 1]
+            plan = re.search(r"plan=(\S+)", log[i + 1]).group(1)
+            plans.append(plan)
         elif l.startswith("block_sparse"):
             assert re.search(r"rp=(\S+) ci=(\S+)", l).groups() == cur
+            assert re.search(r"plan=(\S+)", l).group(1) == plan
     assert bufs[0] != bufs[1] and bufs[0] == bufs[2]
+    assert plans[0] != plans[1] and plans[0] == plans[2] and "(nil)" not in plans
     counts = (ctypes.c_int64 * 4)()
     last = ctypes.c_int32(0)
     assert fake.sdattn_schedule_stats(h, counts, ctypes.byref(last)) == 0
@@ -145,6 +153,11 @@ def test_failed_selection_keeps_the_cached_pattern(fake):
     fake.sdattn_fake_reset(0, 7)  # the next backend call (the step-32 selection) fails
     assert _step(fake, h, 32) == 7
     assert "injected" in fake.sdattn_last_error().decode()
+    assert fake.sdattn_schedule_mask(h, ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(cap)) == 0
+    assert (rp.value, ci.value) == before
+    fake.sdattn_fake_reset(1, 7)  # the selection succeeds, its dispatch plan fails: still the cached pattern
+    assert _step(fake, h, 32) == 7
+    assert [l.split()[0] for l in _log(fake)] == ["select_blocks", "FAIL"]
     assert fake.sdattn_schedule_mask(h, ctypes.byref(rp), ctypes.byref(ci), ctypes.byref(cap)) == 0
     assert (rp.value, ci.value) == before
     fake.sdattn_fake_reset(-1, 0)
@@ -224,10 +237,13 @@ def test_probe_step_selects_into_the_idle_buffer_and_adopts_over_the_cached_one(
         l = log[i]
         if l.startswith("select_blocks") and i + 1 < len(log) and log[i + 1].startswith("overlap"):
             # a probe: selection into the idle buffer, overlap(cached, probe),
-            # adoption of the probe over the cached buffer, attention on the cached buffer
+            # adoption of the probe over the cached buffer, the cached buffer's
+            # dispatch plan computed again, attention on the cached buffer
             probe_buf = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
             assert probe_buf != cached
-            ov, ad, bs = log[i + 1], log[i + 2], log[i + 3]
+            ov, ad, pl, bs = log[i + 1], log[i + 2], log[i + 3], log[i + 4]
+            assert pl.startswith("block_plan") and re.search(r"rp=(\S+)", pl).group(1) == cached[0]
+            assert re.search(r"plan=(\S+)", bs).group(1) == re.search(r"plan=(\S+)", pl).group(1)
             assert re.search(r"a=(\S+),(\S+) b=(\S+),(\S+)", ov).groups() == cached + probe_buf
             assert f"rows={32 * 128}" in ov
             assert re.search(r"dst=(\S+),(\S+) src=(\S+),(\S+)", ad).groups() == cached + probe_buf
@@ -235,7 +251,7 @@ def test_probe_step_selects_into_the_idle_buffer_and_adopts_over_the_cached_one(
             assert f"state={state}" in ad and "min_overlap=0.7" in ad and "max_copy=52428" in ad
             assert bs.startswith("block_sparse") and re.search(r"rp=(\S+) ci=(\S+)", bs).groups() == cached
             probes += 1
-            i += 4
+            i += 5
             continue
         if l.startswith("select_blocks"):  # a scheduled refresh switches buffers
             cached = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
@@ -288,7 +304,8 @@ def test_probe_step_errors_leave_the_pattern_alone(fake):
     assert (n.value, a.value, j.value) == (0, 0, 1.0)
     fake.sdattn_fake_reset(-1, 0)
     assert _step(fake, h, 3) == 0
-    assert [l.split()[0] for l in _log(fake)] == ["select_blocks", "overlap", "probe_adopt", "block_sparse"]
+    assert [l.split()[0] for l in _log(fake)] == ["select_blocks", "overlap", "probe_adopt", "block_plan",
+                                                  "block_sparse"]
     fake.sdattn_schedule_destroy(h)
     assert fake.sdattn_fake_live_allocs() == 0
 
@@ -312,13 +329,17 @@ def test_exact_selector_schedule_uses_the_dense_lse(fake):
         own = re.search(r"lse=(\S+)", log[i - 1]).group(1)
         assert own != "(nil)" and re.search(r"lse=(\S+)", log[i]).group(1) == own
         assert "cap=425984" in log[i]
-    # sparse steps use the pattern of the latest selection (applies from the next step)
-    cur = None
-    for l in log:
+    # sparse steps use the pattern of the latest selection (applies from the
+    # next step) and the dispatch plan computed right after it
+    cur = plan = None
+    for i, l in enumerate(log):
         if l.startswith("select_blocks_exact"):
             cur = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
+            assert log[i + 1].startswith("block_plan") and re.search(r"rp=(\S+)", log[i + 1]).group(1) == cur[0]
+            plan = re.search(r"plan=(\S+)", log[i + 1]).group(1)
         elif l.startswith("block_sparse"):
             assert re.search(r"rp=(\S+) ci=(\S+)", l).groups() == cur
+            assert re.search(r"plan=(\S+)", l).group(1) == plan
     # a caller lse is used when given
     fake.sdattn_fake_reset(-1, 0)
     assert _step(fake, h, 3, lse=ctypes.c_void_p(0x7000)) == 0
