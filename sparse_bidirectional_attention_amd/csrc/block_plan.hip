@@ -13,15 +13,19 @@
 //     most first, and dealt to the XCDs in snake order (ranks 0..7 to XCDs
 //     0..7, ranks 8..15 to XCDs 7..0, ...), which evens the XCDs' totals and
 //     leaves the lightest segments for the end of the launch;
+//   * within a segment the rows go longest first, so the rows an XCD starts
+//     last, as its slots drain at the end of the launch, are its shortest;
 //   * equal totals keep the plain order (segment s on XCD s mod 8, in round
-//     s / 8), so a top-k pattern gets the same dispatch as without the ranking.
-// The k-th workgroup of XCD x (id 8k + x) then takes row k mod S of the
+//     s / 8, its rows in order), so a top-k pattern gets the same dispatch as
+//     without the ranking.
+// The k-th workgroup of XCD x (id 8k + x) then takes position k mod S of the
 // segment dealt to x in round k / S.  Any order gives the same result: each
 // row is computed by one workgroup.
 //
-// One workgroup of 1024 threads sorts the segment keys in LDS (bitonic, at
-// most kMaxSegments); shapes whose segments do not fill whole rounds of eight
-// get the identity plan.
+// One workgroup per segment: it ranks its segment against all the others
+// (their totals read from row_ptr), sorts its rows in LDS and writes their
+// plan entries.  Shapes whose segments do not fill whole rounds of eight get
+// the identity plan.
 
 #include <stdint.h>
 
@@ -31,8 +35,10 @@
 namespace sdattn {
 namespace {
 
-constexpr int kMaxSegments = 8192;
-constexpr int kTieBits = 20;  // >= log2(kMaxSegments)
+constexpr int kMaxSegments = 1 << 20;  // segment indices fit the tie bits
+constexpr int kMaxSegRows = 1024;      // rows of one segment, sorted in LDS
+constexpr int kTieBits = 20;
+constexpr unsigned long long kTieMask = (1ull << kTieBits) - 1;
 
 // position of segment s in the snake deal (an involution)
 __device__ __forceinline__ int snake_pos(int s) {
@@ -40,39 +46,54 @@ __device__ __forceinline__ int snake_pos(int s) {
     return 8 * j + ((j & 1) ? 7 - x : x);
 }
 
-__global__ __launch_bounds__(1024) void block_plan_kernel(const int32_t* __restrict__ row_ptr, int rows, int nqt,
-                                                          int seg_rows, int n_seg, int np2,
-                                                          int32_t* __restrict__ plan) {
-    __shared__ unsigned long long keys[kMaxSegments];
+__global__ __launch_bounds__(256) void identity_plan_kernel(int rows, int32_t* __restrict__ plan) {
+    const int id = blockIdx.x * blockDim.x + threadIdx.x;
+    if (id < rows) plan[id] = id;
+}
+
+__global__ __launch_bounds__(256) void block_plan_kernel(const int32_t* __restrict__ row_ptr, int nqt, int seg_rows,
+                                                         int n_seg, int np2, int32_t* __restrict__ plan) {
+    __shared__ unsigned long long keys[kMaxSegRows];
+    __shared__ int part[256 / 64];
+    const int seg = blockIdx.x;
     const int tid = threadIdx.x;
-    if (n_seg == 0) {  // identity plan
-        for (int id = tid; id < rows; id += blockDim.x) plan[id] = id;
-        return;
-    }
     const int parts = nqt / seg_rows;
-    // key: (kept blocks + 1) above the tie bits, larger first; ties in the
-    // plain order (rank of segment s = its snake position)
-    for (int s = tid; s < np2; s += blockDim.x) {
+    auto first_row = [&](int t) { return (t / parts) * nqt + (t % parts) * seg_rows; };
+    // key of segment t: (kept blocks + 1) above the tie bits, larger first;
+    // ties in the plain order (rank of segment t = its snake position)
+    auto seg_key = [&](int t) -> unsigned long long {
+        const int r0 = first_row(t);
+        const long long total = static_cast<long long>(row_ptr[r0 + seg_rows]) - row_ptr[r0];
+        const unsigned long long v = static_cast<unsigned long long>(min(max(total, 0LL), (1LL << 40))) + 1;
+        return (v << kTieBits) | static_cast<unsigned long long>(n_seg - 1 - snake_pos(t));
+    };
+    // rank of this segment: the number of segments with a larger key
+    const unsigned long long mine = seg_key(seg);
+    int c = 0;
+    for (int t = tid; t < n_seg; t += blockDim.x) c += seg_key(t) > mine ? 1 : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off);
+    if ((tid & 63) == 0) part[tid >> 6] = c;
+    // rows of this segment, most kept blocks first (ties: lower row first)
+    const int r0 = first_row(seg);
+    for (int i = tid; i < np2; i += blockDim.x) {
         unsigned long long key = 0;
-        if (s < n_seg) {
-            const int p = s / parts, j = s - (s / parts) * parts;
-            const int r0 = p * nqt + j * seg_rows;
-            const long long total = static_cast<long long>(row_ptr[r0 + seg_rows]) - row_ptr[r0];
-            const unsigned long long t = static_cast<unsigned long long>(min(max(total, 0LL), (1LL << 40))) + 1;
-            key = (t << kTieBits) | static_cast<unsigned long long>(n_seg - 1 - snake_pos(s));
+        if (i < seg_rows) {
+            const long long ne = static_cast<long long>(row_ptr[r0 + i + 1]) - row_ptr[r0 + i];
+            const unsigned long long v = static_cast<unsigned long long>(min(max(ne, 0LL), (1LL << 40))) + 1;
+            key = (v << kTieBits) | (kTieMask - static_cast<unsigned long long>(i));
         }
-        keys[s] = key;
+        keys[i] = key;
     }
     __syncthreads();
-    // bitonic sort, descending
-    for (int k = 2; k <= np2; k <<= 1) {
+    const int rank = part[0] + part[1] + part[2] + part[3];
+    for (int k = 2; k <= np2; k <<= 1) {  // bitonic sort, descending
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = tid; i < np2; i += blockDim.x) {
                 const int l = i ^ j;
                 if (l > i) {
                     const unsigned long long a = keys[i], b = keys[l];
-                    const bool swap = (i & k) == 0 ? a < b : a > b;
-                    if (swap) {
+                    if ((i & k) == 0 ? a < b : a > b) {
                         keys[i] = b;
                         keys[l] = a;
                     }
@@ -81,15 +102,13 @@ __global__ __launch_bounds__(1024) void block_plan_kernel(const int32_t* __restr
             __syncthreads();
         }
     }
-    // workgroup id -> block row
-    constexpr unsigned long long kTieMask = (1ull << kTieBits) - 1;
-    for (int id = tid; id < rows; id += blockDim.x) {
-        const int x = id & 7, m = id >> 3;
-        const int k = m / seg_rows, i = m - (m / seg_rows) * seg_rows;
-        const int r = 8 * k + ((k & 1) ? 7 - x : x);  // rank dealt to XCD x in round k
-        const int s = snake_pos(n_seg - 1 - static_cast<int>(keys[r] & kTieMask));
-        const int p = s / parts, j = s - (s / parts) * parts;
-        plan[id] = p * nqt + j * seg_rows + i;
+    // the segment of rank `rank` goes to XCD x in round rank / 8; position i
+    // of it to workgroup 8 (round * S + i) + x
+    const int round = rank >> 3, w = rank & 7;
+    const int x = (round & 1) ? 7 - w : w;
+    for (int i = tid; i < seg_rows; i += blockDim.x) {
+        const int row = r0 + static_cast<int>(kTieMask - (keys[i] & kTieMask));
+        plan[8 * (round * seg_rows + i) + x] = row;
     }
 }
 
@@ -110,11 +129,14 @@ int block_plan_segment_rows(int block_q, int nqt) {
 hipError_t launch_block_plan(int rows, int nqt, int block_q, const int32_t* row_ptr, int32_t* plan, hipStream_t st) {
     if (rows <= 0) return hipSuccess;
     const int seg_rows = block_plan_segment_rows(block_q, nqt);
-    int n_seg = rows / seg_rows;
-    if (nqt % seg_rows != 0 || n_seg % 8 != 0 || n_seg > kMaxSegments) n_seg = 0;  // identity plan
+    const int n_seg = rows / seg_rows;
+    if (nqt % seg_rows != 0 || n_seg % 8 != 0 || n_seg > kMaxSegments || seg_rows > kMaxSegRows) {
+        hipLaunchKernelGGL(identity_plan_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, rows, plan);
+        return hipGetLastError();
+    }
     int np2 = 1;
-    while (np2 < n_seg) np2 <<= 1;
-    hipLaunchKernelGGL(block_plan_kernel, dim3(1), dim3(1024), 0, st, row_ptr, rows, nqt, seg_rows, n_seg, np2, plan);
+    while (np2 < seg_rows) np2 <<= 1;
+    hipLaunchKernelGGL(block_plan_kernel, dim3(n_seg), dim3(256), 0, st, row_ptr, nqt, seg_rows, n_seg, np2, plan);
     return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@
 The plan is a scheduling choice, not part of what the method computes, so
 it is checked by what it must satisfy: it equals the rule written out on the
 host below (segments of consecutive query blocks ranked by their kept
-blocks, ties in the plain order, dealt to the eight XCDs in snake order), it
+blocks, ties in the plain order, dealt to the eight XCDs in snake order, the
+rows of a segment longest first), it
 is a permutation of the block rows, it evens the XCDs' kept blocks under
 head-skewed budgets (Step-dLLM, Abstract: head-adaptive budget), and the
 planned forward is bit-identical to the unplanned one (each row is computed
@@ -51,12 +52,15 @@ def host_plan(row_ptr, rows, nqt, block_q):
 
     tot = [int(row_ptr[first_row(s) + seg]) - int(row_ptr[first_row(s)]) for s in range(n_seg)]
     ranked = sorted(range(n_seg), key=lambda s: (-tot[s], _snake(s)))
+    ne = np.diff(np.asarray(row_ptr, np.int64))
+    # within a segment: most kept blocks first, ties in row order
+    inner = {s: sorted(range(seg), key=lambda t: (-ne[first_row(s) + t], t)) for s in range(n_seg)}
     plan = np.empty(rows, np.int64)
     for i in range(rows):
         x, m = i % 8, i // 8
         k, j = divmod(m, seg)
         r = 8 * k + (7 - x if k % 2 else x)
-        plan[i] = first_row(ranked[r]) + j
+        plan[i] = first_row(ranked[r]) + inner[ranked[r]][j]
     return plan
 
 
