@@ -43,7 +43,7 @@ def _snake(s):
 def host_plan(row_ptr, rows, nqt, block_q):
     seg = _segment_rows(block_q, nqt)
     n_seg = rows // seg
-    if nqt % seg or n_seg % 8 or n_seg > 8192:
+    if nqt % seg or n_seg % 8 or n_seg > (1 << 20) or seg > 1024:
         return np.arange(rows)
     parts = nqt // seg
 
