@@ -1020,6 +1020,111 @@ def operand_study(args, w0):
     print(json.dumps(out), flush=True)
 
 
+def split_study(args, w0):
+    """Split rows against the dispatch plan alone, on the workload's inputs and
+    block size with head-skewed patterns: n heads keep every key block, the
+    others a few (seeded random kept blocks, ascending), n = 0, 1, 2, 4; and
+    the pooled selection's own pattern.  A near-dense head beside sparse ones
+    is what a head-adaptive budget without a cap can produce (Step-dLLM,
+    Abstract); no schedule of the five workloads makes one, so this is a
+    study, not the headline.  Reports per pattern the kept blocks, the rows
+    the split plan cuts and its chunk length, both forwards' launch times
+    (HIP events, median of three rounds) and TFLOP/s on the kept blocks, and
+    the split output's largest difference from the planned one."""
+    import numpy as np
+    import torch
+
+    import sparse_bidirectional_attention_amd as sd
+    from workloads import make_base, make_step
+
+    w = w0
+    if w.selector == "columns":
+        raise SystemExit("--split-study takes a block workload")
+    p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
+    base = make_base(w)
+    xh = make_step(w, w.select_step, base)
+    del base
+    x = {n: to_dev(a) for n, a in xh.items()}
+    del xh
+    bq = w.block
+    nqb = -(-w.seq_len // bq)
+    pairs = w.batch * w.q_heads
+    rows = pairs * nqb
+    slots = 256 * (4 if bq == 64 else 2)
+    o1 = torch.empty_like(x["q"])
+    o2 = torch.empty_like(x["q"])
+    l1 = torch.empty(x["q"].shape[:3], dtype=torch.float32, device="cuda")
+    l2 = torch.empty_like(l1)
+    rng = np.random.default_rng(12345)
+    few = 4 if nqb <= 128 else max(4, int(round(0.05 * nqb)))
+
+    def skewed(n_dense):
+        rp, kept = [0], []
+        for pr in range(pairs):
+            k = nqb if pr % w.q_heads < n_dense else few
+            for _ in range(nqb):
+                kept.append(np.sort(rng.choice(nqb, size=k, replace=False)).astype(np.int32))
+                rp.append(rp[-1] + k)
+        return (torch.from_numpy(np.array(rp, np.int32)).cuda(),
+                torch.from_numpy(np.concatenate(kept)).cuda())
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        meds = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            meds.append(e0.elapsed_time(e1) / n)
+        return float(np.median(meds))
+
+    patterns = {}
+    budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
+    wsb, cap = sd.sdattn_select_blocks_workspace(p, bq, bq, budget)
+    rp = torch.empty(rows + 1, dtype=torch.int32, device="cuda")
+    ci = torch.empty(max(cap, 1), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    sd.sdattn_select_blocks(p, x["q"], x["k"], bq, bq, budget, rp, ci, cap, None, ws, wsb)
+    del ws
+    patterns["pooled selection"] = (rp, ci)
+    for n in (1, 2, 4):
+        patterns[f"{n} dense head{'s' if n > 1 else ''}, others {few} blocks"] = skewed(n)
+    swsb = sd.sdattn_block_split_workspace(p, bq, bq)
+    sws = torch.empty(swsb, dtype=torch.uint8, device="cuda")
+    plan = torch.empty(rows, dtype=torch.int32, device="cuda")
+    out = {"kind": "block-sparse forward: dispatch plan vs split rows (online-softmax merge)",
+           "workload": w.name, "block": bq, "patterns": {}}
+    for name, (rpp, cip) in patterns.items():
+        torch.cuda.synchronize()
+        nnz = int(rpp[rows].item())
+        flops = 4.0 * w.head_dim * bq * bq * nnz
+        sd.sdattn_block_plan(p, bq, bq, rpp, plan)
+        sd.sdattn_block_split_plan(p, bq, bq, rpp, sws, swsb)
+        torch.cuda.synchronize()
+        w32 = sws.view(torch.int32)
+        cnt = rows + 2 * slots + rows
+        cut, T = int(w32[cnt].item()), int(w32[cnt + 1].item())
+        n = max(5, min(200, int(2000.0 / max(0.05, flops / 1e12))))
+        t_plan = timed(lambda: sd.sdattn_forward_block_sparse_planned(p, x["q"], x["k"], x["v"], bq, bq, rpp, cip,
+                                                                      plan, o1, l1), n)
+        t_split = timed(lambda: sd.sdattn_forward_block_sparse_split(p, x["q"], x["k"], x["v"], bq, bq, rpp, cip,
+                                                                     sws, o2, l2, ws_bytes=swsb), n)
+        torch.cuda.synchronize()
+        diff = float((o1.float() - o2.float()).abs().max().item())
+        rec = {"kept_blocks": nnz, "rows_cut": cut, "chunk_blocks": T,
+               "planned_ms": round(t_plan, 4), "split_ms": round(t_split, 4),
+               "speedup": round(t_plan / t_split, 3),
+               "planned_tflops": round(flops / t_plan / 1e9, 1), "split_tflops": round(flops / t_split / 1e9, 1),
+               "max_abs_diff_vs_planned": diff}
+        out["patterns"][name] = rec
+        log(f"split study {name}: {rec}")
+    print(json.dumps(out), flush=True)
+
+
 def mfma_ceiling(args):
     """The MFMA-only ceiling: a probe kernel (libsdattn_probe.so) that keeps
     its operands in registers and issues nothing but bf16 32x32x16 MFMAs,
@@ -1120,6 +1225,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="run only the MFMA-only probe on three operand sets (random, zeros, ones) and print "
                          "its throughput, clock and power")
+    ap.add_argument("--split-study", action="store_true",
+                    help="instead of the schedule: the block-sparse forward over the dispatch plan against split "
+                         "rows, on head-skewed patterns (dense heads beside sparse ones) and the pooled pattern")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a known-size "
                          "kernel that scales the profiler's HBM byte counters)")
@@ -1154,6 +1262,9 @@ def main():
         return
     if args.mfma_ceiling:
         mfma_ceiling(args)
+        return
+    if args.split_study:
+        split_study(args, w0)
         return
     out, (acts, x0h, xsh) = run_schedule(args, w0, K, args.warmup)
     if not args.no_cpu_baseline:

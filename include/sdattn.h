@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define SDATTN_ABI_VERSION 5
+#define SDATTN_ABI_VERSION 6
 
 /* Exported entry points (the library is built with hidden visibility). */
 #define SDATTN_API __attribute__((visibility("default")))
@@ -257,6 +257,48 @@ SDATTN_API sdattn_status sdattn_forward_block_sparse_planned(const sdattn_proble
                                                   const void* v, int32_t block_q, int32_t block_k,
                                                   const int32_t* row_ptr, const int32_t* col_idx,
                                                   const int32_t* plan, void* o, float* lse, void* stream);
+
+/*
+ * Split rows.  A dispatch plan cannot shorten a launch below its longest
+ * block row: under a head-adaptive budget (Step-dLLM, Abstract) one head may
+ * keep most key blocks while the others keep few.  A split plan cuts every
+ * row with more kept blocks than T = max(4, ceil(nnz / slots)) (slots = the
+ * workgroups the GPU holds at once: 1024 for 64-query blocks, 512 for 128)
+ * into c = min(8, ceil(ne / T)) chunks of consecutive kept blocks.  Each
+ * chunk is computed by its own workgroup, which writes its output
+ * normalised over the chunk together with the chunk's log-sum-exp; a merge
+ * then combines a row's chunks, O = sum_k exp(lse_k - LSE) O_k with
+ * LSE = log sum_k exp(lse_k) (the online-softmax merge of partial rows, LoSA
+ * section 3, step 5).  The chunks of the cut rows are dealt first, spread
+ * over the XCDs; the rows that are not cut follow, computed whole, in the
+ * dispatch plan's order.
+ *
+ * sdattn_block_split_workspace: bytes of the one workspace that holds the
+ * plan and the partial results (host only; 0 when L == 0).  Errors as for
+ * sdattn_block_plan, and SDATTN_ERR_SHAPE when B*Hq*nQB >= 2^24.
+ *
+ * sdattn_block_split_plan: computes the split plan of a pattern into ws
+ * (device, enqueued on `stream`; worth doing once per pattern).  It depends on
+ * row_ptr only.  SDATTN_ERR_NULL for a NULL row_ptr (L > 0),
+ * SDATTN_ERR_WORKSPACE for a NULL or short ws.
+ *
+ * sdattn_forward_block_sparse_split: sdattn_forward_block_sparse over a split
+ * plan computed for the same row_ptr and problem, in the same ws (which the
+ * call also writes: the partial results).  Results equal the unsplit
+ * forward's within the bf16 rounding of O (rows that are not cut are
+ * bit-identical to it).  Two kernels on `stream`: the forward over the plan's
+ * items, then the merge.  Calls that share a ws must not overlap.  float32
+ * problems compute every row whole.  Errors as for the forward, plus
+ * SDATTN_ERR_WORKSPACE and SDATTN_ERR_SHAPE as above.
+ */
+SDATTN_API sdattn_status sdattn_block_split_workspace(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                           size_t* ws_bytes);
+SDATTN_API sdattn_status sdattn_block_split_plan(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                      const int32_t* row_ptr, void* ws, size_t ws_bytes, void* stream);
+SDATTN_API sdattn_status sdattn_forward_block_sparse_split(const sdattn_problem* p, const void* q, const void* k,
+                                                const void* v, int32_t block_q, int32_t block_k,
+                                                const int32_t* row_ptr, const int32_t* col_idx, void* ws,
+                                                size_t ws_bytes, void* o, float* lse, void* stream);
 
 /*
  * Overlap of two block patterns (the test of an adaptive anchor: Step-dLLM,

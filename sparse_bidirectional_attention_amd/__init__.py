@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsdattn.so")
 
 # ABI of include/sdattn.h that this binding marshals for (SDATTN_ABI_VERSION)
-SDATTN_ABI_VERSION = 5
+SDATTN_ABI_VERSION = 6
 
 # ---- enums ------------------------------------------------------------------
 SDATTN_OK = 0
@@ -92,6 +92,12 @@ _SIGS = {
     "sdattn_block_plan": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32, _P, _P, _P]),
     "sdattn_forward_block_sparse_planned": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32,
                                                            ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
+    "sdattn_block_split_workspace": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "sdattn_block_split_plan": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                               ctypes.c_size_t, _P]),
+    "sdattn_forward_block_sparse_split": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32,
+                                                         ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P, _P, _P]),
     "sdattn_select_columns_workspace": (ctypes.c_int, [ctypes.POINTER(Problem), ctypes.c_int32,
                                                        ctypes.POINTER(ctypes.c_size_t)]),
     "sdattn_select_columns": (ctypes.c_int, [ctypes.POINTER(Problem), _P, _P, _P, ctypes.c_int32, _P, _P, _P,
@@ -286,6 +292,30 @@ def sdattn_forward_block_sparse_planned(p, q, k, v, block_q, block_k, row_ptr, c
     _check(lib().sdattn_forward_block_sparse_planned(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), block_q, block_k,
                                                      _ptr(row_ptr), _ptr(col_idx), _ptr(plan), _ptr(o), _ptr(lse),
                                                      _stream(stream)), "sdattn_forward_block_sparse_planned")
+
+
+def sdattn_block_split_workspace(p, block_q, block_k):
+    ws = ctypes.c_size_t(0)
+    _check(lib().sdattn_block_split_workspace(ctypes.byref(p), block_q, block_k, ctypes.byref(ws)),
+           "sdattn_block_split_workspace")
+    return ws.value
+
+
+def sdattn_block_split_plan(p, block_q, block_k, row_ptr, ws, ws_bytes=None, stream=None):
+    """ws: uint8 device tensor of sdattn_block_split_workspace bytes <- the split plan of row_ptr's pattern."""
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().sdattn_block_split_plan(ctypes.byref(p), block_q, block_k, _ptr(row_ptr), _ptr(ws), ws_bytes,
+                                         _stream(stream)), "sdattn_block_split_plan")
+
+
+def sdattn_forward_block_sparse_split(p, q, k, v, block_q, block_k, row_ptr, col_idx, ws, o, lse=None,
+                                      ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().sdattn_forward_block_sparse_split(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), block_q, block_k,
+                                                   _ptr(row_ptr), _ptr(col_idx), _ptr(ws), ws_bytes, _ptr(o),
+                                                   _ptr(lse), _stream(stream)), "sdattn_forward_block_sparse_split")
 
 
 def sdattn_select_columns_workspace(p, kcol):

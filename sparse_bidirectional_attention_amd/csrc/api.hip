@@ -239,6 +239,84 @@ sdattn_status sdattn_forward_block_sparse_planned(const sdattn_problem* p, const
     return run_attention(MODE_BLOCK, pr, q, k, v, o, lse, ix, stream, name);
 }
 
+namespace {
+
+// Shared checks of the split-plan calls; *rows_out = B * Hq * nQB.
+sdattn_status check_split(const sdattn_problem* p, int32_t block_q, int32_t block_k, Problem* pr, int* rows_out) {
+    sdattn_status s = check_problem(p, pr);
+    if (s != SDATTN_OK) return s;
+    if ((block_q != 64 && block_q != 128) || (block_k != 64 && block_k != 128))
+        return fail(SDATTN_ERR_UNSUPPORTED, "block_q and block_k must be 64 or 128");
+    const int nqt = (pr->L + block_q - 1) / block_q;
+    const long long rows = static_cast<long long>(pr->B) * pr->Hq * nqt;
+    if (rows >= (1LL << kSplitRowBits)) return fail(SDATTN_ERR_SHAPE, "B * Hq * nQB must be below 2^24 for a split plan");
+    *rows_out = static_cast<int>(rows);
+    return SDATTN_OK;
+}
+
+sdattn_status check_split_ws(const Problem& pr, int rows, int32_t block_q, const void* ws, size_t ws_bytes) {
+    const size_t need = split_ws_bytes(rows, block_q, pr.D);
+    if (ws == nullptr || ws_bytes < need) {
+        char buf[160];
+        snprintf(buf, sizeof buf, "workspace of %zu bytes < required %zu", ws == nullptr ? 0 : ws_bytes, need);
+        return fail(SDATTN_ERR_WORKSPACE, buf);
+    }
+    return SDATTN_OK;
+}
+
+}  // namespace
+
+sdattn_status sdattn_block_split_workspace(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                           size_t* ws_bytes) {
+    if (ws_bytes == nullptr) return fail(SDATTN_ERR_NULL, "ws_bytes must be non-NULL");
+    Problem pr;
+    int rows = 0;
+    sdattn_status s = check_split(p, block_q, block_k, &pr, &rows);
+    if (s != SDATTN_OK) return s;
+    *ws_bytes = pr.L == 0 ? 0 : split_ws_bytes(rows, block_q, pr.D);
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_block_split_plan(const sdattn_problem* p, int32_t block_q, int32_t block_k,
+                                      const int32_t* row_ptr, void* ws, size_t ws_bytes, void* stream) {
+    Problem pr;
+    int rows = 0;
+    sdattn_status s = check_split(p, block_q, block_k, &pr, &rows);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (row_ptr == nullptr) return fail(SDATTN_ERR_NULL, "row_ptr must be non-NULL");
+    s = check_split_ws(pr, rows, block_q, ws, ws_bytes);
+    if (s != SDATTN_OK) return s;
+    const int nqt = (pr.L + block_q - 1) / block_q;
+    hipError_t e = launch_split_plan(rows, nqt, block_q, row_ptr, static_cast<int32_t*>(ws),
+                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "sdattn_block_split_plan");
+    return SDATTN_OK;
+}
+
+sdattn_status sdattn_forward_block_sparse_split(const sdattn_problem* p, const void* q, const void* k,
+                                                const void* v, int32_t block_q, int32_t block_k,
+                                                const int32_t* row_ptr, const int32_t* col_idx, void* ws,
+                                                size_t ws_bytes, void* o, float* lse, void* stream) {
+    Problem pr;
+    int rows = 0;
+    sdattn_status s = check_split(p, block_q, block_k, &pr, &rows);
+    if (s != SDATTN_OK) return s;
+    s = check_tensors(pr, q, k, v, o);
+    if (s != SDATTN_OK) return s;
+    if (pr.L == 0) return SDATTN_OK;
+    if (row_ptr == nullptr || col_idx == nullptr) return fail(SDATTN_ERR_NULL, "row_ptr and col_idx must be non-NULL");
+    s = check_split_ws(pr, rows, block_q, ws, ws_bytes);
+    if (s != SDATTN_OK) return s;
+    SparseIndex ix;
+    ix.block_q = block_q;
+    ix.block_k = block_k;
+    ix.row_ptr = row_ptr;
+    ix.col_idx = col_idx;
+    ix.split = static_cast<int32_t*>(ws);
+    return run_attention(MODE_BLOCK, pr, q, k, v, o, lse, ix, stream, "sdattn_forward_block_sparse_split");
+}
+
 sdattn_status sdattn_select_columns_workspace(const sdattn_problem* p, int32_t kcol, size_t* ws_bytes) {
     if (ws_bytes == nullptr) return fail(SDATTN_ERR_NULL, "ws_bytes must be non-NULL");
     Problem pr;

@@ -112,6 +112,82 @@ __global__ __launch_bounds__(256) void block_plan_kernel(const int32_t* __restri
     }
 }
 
+// Split plan (layout in launch.h), one 1024-thread workgroup after the
+// dispatch plan has been written into the workspace.  Each thread takes a
+// contiguous range of rows; an exclusive scan over the threads of (split
+// rows, partial slots) gives every split row its entry in the split-row list
+// and its c consecutive partial slots, in row order; chunk k of the row is
+// the workgroup at its slot, so the items' chunk section is the slot list.
+constexpr int kSplitThreads = 1024;
+constexpr int kPackBits = 24;  // per-field totals stay below 2 slots <= 2^12
+
+__global__ __launch_bounds__(kSplitThreads) void split_plan_kernel(const int32_t* __restrict__ row_ptr, int rows,
+                                                                 int slots, int32_t* __restrict__ ws) {
+    __shared__ unsigned long long scan[kSplitThreads];
+    const int tid = threadIdx.x;
+    const long long nnz = static_cast<long long>(row_ptr[rows]) - row_ptr[0];
+    const long long tl = max(static_cast<long long>(kSplitMinBlocks), (nnz + slots - 1) / slots);
+    const int T = static_cast<int>(min(tl, static_cast<long long>(INT32_MAX)));
+    auto chunks = [&](int r) -> int {
+        const long long ne = static_cast<long long>(row_ptr[r + 1]) - row_ptr[r];
+        if (ne <= T) return 1;
+        return static_cast<int>(min(static_cast<long long>(kSplitMaxChunks), (ne + T - 1) / T));
+    };
+    constexpr unsigned long long kMask = (1ull << kPackBits) - 1;
+    const int per = (rows + kSplitThreads - 1) / kSplitThreads;
+    const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
+    unsigned long long n = 0, sl = 0;
+    for (int r = r0; r < r1; ++r) {
+        const int c = chunks(r);
+        if (c > 1) {
+            n += 1;
+            sl += c;
+        }
+    }
+    const unsigned long long mine = n | (sl << kPackBits);
+    scan[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kSplitThreads; off <<= 1) {  // inclusive scan (the packed fields never carry)
+        const unsigned long long add = tid >= off ? scan[tid - off] : 0ull;
+        __syncthreads();
+        scan[tid] += add;
+        __syncthreads();
+    }
+    const unsigned long long total = scan[kSplitThreads - 1];
+    const unsigned long long ex = scan[tid] - mine;
+    int pn = static_cast<int>(ex & kMask), ps = static_cast<int>((ex >> kPackBits) & kMask);
+    int32_t* slot_base = ws + split_slot_base_offset(rows, slots);
+    int32_t* split_rows = ws + split_rows_offset(rows, slots);
+    for (int r = r0; r < r1; ++r) {
+        const int c = chunks(r);
+        if (c > 1) {
+            const int head = r | ((c - 1) << kSplitCountShift);
+            slot_base[r] = ps;
+            split_rows[pn] = head;
+            for (int k = 0; k < c; ++k) ws[ps + k] = head | (k << kSplitChunkShift);
+            pn += 1;
+            ps += c;
+        } else {
+            slot_base[r] = -1;
+        }
+    }
+    const int CS = static_cast<int>((total >> kPackBits) & kMask);  // chunks of the split rows (< 2 slots)
+    const int C8 = (CS + 7) & ~7;  // the plan part starts on a multiple of 8: each entry keeps its XCD
+    for (int i = CS + tid; i < C8; i += kSplitThreads) ws[i] = -1;
+    const int32_t* plan = ws + split_plan_offset(rows, slots);
+    for (int i = tid; i < rows; i += kSplitThreads) {
+        const int r = plan[i];
+        ws[C8 + i] = chunks(r) > 1 ? -1 : r;
+    }
+    const int items = static_cast<int>(split_items(rows, slots));
+    for (int i = C8 + rows + tid; i < items; i += kSplitThreads) ws[i] = -1;
+    if (tid == 0) {
+        int32_t* counts = ws + split_counts_offset(rows, slots);
+        counts[0] = static_cast<int>(total & kMask);
+        counts[1] = T;
+    }
+}
+
 }  // namespace
 
 int block_plan_segment_rows(int block_q, int nqt) {
@@ -137,6 +213,15 @@ hipError_t launch_block_plan(int rows, int nqt, int block_q, const int32_t* row_
     int np2 = 1;
     while (np2 < seg_rows) np2 <<= 1;
     hipLaunchKernelGGL(block_plan_kernel, dim3(n_seg), dim3(256), 0, st, row_ptr, nqt, seg_rows, n_seg, np2, plan);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_plan(int rows, int nqt, int block_q, const int32_t* row_ptr, int32_t* ws, hipStream_t st) {
+    if (rows <= 0) return hipSuccess;
+    const int slots = split_slots(block_q);
+    hipError_t e = launch_block_plan(rows, nqt, block_q, row_ptr, ws + split_plan_offset(rows, slots), st);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(kSplitThreads), 0, st, row_ptr, rows, slots, ws);
     return hipGetLastError();
 }
 

@@ -48,11 +48,13 @@ struct FlashParams {
     float* lse;
     const int32_t* row_ptr;
     const int32_t* col_idx;
-    const int32_t* order;  // block form: block row of each workgroup id (a dispatch plan), or nullptr
+    const int32_t* order;  // block form: block row of each workgroup id (a dispatch plan), a split
+                           // plan's workspace (split instantiations), or nullptr
     int Hq, Hkv, L, group, n_qtiles, n_items, block_k;
     union {
-        int kcol;     // column forms: kept columns per kv head
-        int n_pairs;  // block form: (batch, head) pairs of the balanced order (0: the xcd_group order)
+        int kcol;         // column forms: kept columns per kv head
+        int n_pairs;      // block form without a plan: (batch, head) pairs of the balanced order (0: the xcd_group order)
+        int split_slots;  // block form over a split plan: its slot count
     };
     int xcd_group;
     float c;      // scale * log2(e)
@@ -148,11 +150,14 @@ __device__ __forceinline__ int balanced_block_item(int id, int n_qtiles, int n_p
     return pair * n_qtiles + qt;
 }
 
-template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST>
+template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false>
 __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // KT keys per tile (32 or 64), NST LDS stages (tiles in flight: NST - 1);
     // the pipelined pass over 32-key tiles uses a ring of NK K slots and NV V
-    // slots instead (K fetched NK - 1 units ahead, V NV - 1)
+    // slots instead (K fetched NK - 1 units ahead, V NV - 1).  SPLIT: block
+    // form over a split plan (p.order is its workspace, launch.h): a
+    // workgroup may compute one chunk of a row's kept blocks and write a
+    // partial result that split_merge_kernel combines.
     constexpr int KB = KT / 32;             // 32-key MFMA blocks per tile
     constexpr int T = NW * 64;
     constexpr int DK = D / 16;
@@ -188,7 +193,15 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     const int hl = lane >> 5;
 
     int item;
-    if (MODE == MODE_BLOCK && p.order != nullptr) {
+    int chunk = 0, n_chunks = 1;  // split plan: this workgroup's chunk of its row
+    if constexpr (SPLIT) {
+        const int raw = ((const cint32*)(p.order))[blockIdx.x];
+        if (raw < 0) return;  // idle entry
+        item = raw & ((1 << kSplitRowBits) - 1);
+        chunk = (raw >> kSplitChunkShift) & (kSplitMaxChunks - 1);
+        n_chunks = ((raw >> kSplitCountShift) & (kSplitMaxChunks - 1)) + 1;
+        if (item >= p.n_items) return;
+    } else if (MODE == MODE_BLOCK && p.order != nullptr) {
         item = ((const cint32*)(p.order))[blockIdx.x];
         if (static_cast<unsigned>(item) >= static_cast<unsigned>(p.n_items)) return;  // not a plan: nothing read
     }
@@ -244,6 +257,15 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
         const cint32* rp = (const cint32*)(p.row_ptr);
         e0 = rp[r];
         ne = rp[r + 1] - e0;
+        if constexpr (SPLIT) {
+            // chunk k of c: kept blocks [floor(k ne / c), floor((k + 1) ne / c)) of the row
+            if (n_chunks > 1) {
+                const int a = static_cast<int>(static_cast<long long>(ne) * chunk / n_chunks);
+                const int z = static_cast<int>(static_cast<long long>(ne) * (chunk + 1) / n_chunks);
+                e0 += a;
+                ne = z - a;
+            }
+        }
         // block_k / KT tiles per kept key block (block_k in {64, 128}, KT in {32, 64})
         sub_shift = (p.block_k == 128 ? 1 : 0) + (KT == 32 ? 1 : 0);
         if constexpr (RING) {
@@ -955,6 +977,29 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     // ---- epilogue: normalise, stage through LDS, coalesced stores ----------
     const float lt = sum_with_half_swap(l_acc);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if constexpr (SPLIT) {
+        if (n_chunks > 1) {
+            // one chunk of a split row: O over the chunk, normalised, in the
+            // accumulator layout (16-byte unit (wave, db, rq) of lane `lane`),
+            // and the chunk's log-sum-exp per query, into its partial slot
+            const int rows = p.n_items, slots = p.split_slots;
+            const cint32* ws = (const cint32*)(p.order);
+            const int slot = ws[split_slot_base_offset(rows, slots) + item] + chunk;
+            constexpr int BQ = NW * 32;
+            float* part = reinterpret_cast<float*>(const_cast<int32_t*>(p.order) + split_partial_offset(rows, slots)) +
+                          static_cast<size_t>(slot) * BQ * (D + 1);
+#pragma unroll
+            for (int db = 0; db < ND; ++db)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const f32x4 val = {oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv, oacc[db][4 * rq + 2] * inv,
+                                       oacc[db][4 * rq + 3] * inv};
+                    reinterpret_cast<f32x4*>(part)[((wave * ND + db) * 4 + rq) * 64 + lane] = val;
+                }
+            if (hl == 0) part[BQ * D + wave * 32 + l32] = lt > 0.f ? m_ref * p.scale + __logf(lt) : -kInf;
+            return;
+        }
+    }
     // Each wave stages its own 32 rows; 16-byte unit u of row r sits at unit
     // u ^ (r mod UNITS), so the column-wise writes spread over the banks and
     // the row-wise reads stay conflict-free.
@@ -996,9 +1041,73 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     }
 }
 
-template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST>
-hipError_t launch_one(const FlashParams& fp, hipStream_t st) {
-    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE, NK, NV>), dim3(fp.n_items), dim3(NW * 64), 0, st, fp);
+// Merge of split rows (split plan, launch.h): workgroup s combines the c
+// chunks of the s-th split row.  Each thread takes the 16-byte units of the
+// accumulator layout that the forward's lane of the same wave and lane wrote
+// (query 32 wave + lane mod 32, channels 32 db + 8 rq + 4 (lane / 32) + [0, 4)),
+// weights chunk k by exp(lse_k - LSE), LSE = log sum_k exp(lse_k) (the
+// online-softmax merge of partial rows), and writes O in bf16 and LSE.
+struct MergeParams {
+    const int32_t* ws;
+    uint16_t* o;
+    float* lse;
+    int Hq, L, n_qtiles, rows, slots;
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void split_merge_kernel(MergeParams m) {
+    constexpr int ND = D / 32;
+    constexpr int BQ = NW * 32;
+    const int s = blockIdx.x;
+    const int32_t* ws = m.ws;
+    if (s >= ws[split_counts_offset(m.rows, m.slots)]) return;
+    const int raw = ws[split_rows_offset(m.rows, m.slots) + s];
+    const int row = raw & ((1 << kSplitRowBits) - 1);
+    const int c = ((raw >> kSplitCountShift) & (kSplitMaxChunks - 1)) + 1;
+    const int slot0 = ws[split_slot_base_offset(m.rows, m.slots) + row];
+    const float* part = reinterpret_cast<const float*>(ws + split_partial_offset(m.rows, m.slots)) +
+                        static_cast<size_t>(slot0) * BQ * (D + 1);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const int qq = wave * 32 + l32;
+    float lk[kSplitMaxChunks];
+    float mx = -kInf;
+#pragma unroll
+    for (int k = 0; k < kSplitMaxChunks; ++k) {
+        lk[k] = k < c ? part[static_cast<size_t>(k) * BQ * (D + 1) + BQ * D + qq] : -kInf;
+        mx = fmaxf(mx, lk[k]);
+    }
+    float w[kSplitMaxChunks];
+    float sum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSplitMaxChunks; ++k) {
+        w[k] = (k < c && lk[k] > -kInf) ? __expf(lk[k] - mx) : 0.f;
+        sum += w[k];
+    }
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    const int bh = row / m.n_qtiles, qt = row - bh * m.n_qtiles;
+    const int qi = qt * BQ + qq;
+    if (qi >= m.L) return;
+    uint16_t* orow = m.o + (static_cast<size_t>(bh) * m.L + qi) * D;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < c; ++k) {
+                const f32x4 v = reinterpret_cast<const f32x4*>(part + static_cast<size_t>(k) * BQ * (D + 1))
+                    [((wave * ND + db) * 4 + rq) * 64 + lane];
+                acc += v * (w[k] * inv);
+            }
+            const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * hl) = out;
+        }
+    if (m.lse != nullptr && hl == 0) m.lse[static_cast<size_t>(bh) * m.L + qi] = sum > 0.f ? mx + __logf(sum) : -kInf;
+}
+
+template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false>
+hipError_t launch_one(const FlashParams& fp, hipStream_t st, int grid) {
+    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE, NK, NV, SPLIT>), dim3(grid), dim3(NW * 64), 0, st, fp);
     return hipGetLastError();
 }
 
@@ -1027,15 +1136,37 @@ namespace {
 //   kRingV V slots (40 KiB at d = 128, four workgroups per CU).
 template <int D>
 hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st) {
+    const int g = fp.n_items;
     switch (mode) {
-        case MODE_DENSE: return launch_one<D, 8, 64, 2, MODE_DENSE>(fp, st);
-        case MODE_COLUMN: return launch_one<D, 8, 64, 2, MODE_COLUMN>(fp, st);
-        case MODE_COLUMN_PACKED: return launch_one<D, 8, 64, 2, MODE_COLUMN_PACKED>(fp, st);
+        case MODE_DENSE: return launch_one<D, 8, 64, 2, MODE_DENSE>(fp, st, g);
+        case MODE_COLUMN: return launch_one<D, 8, 64, 2, MODE_COLUMN>(fp, st, g);
+        case MODE_COLUMN_PACKED: return launch_one<D, 8, 64, 2, MODE_COLUMN_PACKED>(fp, st, g);
         case MODE_BLOCK:
-            if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK, kRingK, kRingV>(fp, st);
-            return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st);
+            if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK, kRingK, kRingV>(fp, st, g);
+            return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st, g);
     }
     return hipErrorInvalidValue;
+}
+
+// Block form over a split plan: the forward over its items (rows + 2 slots
+// workgroups), then the merge of the split rows (slots workgroups, the idle
+// ones return at once).
+template <int D>
+hipError_t launch_split_d(const FlashParams& fp, int bq, hipStream_t st) {
+    const int slots = fp.split_slots;
+    const int grid = static_cast<int>(split_items(fp.n_items, slots));
+    MergeParams m{fp.order, fp.o, fp.lse, fp.Hq, fp.L, fp.n_qtiles, fp.n_items, slots};
+    hipError_t e;
+    if (bq == 64) {
+        e = launch_one<D, 2, 32, 2, MODE_BLOCK, kRingK, kRingV, true>(fp, st, grid);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((split_merge_kernel<D, 2>), dim3(slots), dim3(128), 0, st, m);
+    } else {
+        e = launch_one<D, 4, 64, 2, MODE_BLOCK, 2, 2, true>(fp, st, grid);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((split_merge_kernel<D, 4>), dim3(slots), dim3(256), 0, st, m);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1052,7 +1183,7 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.lse = lse;
     fp.row_ptr = ix.row_ptr;
     fp.col_idx = ix.col_idx;
-    fp.order = mode == MODE_BLOCK ? ix.order : nullptr;
+    fp.order = mode == MODE_BLOCK ? (ix.split != nullptr ? ix.split : ix.order) : nullptr;
     fp.Hq = s.Hq;
     fp.Hkv = s.Hkv;
     fp.L = s.L;
@@ -1082,6 +1213,10 @@ hipError_t launch_flash_bf16(AttnMode mode, const AttnShape& s, const void* q, c
     fp.scale = s.scale;
     fp.c = s.scale * kLog2e;
     if (fp.n_items == 0) return hipSuccess;
+    if (mode == MODE_BLOCK && ix.split != nullptr) {
+        fp.split_slots = split_slots(bq);
+        return s.D == 128 ? launch_split_d<128>(fp, bq, st) : launch_split_d<64>(fp, bq, st);
+    }
     return s.D == 128 ? launch_d<128>(mode, fp, bq, st) : launch_d<64>(mode, fp, bq, st);
 }
 

@@ -23,6 +23,7 @@ struct SparseIndex {
     const int32_t* col_idx = nullptr;     // MODE_BLOCK (CSR) / MODE_COLUMN ([B][Hkv][kcol])
     int kcol = 0;                         // MODE_COLUMN, MODE_COLUMN_PACKED
     const int32_t* order = nullptr;       // MODE_BLOCK: dispatch plan (launch_block_plan), or computed in the kernel
+    int32_t* split = nullptr;             // MODE_BLOCK: a split plan's workspace (launch_split_plan) instead of `order`
 };
 
 // Flash-style forward; bf16 inputs (MFMA) or f32 inputs (VALU).
@@ -40,6 +41,48 @@ int block_rows_per_cu(int block_q);
 // equal share of the kept blocks (see block_plan.hip).  rows = B*Hq*nqt.
 int block_plan_segment_rows(int block_q, int nqt);
 hipError_t launch_block_plan(int rows, int nqt, int block_q, const int32_t* row_ptr, int32_t* plan, hipStream_t st);
+
+// Split plan of the block-sparse forward.  Rows with more kept blocks than
+// one workgroup slot's share of the launch (T = max(kSplitMinBlocks,
+// ceil(nnz / slots)), slots = the workgroups the GPU holds at once) are cut
+// into c = min(8, ceil(ne / T)) chunks of consecutive kept blocks; every
+// chunk is a workgroup of the forward that writes a partial result (O
+// normalised over its chunk, fp32, and its log-sum-exp), and a merge kernel
+// combines a row's chunks by their log-sum-exps.  One workspace holds it
+// all, in int32 units from its start:
+//   items      [rows + 2 slots]  workgroup id -> item: -1 (idle) or
+//                                row | chunk << 24 | (c - 1) << 27
+//   slot_base  [rows]            first partial slot of a split row (-1: not cut)
+//   counts     [2]               split rows S, chunk length T
+//   split_rows [slots]           the S split rows (item encoding, chunk 0)
+//   plan       [rows]            the dispatch plan the items are built from
+// then, from the next 256-byte boundary, 2 slots partial slots of
+// block_q * (D + 1) floats each (O in the MFMA accumulator layout, then the
+// log-sum-exps).  Items: every chunk of the split rows first, chunk k of row
+// r at its partial slot slot_base[r] + k (consecutive ids: the chunks of a
+// row go to different XCDs), idle entries up to a multiple of 8, then the
+// dispatch plan with the split rows idle (so each remaining entry keeps its
+// XCD), then idle entries.  Needs rows < 2^24.
+constexpr int kSplitCUs = 256;        // MI355X compute units
+constexpr int kSplitMinBlocks = 4;    // rows of at most this many kept blocks stay whole
+constexpr int kSplitRowBits = 24;
+constexpr int kSplitChunkShift = 24;  // 3 bits
+constexpr int kSplitCountShift = 27;  // 3 bits: chunks - 1
+constexpr int kSplitMaxChunks = 8;
+inline int split_slots(int block_q) { return kSplitCUs * block_rows_per_cu(block_q); }
+__host__ __device__ inline size_t split_items(int rows, int slots) { return static_cast<size_t>(rows) + 2 * slots; }
+__host__ __device__ inline size_t split_slot_base_offset(int rows, int slots) { return split_items(rows, slots); }
+__host__ __device__ inline size_t split_counts_offset(int rows, int slots) { return split_items(rows, slots) + rows; }
+__host__ __device__ inline size_t split_rows_offset(int rows, int slots) { return split_counts_offset(rows, slots) + 2; }
+__host__ __device__ inline size_t split_plan_offset(int rows, int slots) { return split_rows_offset(rows, slots) + slots; }
+__host__ __device__ inline size_t split_partial_offset(int rows, int slots) {
+    return (split_plan_offset(rows, slots) + rows + 63) / 64 * 64;  // int32 units, 256-byte aligned
+}
+inline size_t split_ws_bytes(int rows, int block_q, int D) {
+    const int slots = split_slots(block_q);
+    return split_partial_offset(rows, slots) * 4 + 2 * static_cast<size_t>(slots) * block_q * (D + 1) * 4;
+}
+hipError_t launch_split_plan(int rows, int nqt, int block_q, const int32_t* row_ptr, int32_t* ws, hipStream_t st);
 
 // Block selection.  Workspace layout is defined by select_blocks_ws_layout.
 struct BlockSelectWs {

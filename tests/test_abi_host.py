@@ -23,7 +23,7 @@ def _declared():
 
 def test_every_declared_symbol_is_exported():
     names = _declared()
-    assert len(names) == 29
+    assert len(names) == 32
     out = subprocess.run(["nm", "-D", "--defined-only", sd.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(sdattn_\w+)", out))
     assert set(names) == exported  # nothing missing, nothing extra
@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 5
+    assert sd.sdattn_abi_version() == sd.SDATTN_ABI_VERSION == 6
     hdr = open(os.path.join(ROOT, "include", "sdattn.h")).read()
     assert f"#define SDATTN_ABI_VERSION {sd.SDATTN_ABI_VERSION}" in hdr
     for i, name in enumerate(sd.STATUS_NAMES):
@@ -112,6 +112,34 @@ def test_sparse_and_column_validation():
                                                    None) == 8
     assert lib.sdattn_forward_block_sparse_planned(ctypes.byref(p), BAD, BAD, BAD, 64, 64, BAD, None, BAD, BAD, None,
                                                    None) == 1
+    # split plan: block sizes, NULL ws_bytes, short or NULL workspace, NULL row_ptr / col_idx, L == 0 a no-op,
+    # at most 2^24 - 1 block rows
+    with pytest.raises(sd.SdattnError, match="UNSUPPORTED"):
+        sd.sdattn_block_split_workspace(p, 96, 128)
+    assert lib.sdattn_block_split_workspace(ctypes.byref(p), 64, 64, None) == 1
+    wsb = sd.sdattn_block_split_workspace(p, 64, 64)
+    rows = 28 * 256
+    assert wsb >= (3 * rows + 2 * 1024 + 2) * 4 + 2 * 1024 * 64 * 129 * 4
+    assert sd.sdattn_block_split_workspace(p, 128, 64) >= 2 * 512 * 128 * 129 * 4
+    assert lib.sdattn_block_split_plan(ctypes.byref(p), 64, 64, None, BAD, wsb, None) == 1
+    assert lib.sdattn_block_split_plan(ctypes.byref(p), 64, 64, BAD, BAD, wsb - 4, None) == 5
+    assert lib.sdattn_block_split_plan(ctypes.byref(p), 64, 64, BAD, None, wsb, None) == 5
+    assert lib.sdattn_block_split_plan(ctypes.byref(p), 64, 96, BAD, BAD, wsb, None) == 8
+    assert lib.sdattn_forward_block_sparse_split(ctypes.byref(p), BAD, BAD, BAD, 64, 64, BAD, None, BAD, wsb, BAD,
+                                                 None, None) == 1
+    assert lib.sdattn_forward_block_sparse_split(ctypes.byref(p), BAD, BAD, BAD, 64, 64, BAD, BAD, BAD, wsb - 4, BAD,
+                                                 None, None) == 5
+    assert lib.sdattn_forward_block_sparse_split(ctypes.byref(p), BAD, BAD, BAD, 64, 64, BAD, BAD, BAD, wsb, None,
+                                                 None, None) == 1
+    assert lib.sdattn_forward_block_sparse_split(ctypes.byref(p), BAD, BAD, BAD, 128, 96, BAD, BAD, BAD, wsb, BAD,
+                                                 None, None) == 8
+    assert sd.sdattn_block_split_workspace(p0, 64, 64) == 0
+    assert lib.sdattn_block_split_plan(ctypes.byref(p0), 64, 64, None, None, 0, None) == 0
+    assert lib.sdattn_forward_block_sparse_split(ctypes.byref(p0), None, None, None, 64, 64, None, None, None, 0,
+                                                 None, None, None) == 0
+    big = sd.problem(8, 64, 64, 1 << 21, 128, "bf16")
+    with pytest.raises(sd.SdattnError, match="SHAPE"):
+        sd.sdattn_block_split_workspace(big, 64, 64)
     assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, BAD, 0, BAD, None, None) == 4
     assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, BAD, 16385, BAD, None, None) == 4
     assert lib.sdattn_forward_column_sparse(ctypes.byref(p), BAD, BAD, BAD, None, 492, BAD, None, None) == 1
