@@ -425,6 +425,10 @@ typedef struct {
     double column_keep_frac;        /* columns only */
     int32_t probe_interval;         /* 0 = no probes; blocks only (ABI 2) */
     double min_overlap;             /* adoption threshold of a probe (ABI 2) */
+    int32_t split_rows;             /* blocks only: 1 = sparse steps run over a split plan
+                                       (sdattn_forward_block_sparse_split: rows far longer
+                                       than the rest are cut and merged), 0 = over the
+                                       dispatch plan alone (ABI 6) */
 } sdattn_schedule_desc;
 
 typedef struct sdattn_schedule sdattn_schedule; /* opaque */

@@ -57,7 +57,7 @@ class ScheduleDesc(ctypes.Structure):
                 ("n_refresh_steps", ctypes.c_int32), ("refresh_dense", ctypes.c_int32), ("sel", ctypes.c_int),
                 ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32), ("budget", Budget),
                 ("column_keep_frac", ctypes.c_double), ("probe_interval", ctypes.c_int32),
-                ("min_overlap", ctypes.c_double)]
+                ("min_overlap", ctypes.c_double), ("split_rows", ctypes.c_int32)]
 
 
 class LosaProblem(ctypes.Structure):
@@ -357,13 +357,13 @@ def sdattn_mask_overlap(rows, row_ptr_a, col_idx_a, row_ptr_b, col_idx_b, counts
 
 def schedule_desc(total_steps, dense_steps, select_step, refresh_interval=0, refresh_steps=(), refresh_dense=False,
                   sel=SDATTN_SEL_BLOCKS, block_q=128, block_k=128, budget=None, column_keep_frac=0.0,
-                  probe_interval=0, min_overlap=0.0):
+                  probe_interval=0, min_overlap=0.0, split_rows=False):
     arr = (ctypes.c_int32 * max(1, len(refresh_steps)))(*refresh_steps)
     d = ScheduleDesc(total_steps, dense_steps, select_step, refresh_interval,
                      ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)) if refresh_steps else None,
                      len(refresh_steps), int(bool(refresh_dense)), sel, block_q, block_k,
                      budget if budget is not None else topk_budget(1.0), column_keep_frac, probe_interval,
-                     min_overlap)
+                     min_overlap, int(bool(split_rows)))
     d._keep = arr  # the C side copies the array at create; keep it alive until then
     return d
 

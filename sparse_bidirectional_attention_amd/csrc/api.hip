@@ -432,6 +432,18 @@ sdattn_status be_block_plan(void*, const sdattn_problem* p, int32_t bq, int32_t 
                             void* st) {
     return sdattn_block_plan(p, bq, bk, rp, plan, st);
 }
+sdattn_status be_block_split_ws(void*, const sdattn_problem* p, int32_t bq, int32_t bk, size_t* ws) {
+    return sdattn_block_split_workspace(p, bq, bk, ws);
+}
+sdattn_status be_block_split_plan(void*, const sdattn_problem* p, int32_t bq, int32_t bk, const int32_t* rp, void* ws,
+                                  size_t wsb, void* st) {
+    return sdattn_block_split_plan(p, bq, bk, rp, ws, wsb, st);
+}
+sdattn_status be_block_sparse_split(void*, const sdattn_problem* p, const void* q, const void* k, const void* v,
+                                    int32_t bq, int32_t bk, const int32_t* rp, const int32_t* ci, void* ws, size_t wsb,
+                                    void* o, float* lse, void* st) {
+    return sdattn_forward_block_sparse_split(p, q, k, v, bq, bk, rp, ci, ws, wsb, o, lse, st);
+}
 sdattn_status be_select_columns(void*, const sdattn_problem* p, const void* q, const void* k, const float* lse,
                                 int32_t kcol, int32_t* ci, void* ws, size_t wsb, void* st) {
     return sdattn_select_columns(p, q, k, lse, kcol, ci, nullptr, ws, wsb, st);
@@ -502,7 +514,8 @@ sdattn_status be_column_packed(void*, const sdattn_problem* p, const void* q, co
 const Backend kHipBackend = {nullptr,          be_dense,       be_select_blocks, be_block_sparse, be_select_columns,
                              be_column_sparse, be_ws_blocks,   be_ws_columns,    be_alloc,        be_release,
                              be_overlap,       be_probe_adopt, be_probe_init,    be_probe_read,   be_select_blocks_exact,
-                             be_ws_blocks_exact, be_gather_columns, be_column_packed, be_block_plan};
+                             be_ws_blocks_exact, be_gather_columns, be_column_packed, be_block_plan,
+                             be_block_split_ws, be_block_split_plan, be_block_sparse_split};
 
 }  // namespace
 

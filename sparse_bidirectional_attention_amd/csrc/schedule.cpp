@@ -28,7 +28,8 @@ struct sdattn_schedule {
     // pattern buffers (device)
     int32_t* row_ptr[2] = {nullptr, nullptr};
     int32_t* col_idx[2] = {nullptr, nullptr};
-    int32_t* plan[2] = {nullptr, nullptr};  // block patterns: dispatch plan of each buffer's forward
+    int32_t* plan[2] = {nullptr, nullptr};  // block patterns: dispatch plan (or split plan) of each buffer's forward
+    size_t plan_bytes = 0;
     int64_t nnz_cap = 0;
     int32_t kcol = 0;
     int active = -1;  // -1: no pattern yet
@@ -46,6 +47,30 @@ struct sdattn_schedule {
 };
 
 namespace sdattn {
+
+namespace {
+
+// The plan of pattern buffer i, and the block-sparse forward over it: the
+// dispatch plan, or the split plan when the descriptor asks for split rows.
+sdattn_status plan_pattern(sdattn_schedule* s, int i, void* stream) {
+    const Backend& be = s->be;
+    if (s->desc.split_rows)
+        return be.block_split_plan(be.ctx, &s->prob, s->desc.block_q, s->desc.block_k, s->row_ptr[i], s->plan[i],
+                                   s->plan_bytes, stream);
+    return be.block_plan(be.ctx, &s->prob, s->desc.block_q, s->desc.block_k, s->row_ptr[i], s->plan[i], stream);
+}
+
+sdattn_status sparse_over(sdattn_schedule* s, int i, const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* stream) {
+    const Backend& be = s->be;
+    if (s->desc.split_rows)
+        return be.block_sparse_split(be.ctx, &s->prob, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[i],
+                                     s->col_idx[i], s->plan[i], s->plan_bytes, o, lse, stream);
+    return be.block_sparse(be.ctx, &s->prob, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[i], s->col_idx[i],
+                           s->plan[i], o, lse, stream);
+}
+
+}  // namespace
 
 sdattn_action schedule_action_of(const sdattn_schedule_desc& d, int32_t t) {
     bool in_s = t == d.select_step;
@@ -100,6 +125,9 @@ sdattn_status check_desc(const Problem& pr, const sdattn_schedule_desc* d) {
             return fail(SDATTN_ERR_UNSUPPORTED, "probes are for block patterns (column selection needs a dense pass)");
     }
     if (d->probe_interval < 0) return fail(SDATTN_ERR_SHAPE, "probe_interval must be >= 0");
+    if (d->split_rows != 0 && d->split_rows != 1) return fail(SDATTN_ERR_SHAPE, "split_rows must be 0 or 1");
+    if (d->split_rows && d->sel == SDATTN_SEL_COLUMNS)
+        return fail(SDATTN_ERR_UNSUPPORTED, "split_rows is for block patterns");
     if (d->probe_interval > 0 && !(d->min_overlap >= 0.0 && d->min_overlap <= 1.0))
         return fail(SDATTN_ERR_BUDGET, "min_overlap must be in [0, 1]");
     (void)pr;
@@ -153,6 +181,13 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         }
         s->nnz_cap = std::max<int64_t>(max_nnz, 1);
         s->rows = plan.rows;
+        s->plan_bytes = static_cast<size_t>(std::max<int64_t>(s->rows, 1)) * sizeof(int32_t);
+        if (desc->split_rows) {
+            size_t split_bytes = 0;
+            st = s->be.block_split_ws(s->be.ctx, p, desc->block_q, desc->block_k, &split_bytes);
+            if (st != SDATTN_OK) return cleanup_fail(st);
+            s->plan_bytes = std::max(split_bytes, s->plan_bytes);
+        }
         rp_bytes = static_cast<size_t>(plan.rows + 1) * sizeof(int32_t);
         ci_bytes = static_cast<size_t>(s->nnz_cap) * sizeof(int32_t);
     } else {
@@ -174,8 +209,7 @@ sdattn_status sdattn_schedule_create(const sdattn_problem* p, const sdattn_sched
         if (rp_bytes) {
             st = s->be.alloc(s->be.ctx, rp_bytes, reinterpret_cast<void**>(&s->row_ptr[i]));
             if (st != SDATTN_OK) return cleanup_fail(st);
-            const size_t plan_bytes = static_cast<size_t>(std::max<int64_t>(s->rows, 1)) * sizeof(int32_t);
-            st = s->be.alloc(s->be.ctx, plan_bytes, reinterpret_cast<void**>(&s->plan[i]));
+            st = s->be.alloc(s->be.ctx, s->plan_bytes, reinterpret_cast<void**>(&s->plan[i]));
             if (st != SDATTN_OK) return cleanup_fail(st);
         }
         st = s->be.alloc(s->be.ctx, ci_bytes, reinterpret_cast<void**>(&s->col_idx[i]));
@@ -225,16 +259,14 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
                                                 s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes,
                                                 stream);
                 if (st == SDATTN_OK)
-                    st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[next], s->plan[next],
-                                       stream);
+                    st = plan_pattern(s, next, stream);
             } else if (blocks) {
                 st = be.dense(be.ctx, p, q, k, v, o, lse, stream);
                 if (st == SDATTN_OK)
                     st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
                                           s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
                 if (st == SDATTN_OK)
-                    st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[next], s->plan[next],
-                                       stream);
+                    st = plan_pattern(s, next, stream);
             } else {
                 float* l = lse != nullptr ? lse : s->lse;
                 st = be.dense(be.ctx, p, q, k, v, o, l, stream);
@@ -252,11 +284,9 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
             st = be.select_blocks(be.ctx, p, q, k, s->desc.block_q, s->desc.block_k, &s->desc.budget,
                                   s->row_ptr[next], s->col_idx[next], s->nnz_cap, s->ws, s->ws_bytes, stream);
             if (st == SDATTN_OK)
-                st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[next], s->plan[next],
-                                   stream);
+                st = plan_pattern(s, next, stream);
             if (st == SDATTN_OK)
-                st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[next],
-                                     s->col_idx[next], s->plan[next], o, lse, stream);
+                st = sparse_over(s, next, q, k, v, o, lse, stream);
             if (st == SDATTN_OK) {
                 s->active = next;
                 s->last_select = step;
@@ -284,18 +314,16 @@ sdattn_status sdattn_schedule_step(sdattn_schedule* s, int32_t step, const void*
                                     s->desc.min_overlap, s->nnz_cap, stream);
             // the cached pattern may have been replaced: plan it again
             if (st == SDATTN_OK)
-                st = be.block_plan(be.ctx, p, s->desc.block_q, s->desc.block_k, s->row_ptr[a], s->plan[a], stream);
+                st = plan_pattern(s, a, stream);
             if (st == SDATTN_OK)
-                st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[a],
-                                     s->col_idx[a], s->plan[a], o, lse, stream);
+                st = sparse_over(s, a, q, k, v, o, lse, stream);
             if (st == SDATTN_OK) s->n_probes += 1;
             return st;
         }
         case SDATTN_ACT_SPARSE:
             if (s->active < 0) return fail(SDATTN_ERR_STATE, "sparse step before any pattern was selected");
             if (blocks)
-                st = be.block_sparse(be.ctx, p, q, k, v, s->desc.block_q, s->desc.block_k, s->row_ptr[s->active],
-                                     s->col_idx[s->active], s->plan[s->active], o, lse, stream);
+                st = sparse_over(s, s->active, q, k, v, o, lse, stream);
             else {
                 // the kept columns' K/V rows are gathered once, then streamed
                 // by every query tile of the group

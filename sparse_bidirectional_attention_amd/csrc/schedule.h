@@ -53,6 +53,13 @@ struct Backend {
     // dispatch plan of the block-sparse forward for a pattern's row_ptr
     sdattn_status (*block_plan)(void* ctx, const sdattn_problem*, int32_t bq, int32_t bk, const int32_t* row_ptr,
                                 int32_t* plan, void* stream);
+    // split rows: workspace bytes, the split plan of a pattern, the forward over it
+    sdattn_status (*block_split_ws)(void* ctx, const sdattn_problem*, int32_t bq, int32_t bk, size_t* ws_bytes);
+    sdattn_status (*block_split_plan)(void* ctx, const sdattn_problem*, int32_t bq, int32_t bk,
+                                      const int32_t* row_ptr, void* ws, size_t ws_bytes, void* stream);
+    sdattn_status (*block_sparse_split)(void* ctx, const sdattn_problem*, const void* q, const void* k, const void* v,
+                                        int32_t bq, int32_t bk, const int32_t* row_ptr, const int32_t* col_idx,
+                                        void* ws, size_t ws_bytes, void* o, float* lse, void* stream);
 };
 
 // The backend used by sdattn_schedule_create (defined by the library build

@@ -57,6 +57,21 @@ sdattn_status f_block_plan(void*, const sdattn_problem*, int32_t bq, int32_t bk,
     return record("block_plan rp=" + ptr(rp) + " plan=" + ptr(plan) + " bq=" + std::to_string(bq) +
                   " bk=" + std::to_string(bk));
 }
+sdattn_status f_block_split_ws(void*, const sdattn_problem*, int32_t, int32_t, size_t* ws) {
+    *ws = 1 << 20;
+    return SDATTN_OK;
+}
+sdattn_status f_block_split_plan(void*, const sdattn_problem*, int32_t bq, int32_t bk, const int32_t* rp, void* ws,
+                                 size_t wsb, void*) {
+    return record("block_split_plan rp=" + ptr(rp) + " ws=" + ptr(ws) + " bytes=" + std::to_string(wsb) +
+                  " bq=" + std::to_string(bq) + " bk=" + std::to_string(bk));
+}
+sdattn_status f_block_sparse_split(void*, const sdattn_problem*, const void*, const void*, const void*, int32_t,
+                                   int32_t, const int32_t* rp, const int32_t* ci, void* ws, size_t wsb, void* o, float*,
+                                   void*) {
+    return record("block_sparse_split rp=" + ptr(rp) + " ci=" + ptr(ci) + " ws=" + ptr(ws) + " bytes=" +
+                  std::to_string(wsb) + " o=" + ptr(o));
+}
 sdattn_status f_select_columns(void*, const sdattn_problem*, const void*, const void*, const float* lse, int32_t kcol,
                                int32_t* ci, void*, size_t, void*) {
     return record("select_columns lse=" + ptr(lse) + " ci=" + ptr(ci) + " kcol=" + std::to_string(kcol));
@@ -144,7 +159,8 @@ sdattn_status f_column_packed(void*, const sdattn_problem*, const void*, const v
 const sdattn::Backend kFake = {nullptr,          f_dense,          f_select_blocks, f_block_sparse, f_select_columns,
                                f_column_sparse,  f_ws_blocks,      f_ws_columns,    f_alloc,        f_release,
                                f_overlap,        f_probe_adopt,    f_probe_init,    f_probe_read,   f_select_blocks_exact,
-                               f_ws_blocks_exact, f_gather_columns, f_column_packed, f_block_plan};
+                               f_ws_blocks_exact, f_gather_columns, f_column_packed, f_block_plan,
+                               f_block_split_ws, f_block_split_plan, f_block_sparse_split};
 
 }  // namespace
 

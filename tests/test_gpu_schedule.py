@@ -37,20 +37,20 @@ def _d2h(ptr, n, dtype=np.int32):
     return out
 
 
-def _desc(w):
+def _desc(w, split_rows=False):
     sel = sd.SEL_KINDS[w.selector]
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
                             w.refresh_dense, sel, w.block, w.block, budget, w.column_keep_frac,
-                            w.probe_interval, w.min_overlap)
+                            w.probe_interval, w.min_overlap, split_rows)
 
 
-def _run_and_check(w):
+def _run_and_check(w, split_rows=False):
     base = make_base(w)
     p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
     acts_ref = oracle.schedule_actions(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval,
                                        w.refresh_steps, w.refresh_dense)
-    h = sd.sdattn_schedule_create(p, _desc(w))
+    h = sd.sdattn_schedule_create(p, _desc(w, split_rows))
     nqb = -(-w.seq_len // w.block)
     rows = w.batch * w.q_heads * nqb
     kcol = oracle.count_from_fraction(w.column_keep_frac, w.seq_len) if w.selector == "columns" else 0
@@ -118,6 +118,18 @@ def test_small_mass_refresh_schedule_bf16():
                max_mean_density=0.3)
     say("schedule mass+cap scaled L=1024 T=7")
     _, stats, last, _ = _run_and_check(w)
+    assert stats["SELECT_SPARSE"] == 2 and last == 6
+
+
+def test_small_uncapped_mass_schedule_with_split_rows_bf16():
+    """A mass budget with no cap (head-adaptive: the heads without planted
+    structure keep most blocks, the others few) and split rows: the long rows
+    are cut and merged, and every step still matches the oracle under the
+    pattern in force."""
+    w = scaled(WORKLOADS["llada8b_8k"], seq_len=1024, q_heads=4, kv_heads=4, total_steps=7, refresh_interval=3,
+               max_mean_density=1.0)
+    say("schedule uncapped mass, split rows, scaled L=1024 T=7")
+    _, stats, last, _ = _run_and_check(w, split_rows=True)
     assert stats["SELECT_SPARSE"] == 2 and last == 6
 
 

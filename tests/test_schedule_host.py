@@ -101,6 +101,51 @@ def test_random_schedules_match_oracle(fake):
     assert fake.sdattn_fake_live_allocs() == 0
 
 
+def test_split_rows_schedule_runs_every_sparse_step_over_the_split_plan(fake):
+    """With split_rows, every selection is followed by the split plan of its
+    row_ptr, into that buffer's workspace, and every sparse step runs the
+    split forward over the most recent one; the dispatch-plan calls are not
+    made.  split_rows must be 0 or 1, and is refused for column patterns."""
+    w = WORKLOADS["llada8b_8k"]
+    d = _desc_of(w)
+    d.split_rows = 1
+    h = _create(fake, _prob_of(w), d)
+    fake.sdattn_fake_reset(-1, 0)
+    try:
+        for t in range(w.total_steps):
+            assert _step(fake, h, t) == 0
+        log = _log(fake)
+        assert not any(l.startswith(("block_plan", "block_sparse ")) for l in log)
+        cur = ws = None
+        n_sparse, wss = 0, []
+        for i, l in enumerate(log):
+            if l.startswith("select_blocks"):
+                cur = re.search(r"rp=(\S+) ci=(\S+)", l).groups()
+                nxt = log[i + 1]
+                assert nxt.startswith("block_split_plan") and re.search(r"rp=(\S+)", nxt).group(1) == cur[0]
+                assert "bytes=1048576" in nxt and "bq=64 bk=64" in nxt
+                ws = re.search(r"ws=(\S+)", nxt).group(1)
+                wss.append(ws)
+            elif l.startswith("block_sparse_split"):
+                assert re.search(r"rp=(\S+) ci=(\S+)", l).groups() == cur
+                assert re.search(r"ws=(\S+)", l).group(1) == ws and "bytes=1048576" in l
+                n_sparse += 1
+        assert n_sparse == 255 and wss[0] != wss[1] and wss[0] == wss[2]
+    finally:
+        fake.sdattn_schedule_destroy(h)
+    assert fake.sdattn_fake_live_allocs() == 0
+    for bad, code in ((2, 2), (-1, 2)):
+        d.split_rows = bad
+        hh = ctypes.c_void_p(None)
+        assert fake.sdattn_schedule_create(ctypes.byref(_prob_of(w)), ctypes.byref(d), ctypes.byref(hh)) == code
+    wc = WORKLOADS["pulsecol_dream7b_16k"]
+    dc = _desc_of(wc)
+    dc.split_rows = 1
+    hh = ctypes.c_void_p(None)
+    assert fake.sdattn_schedule_create(ctypes.byref(_prob_of(wc)), ctypes.byref(dc), ctypes.byref(hh)) == 8
+    assert fake.sdattn_fake_live_allocs() == 0
+
+
 def _step(lib, h, t, o=0x5000, lse=None):
     return lib.sdattn_schedule_step(h, t, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000),
                                     ctypes.c_void_p(0x3000), ctypes.c_void_p(o), lse, None)
