@@ -1042,11 +1042,14 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
 }
 
 // Merge of split rows (split plan, launch.h): workgroup s combines the c
-// chunks of the s-th split row.  Each thread takes the 16-byte units of the
+// chunks of the s-th split row, with NW * 64 threads per 32 channels (one
+// group of waves per db).  Each thread takes the 16-byte units of the
 // accumulator layout that the forward's lane of the same wave and lane wrote
-// (query 32 wave + lane mod 32, channels 32 db + 8 rq + 4 (lane / 32) + [0, 4)),
-// weights chunk k by exp(lse_k - LSE), LSE = log sum_k exp(lse_k) (the
-// online-softmax merge of partial rows), and writes O in bf16 and LSE.
+// (query 32 wave + lane mod 32, channels 32 db + 8 rq + 4 (lane / 32) +
+// [0, 4)), weights chunk k by exp(lse_k - LSE), LSE = log sum_k exp(lse_k)
+// (the online-softmax merge of partial rows), and writes O in bf16; the
+// db = 0 threads write LSE.  For each unit the c chunks' loads are issued
+// before any is used, so they are in flight together.
 struct MergeParams {
     const int32_t* ws;
     uint16_t* o;
@@ -1055,28 +1058,31 @@ struct MergeParams {
 };
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void split_merge_kernel(MergeParams m) {
+__global__ __launch_bounds__(NW * 64 * (D / 32)) void split_merge_kernel(MergeParams m) {
     constexpr int ND = D / 32;
     constexpr int BQ = NW * 32;
+    constexpr size_t SLOT = static_cast<size_t>(BQ) * (D + 1);  // floats per partial slot
     const int s = blockIdx.x;
+    const int db = threadIdx.x / (NW * 64);
     const int32_t* ws = m.ws;
     if (s >= ws[split_counts_offset(m.rows, m.slots)]) return;
     const int raw = ws[split_rows_offset(m.rows, m.slots) + s];
     const int row = raw & ((1 << kSplitRowBits) - 1);
     const int c = ((raw >> kSplitCountShift) & (kSplitMaxChunks - 1)) + 1;
     const int slot0 = ws[split_slot_base_offset(m.rows, m.slots) + row];
-    const float* part = reinterpret_cast<const float*>(ws + split_partial_offset(m.rows, m.slots)) +
-                        static_cast<size_t>(slot0) * BQ * (D + 1);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float* part = reinterpret_cast<const float*>(ws + split_partial_offset(m.rows, m.slots)) + slot0 * SLOT;
+    const int lane = threadIdx.x & 63, wave = (threadIdx.x >> 6) % NW;
     const int l32 = lane & 31, hl = lane >> 5;
     const int qq = wave * 32 + l32;
+    const int bh = row / m.n_qtiles, qt = row - bh * m.n_qtiles;
+    const int qi = qt * BQ + qq;
+    if (qi >= m.L) return;
     float lk[kSplitMaxChunks];
+#pragma unroll
+    for (int k = 0; k < kSplitMaxChunks; ++k) lk[k] = k < c ? part[k * SLOT + BQ * D + qq] : -kInf;
     float mx = -kInf;
 #pragma unroll
-    for (int k = 0; k < kSplitMaxChunks; ++k) {
-        lk[k] = k < c ? part[static_cast<size_t>(k) * BQ * (D + 1) + BQ * D + qq] : -kInf;
-        mx = fmaxf(mx, lk[k]);
-    }
+    for (int k = 0; k < kSplitMaxChunks; ++k) mx = fmaxf(mx, lk[k]);
     float w[kSplitMaxChunks];
     float sum = 0.f;
 #pragma unroll
@@ -1085,24 +1091,22 @@ __global__ __launch_bounds__(NW * 64) void split_merge_kernel(MergeParams m) {
         sum += w[k];
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
-    const int bh = row / m.n_qtiles, qt = row - bh * m.n_qtiles;
-    const int qi = qt * BQ + qq;
-    if (qi >= m.L) return;
     uint16_t* orow = m.o + (static_cast<size_t>(bh) * m.L + qi) * D;
+#pragma unroll 1
+    for (int rq = 0; rq < 4; ++rq) {
+        f32x4 v[kSplitMaxChunks];
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+        for (int k = 0; k < kSplitMaxChunks; ++k)
+            if (k < c) v[k] = reinterpret_cast<const f32x4*>(part + k * SLOT)[((wave * ND + db) * 4 + rq) * 64 + lane];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < c; ++k) {
-                const f32x4 v = reinterpret_cast<const f32x4*>(part + static_cast<size_t>(k) * BQ * (D + 1))
-                    [((wave * ND + db) * 4 + rq) * 64 + lane];
-                acc += v * (w[k] * inv);
-            }
-            const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-            *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * hl) = out;
-        }
-    if (m.lse != nullptr && hl == 0) m.lse[static_cast<size_t>(bh) * m.L + qi] = sum > 0.f ? mx + __logf(sum) : -kInf;
+        for (int k = 0; k < kSplitMaxChunks; ++k)
+            if (k < c) acc += v[k] * (w[k] * inv);
+        const u32x2 out = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * hl) = out;
+    }
+    if (db == 0 && m.lse != nullptr && hl == 0)
+        m.lse[static_cast<size_t>(bh) * m.L + qi] = sum > 0.f ? mx + __logf(sum) : -kInf;
 }
 
 template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false>
@@ -1160,11 +1164,11 @@ hipError_t launch_split_d(const FlashParams& fp, int bq, hipStream_t st) {
     if (bq == 64) {
         e = launch_one<D, 2, 32, 2, MODE_BLOCK, kRingK, kRingV, true>(fp, st, grid);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((split_merge_kernel<D, 2>), dim3(slots), dim3(128), 0, st, m);
+        hipLaunchKernelGGL((split_merge_kernel<D, 2>), dim3(slots), dim3(128 * (D / 32)), 0, st, m);
     } else {
         e = launch_one<D, 4, 64, 2, MODE_BLOCK, 2, 2, true>(fp, st, grid);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((split_merge_kernel<D, 4>), dim3(slots), dim3(256), 0, st, m);
+        hipLaunchKernelGGL((split_merge_kernel<D, 4>), dim3(slots), dim3(256 * (D / 32)), 0, st, m);
     }
     return hipGetLastError();
 }
