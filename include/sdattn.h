@@ -284,7 +284,9 @@ SDATTN_API sdattn_status sdattn_forward_block_sparse_planned(const sdattn_proble
  *
  * sdattn_forward_block_sparse_split: sdattn_forward_block_sparse over a split
  * plan computed for the same row_ptr and problem, in the same ws (which the
- * call also writes: the partial results).  Results equal the unsplit
+ * call also writes: the partial results).  The plan is trusted like row_ptr:
+ * a ws that sdattn_block_split_plan did not fill for this pattern and
+ * problem can make the kernels read and write outside it.  Results equal the unsplit
  * forward's within the bf16 rounding of O (rows that are not cut are
  * bit-identical to it).  Two kernels on `stream`: the forward over the plan's
  * items, then the merge.  Calls that share a ws must not overlap.  float32
