@@ -108,15 +108,16 @@ def check_split_plan(ws, rp, rows, nqt, block_q, p, block_k, drp):
     return T, c
 
 
-@pytest.mark.parametrize("L,bq,bk,d", [(1000, 64, 64, 128), (777, 128, 128, 128), (1300, 128, 64, 64),
-                                       (520, 64, 128, 128), (2048, 64, 64, 64)])
-def test_split_forward_matches_the_oracle(L, bq, bk, d):
+@pytest.mark.parametrize("B,L,bq,bk,d", [(1, 1000, 64, 64, 128), (1, 777, 128, 128, 128), (1, 1300, 128, 64, 64),
+                                         (1, 520, 64, 128, 128), (1, 2048, 64, 64, 64), (2, 600, 64, 64, 128),
+                                         (2, 900, 128, 128, 64)])
+def test_split_forward_matches_the_oracle(B, L, bq, bk, d):
     """One head keeps every key block, the others a few, some rows none: long
     rows are cut (chunk length 4 blocks at these sizes), and the merged rows
     match the oracle; rows that are not cut equal the unsplit forward bit for
     bit."""
-    say(f"split forward L={L} bq={bq} bk={bk} d={d}")
-    B, Hq, Hkv = 1, 8, 2
+    say(f"split forward B={B} L={L} bq={bq} bk={bk} d={d}")
+    Hq, Hkv = 8 // B, 2
     rng = np.random.default_rng(L + 7 * bq + bk + d)
     x = {n: to_dev(a) for n, a in tiny_random(L + d + 1, B, Hq, Hkv, L, d, "bf16").items()}
     nqt, nkb = -(-L // bq), -(-L // bk)
