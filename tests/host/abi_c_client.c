@@ -30,6 +30,13 @@ int main(void) {
     CHECK(sdattn_select_blocks_exact_workspace(&p, 128, 128, &topk, &ws_exact, &nnz_exact) == SDATTN_OK);
     CHECK(nnz_exact == nnz && ws_exact >= ws + (size_t)32 * 512 * 512 * 4);
 
+    /* split plan of the 64K block workload: items, slot table and plan ints,
+       then 2 * 512 partial slots of 128 * 129 floats */
+    size_t wss = 0;
+    CHECK(sdattn_block_split_workspace(&p, 128, 128, &wss) == SDATTN_OK);
+    CHECK(wss >= (size_t)2 * 512 * 128 * 129 * 4 + (size_t)3 * 16384 * 4);
+    CHECK(sdattn_block_split_workspace(&p, 128, 128, NULL) == SDATTN_ERR_NULL);
+
     /* the 16K GQA column workload: 492 columns per kv head */
     sdattn_problem pc = {1, 28, 4, 16384, 128, SDATTN_BF16, 0.0f};
     size_t wsc = 0;
