@@ -22,24 +22,28 @@ from workloads.configs import scaled
 pytestmark = pytest.mark.gpu
 
 
-def _desc(w):
+def _desc(w, split_rows=False):
     budget = sd.topk_budget(w.keep_frac) if w.budget == "topk" else sd.mass_budget(w.mass, w.max_mean_density)
     return sd.schedule_desc(w.total_steps, w.dense_steps, w.select_step, w.refresh_interval, list(w.refresh_steps),
                             w.refresh_dense, sd.SEL_KINDS[w.selector], w.block, w.block, budget, w.column_keep_frac,
-                            w.probe_interval, w.min_overlap)
+                            w.probe_interval, w.min_overlap, split_rows)
 
 
 def _inputs(w, base, t):
     return {n: to_dev(a) for n, a in make_step(w, t, base).items()}
 
 
-def test_captured_sparse_steps_replay_like_eager_ones():
+@pytest.mark.parametrize("split_rows", [False, True])
+def test_captured_sparse_steps_replay_like_eager_ones(split_rows):
+    """Also with split rows: a captured step is then the forward over the split
+    plan and the merge of the cut rows (at this size rows of more than 4 kept
+    blocks are cut)."""
     w = scaled(WORKLOADS["llada8b_8k"], seq_len=2048, q_heads=4, kv_heads=4, total_steps=8, refresh_interval=0,
                max_mean_density=0.3)
-    say("graph: capture 3 sparse steps, L=2048 mass budget")
+    say(f"graph: capture 3 sparse steps, L=2048 mass budget, split rows {split_rows}")
     p = sd.problem(w.batch, w.q_heads, w.kv_heads, w.seq_len, w.head_dim, w.dtype)
     base = make_base(w)
-    h = sd.sdattn_schedule_create(p, _desc(w))
+    h = sd.sdattn_schedule_create(p, _desc(w, split_rows))
     try:
         x0 = _inputs(w, base, 0)
         o0 = torch.empty_like(x0["q"])
