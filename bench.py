@@ -14,7 +14,8 @@ line gives the workload's full schedule modelled from the per-action median
 step times (modelled_native_schedule_ms_per_step).
 
 By default the 64K headline is followed by the metric's other contexts, the
-8K, 16K and 32K workloads, each run for the same K steps and reported under
+8K, 16K and 32K workloads, each run as its own whole schedule (256, 192 and
+128 steps; the same K steps instead when --steps is given) and reported under
 "configs" (--no-sweep skips them).
 
 Inputs are the seeded synthetic tensors of the workload (planted per-head
@@ -1276,7 +1277,10 @@ def main():
     if sweep:
         cfgs = {}
         for name in SWEEP:
-            rec, _ = run_schedule(args, get_workload(name), K, args.warmup, with_gpu_state=False)
+            wc = get_workload(name)
+            # each context runs its own schedule unless --steps fixes K for all
+            Kc = args.steps if args.steps is not None else wc.total_steps
+            rec, _ = run_schedule(args, wc, Kc, args.warmup, with_gpu_state=False)
             cfgs[name] = compact(rec)
         out["configs"] = cfgs
     print(json.dumps(out), flush=True)
