@@ -191,13 +191,13 @@ __global__ __launch_bounds__(kSplitThreads) void split_plan_kernel(const int32_t
 }  // namespace
 
 int block_plan_segment_rows(int block_q, int nqt) {
-    // block rows one XCD runs at once: 32 CUs, times the forward's workgroups
-    // per CU for this block size
+    // block rows one XCD runs at once (32 CUs, times the forward's workgroups
+    // per CU for this block size), lowered to the largest divisor of nqt
     const int in_flight = 32 * block_rows_per_cu(block_q);
     int s = nqt;
     if (nqt > in_flight) {
         s = in_flight;
-        while (s > 1 && nqt % s != 0) s >>= 1;
+        while (s > 1 && nqt % s != 0) --s;
     }
     return s;
 }

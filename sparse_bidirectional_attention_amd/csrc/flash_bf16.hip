@@ -150,14 +150,19 @@ __device__ __forceinline__ int balanced_block_item(int id, int n_qtiles, int n_p
     return pair * n_qtiles + qt;
 }
 
-template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false>
-__global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
+template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false, int WPE = 1>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void flash_fwd_bf16(FlashParams p) {
     // KT keys per tile (32 or 64), NST LDS stages (tiles in flight: NST - 1);
     // the pipelined pass over 32-key tiles uses a ring of NK K slots and NV V
     // slots instead (K fetched NK - 1 units ahead, V NV - 1).  SPLIT: block
     // form over a split plan (p.order is its workspace, launch.h): a
     // workgroup may compute one chunk of a row's kept blocks and write a
-    // partial result that split_merge_kernel combines.
+    // partial result that split_merge_kernel combines.  WPE: waves per SIMD
+    // the register allocation must leave room for (at most 512 / WPE
+    // registers per lane).  At three the 32-key block form runs the plain
+    // tile loop: the ring pass keeps two tiles' scores and probabilities
+    // live and would spill, while the third wave on the SIMD overlaps one
+    // wave's softmax with another's MFMAs instead.
     constexpr int KB = KT / 32;             // 32-key MFMA blocks per tile
     constexpr int T = NW * 64;
     constexpr int DK = D / 16;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(NW * 64) void flash_fwd_bf16(FlashParams p) {
     static_assert(NDMA * T == SLOTS && T % UNITS == 0 && ROWS_PER_DMA % 4 == 0, "DMA tiling");
     static_assert(NW * 32 * OPITCH <= NST * STAGEB, "epilogue staging fits in the stages");
     // 32-key piped pass: K ring slots 0..NK-1, then V ring slots 0..NV-1
-    constexpr bool RING = KT == 32 && MODE == MODE_BLOCK;
+    constexpr bool RING = KT == 32 && MODE == MODE_BLOCK && WPE < 3;
     constexpr int RINGB = (NK + NV) * TILEB;
     constexpr int SMEMB = RING && RINGB > NST * STAGEB ? RINGB : NST * STAGEB;
     static_assert(!RING || (NK >= 2 && NV >= 2 && RINGB >= NST * STAGEB), "ring holds the checked pass's stages");
@@ -1109,9 +1114,9 @@ __global__ __launch_bounds__(NW * 64 * (D / 32)) void split_merge_kernel(MergePa
         m.lse[static_cast<size_t>(bh) * m.L + qi] = sum > 0.f ? mx + __logf(sum) : -kInf;
 }
 
-template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false>
+template <int D, int NW, int KT, int NST, int MODE, int NK = NST, int NV = NST, bool SPLIT = false, int WPE = 1>
 hipError_t launch_one(const FlashParams& fp, hipStream_t st, int grid) {
-    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE, NK, NV, SPLIT>), dim3(grid), dim3(NW * 64), 0, st, fp);
+    hipLaunchKernelGGL((flash_fwd_bf16<D, NW, KT, NST, MODE, NK, NV, SPLIT, WPE>), dim3(grid), dim3(NW * 64), 0, st, fp);
     return hipGetLastError();
 }
 
@@ -1127,15 +1132,21 @@ inline int query_tile(AttnMode mode, const SparseIndex& ix) { return mode == MOD
 }  // namespace
 
 // Workgroups of the block-sparse form that share one CU (LDS and registers):
-// four of the 40 KiB 64-query form, two of the 64 KiB 128-query form.
-int block_rows_per_cu(int block_q) { return block_q == 64 ? 4 : 2; }
+// four of the 40 KiB 64-query form; three of the 128-query form (d = 128:
+// 32 KiB and at most 168 registers, three waves per SIMD; d = 64: 32 KiB
+// and 164 registers).
+int block_rows_per_cu(int block_q) { return block_q == 64 ? 4 : 3; }
 
 namespace {
 
 // Tile shapes (waves, keys per tile, LDS stages):
 //   256-query tiles (dense, column): 8 waves, 64-key tiles, two stages (64 KiB);
-//   128-query blocks: 4 waves, 64-key tiles, two stages (64 KiB, two
-//   workgroups per CU);
+//   128-query blocks, d = 128: 4 waves, 32-key tiles, two stages (32 KiB),
+//   the plain tile loop in at most 168 registers, so three workgroups share
+//   a CU with three waves per SIMD (faster than 64-key tiles pipelined in
+//   253 registers with two workgroups per CU);
+//   128-query blocks, d = 64: 4 waves, 64-key tiles, two stages (32 KiB, 164
+//   registers: three workgroups per CU);
 //   64-query blocks: 2 waves, 32-key tiles through a ring of kRingK K and
 //   kRingV V slots (40 KiB at d = 128, four workgroups per CU).
 template <int D>
@@ -1147,7 +1158,10 @@ hipError_t launch_d(AttnMode mode, const FlashParams& fp, int bq, hipStream_t st
         case MODE_COLUMN_PACKED: return launch_one<D, 8, 64, 2, MODE_COLUMN_PACKED>(fp, st, g);
         case MODE_BLOCK:
             if (bq == 64) return launch_one<D, 2, 32, 2, MODE_BLOCK, kRingK, kRingV>(fp, st, g);
-            return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st, g);
+            if constexpr (D == 128)
+                return launch_one<D, 4, 32, 2, MODE_BLOCK, 2, 2, false, 3>(fp, st, g);
+            else
+                return launch_one<D, 4, 64, 2, MODE_BLOCK>(fp, st, g);
     }
     return hipErrorInvalidValue;
 }
@@ -1166,7 +1180,12 @@ hipError_t launch_split_d(const FlashParams& fp, int bq, hipStream_t st) {
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((split_merge_kernel<D, 2>), dim3(slots), dim3(128 * (D / 32)), 0, st, m);
     } else {
-        e = launch_one<D, 4, 64, 2, MODE_BLOCK, 2, 2, true>(fp, st, grid);
+        // the same tile shape as the unsplit forward, so a row that is not cut
+        // gets the same arithmetic
+        if constexpr (D == 128)
+            e = launch_one<D, 4, 32, 2, MODE_BLOCK, 2, 2, true, 3>(fp, st, grid);
+        else
+            e = launch_one<D, 4, 64, 2, MODE_BLOCK, 2, 2, true>(fp, st, grid);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((split_merge_kernel<D, 4>), dim3(slots), dim3(256 * (D / 32)), 0, st, m);
     }

@@ -25,13 +25,14 @@ pytestmark = pytest.mark.gpu
 
 def _segment_rows(block_q, nqt):
     """Rows one XCD runs at once: 32 CUs times the forward's workgroups per
-    CU (four 64-query or two 128-query blocks), halved until it divides nqt."""
-    in_flight = 32 * (4 if block_q == 64 else 2)
+    CU (four 64-query or three 128-query blocks), lowered to the largest
+    divisor of nqt."""
+    in_flight = 32 * (4 if block_q == 64 else 3)
     if nqt <= in_flight:
         return nqt
     s = in_flight
     while s > 1 and nqt % s:
-        s //= 2
+        s -= 1
     return s
 
 

@@ -27,8 +27,8 @@ ROW_MASK = (1 << 24) - 1
 
 
 def _slots(block_q):
-    # workgroups the GPU holds at once: 256 CUs times four 64-query or two 128-query blocks
-    return 256 * (4 if block_q == 64 else 2)
+    # workgroups the GPU holds at once: 256 CUs times four 64-query or three 128-query blocks
+    return 256 * (4 if block_q == 64 else 3)
 
 
 def host_split(rp, rows, block_q):
