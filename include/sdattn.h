@@ -263,7 +263,7 @@ SDATTN_API sdattn_status sdattn_forward_block_sparse_planned(const sdattn_proble
  * block row: under a head-adaptive budget (Step-dLLM, Abstract) one head may
  * keep most key blocks while the others keep few.  A split plan cuts every
  * row with more kept blocks than T = max(4, ceil(nnz / slots)) (slots = the
- * workgroups the GPU holds at once: 1024 for 64-query blocks, 512 for 128)
+ * workgroups the GPU holds at once: 1024 for 64-query blocks, 768 for 128)
  * into c = min(8, ceil(ne / T)) chunks of consecutive kept blocks.  Each
  * chunk is computed by its own workgroup, which writes its output
  * normalised over the chunk together with the chunk's log-sum-exp; a merge
