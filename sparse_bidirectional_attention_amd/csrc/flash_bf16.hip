@@ -12,8 +12,9 @@
 // Each form streams key tiles; only where the tile's rows come from differs.
 //
 // Work decomposition: one workgroup per (batch, head, tile of 32 NW queries),
-// each of the NW waves owning 32 query rows.  Per KT-key tile (KT = 64, or 32
-// for 64-query blocks):
+// each of the NW waves owning 32 query rows.  Per KT-key tile (KT = 64 for
+// 256-query tiles and 128-query blocks at d = 64; 32 for 64-query blocks, and
+// for 128-query tiles at d = 128, which run three workgroups per CU):
 //   * the K and V rows of the tile go from HBM straight into LDS with the
 //     buffer-to-LDS DMA, NST stages deep (one barrier per tile); each lane
 //     fetches the 16-byte chunk that belongs at its LDS slot, so the tile
