@@ -165,7 +165,7 @@ def test_column_sparse_matches_oracle(dtype, Hq, Hkv, L, kcol, d):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("Hq,Hkv,L,kcol,d", [(6, 2, 700, 21, 128), (4, 4, 512, 64, 64), (7, 1, 1000, 130, 128),
                                              (2, 2, 97, 97, 128), (28, 4, 2048, 61, 128), (2, 1, 300, 1, 64),
-                                             (3, 1, 1400, 1040, 128)])
+                                             (3, 1, 1400, 1040, 128), (2, 1, 1100, 1024, 128), (2, 1, 1100, 1025, 128)])
 def test_gathered_columns_and_packed_forward(dtype, Hq, Hkv, L, kcol, d):
     """sdattn_gather_columns copies exactly the listed rows; the packed forward
     over them is bit-identical to the column-sparse forward with the same list
