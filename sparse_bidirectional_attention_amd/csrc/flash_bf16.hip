@@ -510,10 +510,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) 
     // One tile.  Program order puts independent MFMA and VALU work side by
     // side (QK of block 1 with the softmax of block 0, PV of block 0 with the
     // softmax of block 1) so the scheduler can interleave them.
+    // With three waves per SIMD in the plain loop over 32-key tiles, a wave
+    // raises its priority while it issues its MFMAs, so the SIMD's arbiter
+    // prefers it to the waves in their softmax and the matrix pipe stays fed
+    // (results unchanged).
+    constexpr bool PRIO = WPE >= 3 && KB == 1;
     auto compute_tile = [&](const char* stg, int nvalid, auto masked, auto checked) __attribute__((always_inline)) {
         f32x16 s0, s1;
         uint32_t pk0[8], pk1[8];
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
         qk(stg, 0, s0);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         if constexpr (masked.value) mask(0, nvalid, s0);
         if constexpr (KB == 2) {
             qk(stg, 1, s1);
@@ -539,7 +546,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE))) 
         if constexpr (checked.value)
             if (__any(!(ts0 <= kBigSum))) ts0 = rebase(s0, pk0);
         l_acc += ts0;
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
         pv(stg, 0, pk0);
+        if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
         if constexpr (KB == 2) {
             float ts1 = exps(s1, mc, pk1);
             if constexpr (!masked.value) {
